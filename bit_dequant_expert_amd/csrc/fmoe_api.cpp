@@ -1,0 +1,432 @@
+// fmoe_api.cpp -- the C ABI of libfmoe.so (declared in include/fmoe.h).
+//
+// Host side only: validates every argument before anything is enqueued, carves
+// the caller's workspace, picks launch shapes and enqueues the kernels of
+// fmoe_kernels.hip on the caller's stream.  Nothing here allocates, copies or
+// synchronises.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fmoe.h"
+#include "fmoe_internal.h"
+
+namespace {
+
+using fmoe::QFmt;
+
+thread_local char g_err[512] = "";
+
+fmoe_status fail(fmoe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fmoe_status hip_fail(hipError_t e, const char* what) {
+  return fail(FMOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+constexpr int kMaxE = 2048;       // experts held in registers by the top-k wave
+constexpr int kMaxH = 8192;       // router row held in registers
+constexpr int kMaxK = 16;
+constexpr int kMaxSel = 8192;     // T * k selections grouped in LDS
+constexpr int kMfmaThreshold = INT_MAX;  // experts with >= this many tokens use MFMA
+
+fmoe_status check_fmt(const fmoe_qformat* f, QFmt* out) {
+  if (!f) return fail(FMOE_ERR_NULL, "fmt is NULL");
+  if (f->bits != 2 && f->bits != 4)
+    return fail(FMOE_ERR_UNSUPPORTED, "bits=%d (supported: 2, 4)", f->bits);
+  if (f->group != 32 && f->group != 64)
+    return fail(FMOE_ERR_UNSUPPORTED, "group=%d (supported: 32, 64)", f->group);
+  if (f->sdtype != FMOE_F32 && f->sdtype != FMOE_BF16)
+    return fail(FMOE_ERR_UNSUPPORTED, "sdtype=%d (supported: FMOE_F32, FMOE_BF16)", f->sdtype);
+  out->bits = f->bits;
+  out->group = f->group;
+  out->sb = f->sdtype == FMOE_BF16 ? 2 : 4;
+  return FMOE_OK;
+}
+
+// Shape rules for a row of K codes; min_segs > 1 for the expert paths.
+fmoe_status check_k(int K, const QFmt& f, int min_segs, const char* name) {
+  if (K <= 0) return fail(FMOE_ERR_SHAPE, "%s: k=%d must be positive", name, K);
+  if (K % f.group != 0)
+    return fail(FMOE_ERR_SHAPE, "%s: k=%d is not a multiple of group %d", name, K, f.group);
+  if (((int64_t)K * f.bits) % 128 != 0)
+    return fail(FMOE_ERR_SHAPE, "%s: k*bits/8 = %lld is not a multiple of 16", name,
+                (long long)K * f.bits / 8);
+  const int S = (int)((int64_t)K * f.bits / 128);
+  const bool ok = (S < 64 && 64 % S == 0) || S == 64 || S == 128 || S == 256;
+  if (!ok)
+    return fail(FMOE_ERR_UNSUPPORTED,
+                "%s: k=%d gives %d 16-byte segments per row (supported: divisors of 64, "
+                "or 64/128/256)", name, K, S);
+  if (S < min_segs)
+    return fail(FMOE_ERR_UNSUPPORTED, "%s: k=%d is too short (need k*bits >= %d)", name, K,
+                128 * min_segs);
+  return FMOE_OK;
+}
+
+fmoe_status check_qmat(const fmoe_qmat* W, const QFmt& f, int n, int k, int min_segs,
+                       const char* name) {
+  if (!W) return fail(FMOE_ERR_NULL, "%s is NULL", name);
+  if (!W->q || !W->scale || !W->bias)
+    return fail(FMOE_ERR_NULL, "%s: q/scale/bias must not be NULL", name);
+  if (!aligned(W->q, 16) || !aligned(W->scale, 16) || !aligned(W->bias, 16))
+    return fail(FMOE_ERR_ALIGN, "%s: q/scale/bias must be 16-byte aligned", name);
+  if (W->n <= 0) return fail(FMOE_ERR_SHAPE, "%s: n=%d must be positive", name, W->n);
+  if ((n >= 0 && W->n != n) || (k >= 0 && W->k != k))
+    return fail(FMOE_ERR_SHAPE, "%s: shape %dx%d, expected %dx%d", name, W->n, W->k, n, k);
+  return check_k(W->k, f, min_segs, name);
+}
+
+fmoe_status check_vec(const void* p, const char* name) {
+  if (!p) return fail(FMOE_ERR_NULL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(FMOE_ERR_ALIGN, "%s must be 16-byte aligned", name);
+  return FMOE_OK;
+}
+
+int64_t slab_layout(int H, int I, const QFmt& f, int64_t off[9]) {
+  const int64_t rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  int64_t pos = 0;
+  for (int m = 0; m < 3; ++m) {
+    const int64_t qb = rows[m] * cols[m] * f.bits / 8;
+    const int64_t sb = rows[m] * (cols[m] / f.group) * f.sb;
+    off[3 * m] = pos;
+    pos = (int64_t)align256((size_t)(pos + qb));
+    off[3 * m + 1] = pos;
+    pos = (int64_t)align256((size_t)(pos + sb));
+    off[3 * m + 2] = pos;
+    pos = (int64_t)align256((size_t)(pos + sb));
+  }
+  return pos;
+}
+
+// ------------------------------------------------------------- workspace
+struct LayerWs {
+  size_t ctr, lg64, w, g, act, xprep, abuf, ccnt, aprep, yslot, part, total;
+  int maxA, nrb_gu, nrb_d;
+};
+
+size_t act_ints(int maxA, int T, int kp1) { return 2 + 4 * (size_t)maxA + (size_t)T * kp1; }
+
+LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
+  LayerWs w{};
+  const int kp1 = k + 1;
+  const int64_t sel = (int64_t)T * k;
+  w.maxA = (int)((sel < E ? sel : E) + 1);
+  w.nrb_gu = (I + fmoe::rows_per_wg(H, bits) - 1) / fmoe::rows_per_wg(H, bits);
+  w.nrb_d = (H + fmoe::rows_per_wg(I, bits) - 1) / fmoe::rows_per_wg(I, bits);
+  const size_t ent = (size_t)T * kp1;
+  size_t pos = 0;
+  w.ctr = pos; pos += 256;
+  w.lg64 = pos; pos = align256(pos + (size_t)T * (E + 1) * 8);
+  w.w = pos; pos = align256(pos + (size_t)T * k * 4);
+  w.g = pos; pos = align256(pos + (size_t)T * 4);
+  w.act = pos; pos = align256(pos + act_ints(w.maxA, T, kp1) * 4);
+  w.xprep = pos; pos = align256(pos + (size_t)T * fmoe::xprep_bytes(H));
+  w.abuf = pos; pos = align256(pos + ent * I * 4);
+  w.ccnt = pos; pos = align256(pos + ent * (I / 32) * 4);
+  w.aprep = pos; pos = align256(pos + ent * fmoe::xprep_bytes(I));
+  w.yslot = pos; pos = align256(pos + (T > 1 ? ent * H * 4 : 0));
+  w.part = pos; pos = align256(pos + (size_t)w.nrb_d * 4);
+  w.total = pos;
+  return w;
+}
+
+struct FfnWs {
+  size_t ctr, act, xprep, abuf, ccnt, aprep, total;
+};
+
+FfnWs ffn_ws(int H, int I) {
+  FfnWs w{};
+  size_t pos = 0;
+  w.ctr = pos; pos += 256;
+  w.act = pos; pos = align256(pos + act_ints(1, 1, 1) * 4);
+  w.xprep = pos; pos = align256(pos + fmoe::xprep_bytes(H));
+  w.abuf = pos; pos = align256(pos + (size_t)I * 4);
+  w.ccnt = pos; pos = align256(pos + (size_t)(I / 32) * 4);
+  w.aprep = pos; pos = align256(pos + fmoe::xprep_bytes(I));
+  w.total = pos;
+  return w;
+}
+
+size_t route_ws(int T, int E) { return 256 + align256((size_t)T * E * 8); }
+
+fmoe_status check_router(int T, int H, int E, int k) {
+  if (T < 0) return fail(FMOE_ERR_SHAPE, "T=%d must be >= 0", T);
+  if (H <= 0 || H % 4 != 0) return fail(FMOE_ERR_SHAPE, "H=%d must be a positive multiple of 4", H);
+  if (H > kMaxH) return fail(FMOE_ERR_UNSUPPORTED, "H=%d exceeds %d", H, kMaxH);
+  if (E <= 0) return fail(FMOE_ERR_SHAPE, "E=%d must be positive", E);
+  if (E > kMaxE) return fail(FMOE_ERR_UNSUPPORTED, "E=%d exceeds %d", E, kMaxE);
+  if (k < 1 || k > E) return fail(FMOE_ERR_SHAPE, "k=%d must be in [1, E=%d]", k, E);
+  if (k > kMaxK) return fail(FMOE_ERR_UNSUPPORTED, "k=%d exceeds %d", k, kMaxK);
+  if ((int64_t)T * k > kMaxSel)
+    return fail(FMOE_ERR_UNSUPPORTED, "T*k=%lld exceeds %d", (long long)T * k, kMaxSel);
+  return FMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fmoe_abi_version(void) { return FMOE_ABI_VERSION; }
+
+const char* fmoe_last_error(void) { return g_err; }
+
+int64_t fmoe_slab_layout(int32_t hidden, int32_t inter, const fmoe_qformat* fmt, int64_t off[9]) {
+  QFmt f;
+  if (check_fmt(fmt, &f) != FMOE_OK) return -1;
+  if (!off) { fail(FMOE_ERR_NULL, "off is NULL"); return -1; }
+  if (hidden <= 0 || inter <= 0 || hidden % f.group || inter % f.group) {
+    fail(FMOE_ERR_SHAPE, "hidden=%d / inter=%d must be positive multiples of group %d", hidden,
+         inter, f.group);
+    return -1;
+  }
+  return slab_layout(hidden, inter, f, off);
+}
+
+size_t fmoe_route_workspace_size(int32_t T, int32_t E) {
+  if (T < 0 || E <= 0) return 0;
+  return route_ws(T, E);
+}
+
+fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, int32_t H, int32_t E,
+                            int32_t k, int32_t* idx, float* w, float* logits_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  fmoe_status st = check_router(T, H, E, k);
+  if (st != FMOE_OK) return st;
+  if ((st = check_vec(router_w, "router_w")) != FMOE_OK) return st;
+  if ((st = check_vec(x, "x")) != FMOE_OK) return st;
+  if (!idx || !w) return fail(FMOE_ERR_NULL, "idx and w must not be NULL");
+  if (T == 0) return FMOE_OK;
+  if (!ws) return fail(FMOE_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(FMOE_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < route_ws(T, E))
+    return fail(FMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, route_ws(T, E));
+  uint8_t* wsb = (uint8_t*)ws;
+  fmoe::RouteArgs a{};
+  a.Wr = router_w;
+  a.wsg = nullptr;
+  a.x = x;
+  a.T = T; a.H = H; a.E = E; a.k = k; a.rows = E;
+  a.n_router_wgs = (E + 3) / 4;
+  a.lg64 = (double*)(wsb + 256);
+  a.logits_out = logits_out;
+  a.idx_out = idx;
+  a.w_out = w;
+  a.counter = (int*)wsb;
+  a.kp1 = k + 1;
+  a.mfma_thr = kMfmaThreshold;
+  a.n_prep_wgs = 0;
+  const size_t lds = (size_t)T * k * 4 + 64;
+  hipError_t e = fmoe::launch_route(a, lds, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "route kernel");
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_dequant_gemv(const fmoe_qmat* W, const fmoe_qformat* fmt, const float* x,
+                              float* y, void* stream) {
+  QFmt f;
+  fmoe_status st = check_fmt(fmt, &f);
+  if (st != FMOE_OK) return st;
+  if ((st = check_qmat(W, f, -1, -1, 1, "W")) != FMOE_OK) return st;
+  if ((st = check_vec(x, "x")) != FMOE_OK) return st;
+  if ((st = check_vec(y, "y")) != FMOE_OK) return st;
+  if (overlap(x, (size_t)W->k * 4, y, (size_t)W->n * 4)) return fail(FMOE_ERR_SHAPE, "y overlaps x");
+  hipError_t e = fmoe::launch_gemv(f, (const uint8_t*)W->q, (const uint8_t*)W->scale,
+                                   (const uint8_t*)W->bias, W->n, W->k, x, y, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gemv kernel");
+  return FMOE_OK;
+}
+
+size_t fmoe_expert_ffn_workspace_size(const fmoe_expert* e, const fmoe_qformat* fmt) {
+  if (!e || !fmt) return 0;
+  return ffn_ws(e->gate.k, e->gate.n).total;
+}
+
+fmoe_status fmoe_expert_ffn(const fmoe_expert* e, const fmoe_qformat* fmt, const float* x,
+                            float* y, void* ws, size_t ws_bytes, void* stream) {
+  QFmt f;
+  fmoe_status st = check_fmt(fmt, &f);
+  if (st != FMOE_OK) return st;
+  if (!e) return fail(FMOE_ERR_NULL, "expert is NULL");
+  const int H = e->gate.k, I = e->gate.n;
+  if ((st = check_qmat(&e->gate, f, -1, -1, 4, "gate")) != FMOE_OK) return st;
+  if ((st = check_qmat(&e->up, f, I, H, 4, "up")) != FMOE_OK) return st;
+  if ((st = check_qmat(&e->down, f, H, I, 4, "down")) != FMOE_OK) return st;
+  if ((st = check_vec(x, "x")) != FMOE_OK) return st;
+  if ((st = check_vec(y, "y")) != FMOE_OK) return st;
+  if (overlap(x, (size_t)H * 4, y, (size_t)H * 4)) return fail(FMOE_ERR_SHAPE, "y overlaps x");
+  const FfnWs L = ffn_ws(H, I);
+  if (!ws) return fail(FMOE_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(FMOE_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < L.total) return fail(FMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, L.total);
+  uint8_t* wsb = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+
+  fmoe::ExpertSrc src{};
+  src.base = nullptr;
+  src.stride = 0;
+  const fmoe_qmat* m[3] = {&e->gate, &e->up, &e->down};
+  for (int i = 0; i < 3; ++i) {
+    src.off[3 * i] = (int64_t)(uintptr_t)m[i]->q;
+    src.off[3 * i + 1] = (int64_t)(uintptr_t)m[i]->scale;
+    src.off[3 * i + 2] = (int64_t)(uintptr_t)m[i]->bias;
+  }
+  int32_t* act = (int32_t*)(wsb + L.act);
+  hipError_t he = fmoe::launch_ffn_prep(f.bits, x, H, wsb + L.xprep, act, 1, s);
+  if (he != hipSuccess) return hip_fail(he, "ffn prep kernel");
+
+  fmoe::GUArgs g{};
+  g.src = src; g.act = act; g.maxA = 1; g.kp1 = 1; g.H = H; g.I = I;
+  g.xprep = wsb + L.xprep; g.abuf = (float*)(wsb + L.abuf); g.aprep = wsb + L.aprep;
+  g.ccnt = (int*)(wsb + L.ccnt);
+  g.nrb = (I + fmoe::rows_per_wg(H, f.bits) - 1) / fmoe::rows_per_wg(H, f.bits);
+  g.U = fmoe::iters_per_wave(H, f.bits);
+  g.mfma_thr = INT_MAX;
+  he = fmoe::launch_gateup(f, g, g.nrb, s);
+  if (he != hipSuccess) return hip_fail(he, "gate/up kernel");
+
+  fmoe::DArgs d{};
+  d.src = src; d.act = act; d.maxA = 1; d.kp1 = 1; d.k = 0; d.H = H; d.I = I;
+  d.aprep = wsb + L.aprep; d.yslot = y;
+  d.nrb = (H + fmoe::rows_per_wg(I, f.bits) - 1) / fmoe::rows_per_wg(I, f.bits);
+  d.U = fmoe::iters_per_wave(I, f.bits);
+  d.mfma_thr = INT_MAX;
+  he = fmoe::launch_down_slots(f, d, d.nrb, s);
+  if (he != hipSuccess) return hip_fail(he, "down kernel");
+  return FMOE_OK;
+}
+
+size_t fmoe_workspace_size(const fmoe_layer* L, int32_t T) {
+  if (!L || T < 0 || L->n_experts <= 0 || L->top_k <= 0 || L->fmt.bits <= 0) return 0;
+  return layer_ws(T, L->hidden, L->inter, L->n_experts, L->top_k, L->fmt.bits).total;
+}
+
+fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* x,
+                                   const float* residual, float* h_out, float* y_out,
+                                   int32_t* idx_out, float* w_out, float* moe_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!L) return fail(FMOE_ERR_NULL, "layer is NULL");
+  QFmt f;
+  fmoe_status st = check_fmt(&L->fmt, &f);
+  if (st != FMOE_OK) return st;
+  const int H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k;
+  if ((st = check_router(T, H, E, k)) != FMOE_OK) return st;
+  if ((st = check_k(H, f, 4, "hidden")) != FMOE_OK) return st;
+  if ((st = check_k(I, f, 4, "inter")) != FMOE_OK) return st;
+  if ((st = check_vec(L->router_w, "router_w")) != FMOE_OK) return st;
+  if ((st = check_vec(L->shared_gate_w, "shared_gate_w")) != FMOE_OK) return st;
+  if ((st = check_vec(L->norm_w, "norm_w")) != FMOE_OK) return st;
+  if (!L->slabs) return fail(FMOE_ERR_NULL, "slabs is NULL");
+  if (!aligned(L->slabs, 256)) return fail(FMOE_ERR_ALIGN, "slabs must be 256-byte aligned");
+  int64_t off[9];
+  const int64_t slab = slab_layout(H, I, f, off);
+  if (L->slab_stride % 256 != 0)
+    return fail(FMOE_ERR_ALIGN, "slab_stride=%lld is not a multiple of 256", (long long)L->slab_stride);
+  if (L->slab_stride < slab)
+    return fail(FMOE_ERR_SHAPE, "slab_stride=%lld < slab size %lld", (long long)L->slab_stride,
+                (long long)slab);
+  if (!(L->norm_eps >= 0.f)) return fail(FMOE_ERR_SHAPE, "norm_eps must be >= 0");
+  if ((st = check_vec(x, "x")) != FMOE_OK) return st;
+  if ((st = check_vec(residual, "residual")) != FMOE_OK) return st;
+  if ((st = check_vec(h_out, "h_out")) != FMOE_OK) return st;
+  if ((st = check_vec(y_out, "y_out")) != FMOE_OK) return st;
+  if (moe_out && !aligned(moe_out, 16)) return fail(FMOE_ERR_ALIGN, "moe_out must be 16-byte aligned");
+  if (T == 0) return FMOE_OK;
+  const size_t vb = (size_t)T * H * 4;
+  if (residual != x && overlap(residual, vb, x, vb))
+    return fail(FMOE_ERR_SHAPE, "residual partially overlaps x");
+  if (h_out != residual && (overlap(h_out, vb, residual, vb) || overlap(h_out, vb, x, vb)))
+    return fail(FMOE_ERR_SHAPE, "h_out overlaps x/residual without being residual");
+  if (overlap(y_out, vb, x, vb) || overlap(y_out, vb, residual, vb) || overlap(y_out, vb, h_out, vb))
+    return fail(FMOE_ERR_SHAPE, "y_out overlaps x, residual or h_out");
+  if (moe_out && (overlap(moe_out, vb, x, vb) || overlap(moe_out, vb, residual, vb) ||
+                  overlap(moe_out, vb, h_out, vb) || overlap(moe_out, vb, y_out, vb)))
+    return fail(FMOE_ERR_SHAPE, "moe_out overlaps another vector");
+
+  const LayerWs W = layer_ws(T, H, I, E, k, f.bits);
+  if (!ws) return fail(FMOE_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(FMOE_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < W.total) return fail(FMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, W.total);
+
+  uint8_t* wsb = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const int kp1 = k + 1;
+  int32_t* act = (int32_t*)(wsb + W.act);
+  int* ctr = (int*)(wsb + W.ctr);
+
+  fmoe::ExpertSrc src{};
+  src.base = (const uint8_t*)L->slabs;
+  src.stride = L->slab_stride;
+  memcpy(src.off, off, sizeof off);
+
+  fmoe::RouteArgs ra{};
+  ra.Wr = L->router_w; ra.wsg = L->shared_gate_w; ra.x = x;
+  ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.rows = E + 1;
+  ra.n_router_wgs = (E + 1 + 3) / 4;
+  ra.lg64 = (double*)(wsb + W.lg64);
+  ra.idx_out = idx_out; ra.w_out = w_out;
+  ra.w_ws = (float*)(wsb + W.w); ra.g_ws = (float*)(wsb + W.g);
+  ra.counter = ctr + 0;
+  ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = kMfmaThreshold;
+  ra.xprep = wsb + W.xprep; ra.bits = f.bits;
+  ra.n_prep_wgs = (int)(((int64_t)T * (H / 32) + 31) / 32);
+  const size_t rlds = ((size_t)T * k + 3 * (size_t)E) * 4 + 64;
+  hipError_t he = fmoe::launch_route(ra, rlds, s);
+  if (he != hipSuccess) return hip_fail(he, "route kernel");
+
+  fmoe::GUArgs g{};
+  g.src = src; g.act = act; g.maxA = W.maxA; g.kp1 = kp1; g.H = H; g.I = I;
+  g.xprep = wsb + W.xprep; g.abuf = (float*)(wsb + W.abuf); g.aprep = wsb + W.aprep;
+  g.ccnt = (int*)(wsb + W.ccnt);
+  g.nrb = W.nrb_gu; g.U = fmoe::iters_per_wave(H, f.bits); g.mfma_thr = kMfmaThreshold;
+  he = fmoe::launch_gateup(f, g, W.maxA * W.nrb_gu, s);
+  if (he != hipSuccess) return hip_fail(he, "gate/up kernel");
+
+  fmoe::DArgs d{};
+  d.src = src; d.act = act; d.maxA = W.maxA; d.kp1 = kp1; d.k = k; d.H = H; d.I = I;
+  d.aprep = wsb + W.aprep; d.w_ws = (const float*)(wsb + W.w); d.g_ws = (const float*)(wsb + W.g);
+  d.resid = residual; d.h_out = h_out; d.y_out = y_out; d.moe_out = moe_out;
+  d.gamma = L->norm_w; d.eps = L->norm_eps;
+  d.nrb = W.nrb_d; d.U = fmoe::iters_per_wave(I, f.bits); d.mfma_thr = kMfmaThreshold;
+  if (T == 1) {
+    d.partials = (float*)(wsb + W.part);
+    d.ncnt = ctr + 1;
+    const int64_t ab = fmoe::xprep_bytes(I);
+    int nb = (int)(49152 / ab);
+    nb = nb < 1 ? 1 : nb;
+    nb = nb > 8 ? 8 : nb;
+    d.nbatch = nb < kp1 ? nb : kp1;
+    he = fmoe::launch_down_combine(f, d, s);
+    if (he != hipSuccess) return hip_fail(he, "down/combine kernel");
+  } else {
+    d.yslot = (float*)(wsb + W.yslot);
+    he = fmoe::launch_down_slots(f, d, W.maxA * W.nrb_d, s);
+    if (he != hipSuccess) return hip_fail(he, "down kernel");
+    fmoe::CombineArgs c{};
+    c.T = T; c.H = H; c.k = k; c.kp1 = kp1;
+    c.yslot = d.yslot; c.w_ws = d.w_ws; c.g_ws = d.g_ws; c.resid = residual;
+    c.h_out = h_out; c.y_out = y_out; c.moe_out = moe_out; c.gamma = L->norm_w; c.eps = L->norm_eps;
+    he = fmoe::launch_combine_norm(c, s);
+    if (he != hipSuccess) return hip_fail(he, "combine kernel");
+  }
+  return FMOE_OK;
+}
+
+}  // extern "C"

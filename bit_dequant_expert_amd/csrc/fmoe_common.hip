@@ -1,0 +1,110 @@
+// fmoe_common.hip -- launchers of the format-independent kernels and the
+// dispatch of format-templated launches to their translation units.
+#include "fmoe_kernels.h"
+
+namespace fmoe {
+
+// ================================================= combine + norm (tokens)
+__global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
+  __shared__ float s_part[kThreads / kWave];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = (int64_t)t * a.H;
+  float ss = 0.f;
+  for (int m = tid; m < a.H; m += kThreads) {
+    float moe = 0.f;
+    for (int i = 0; i < a.k; ++i)
+      moe = fmaf(a.w_ws[(int64_t)t * a.k + i], a.yslot[((int64_t)t * a.kp1 + i) * a.H + m], moe);
+    moe = fmaf(a.g_ws[t], a.yslot[((int64_t)t * a.kp1 + a.k) * a.H + m], moe);
+    const float h = a.resid[row + m] + moe;
+    a.h_out[row + m] = h;
+    if (a.moe_out) a.moe_out[row + m] = moe;
+    ss = fmaf(h, h, ss);
+  }
+  ss = sum_lanes(ss, kWave);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+  const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
+  for (int m = tid; m < a.H; m += kThreads) a.y_out[row + m] = a.gamma[m] * a.h_out[row + m] * inv;
+}
+
+
+namespace {
+
+hipError_t run_variant(const VCall& c) {
+  if (c.f.bits == 4 && c.f.group == 32) return run_variant_4_32(c);
+  if (c.f.bits == 4 && c.f.group == 64) return run_variant_4_64(c);
+  if (c.f.bits == 2 && c.f.group == 32) return run_variant_2_32(c);
+  if (c.f.bits == 2 && c.f.group == 64) return run_variant_2_64(c);
+  return hipErrorInvalidValue;
+}
+
+VCall make_call(VCall::Kind kind, QFmt f, int ns, int grid, hipStream_t st) {
+  VCall c{};
+  c.kind = kind;
+  c.f = f;
+  c.ns = ns;
+  c.grid = grid;
+  c.st = st;
+  return c;
+}
+
+}  // namespace
+
+hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t* b, int N,
+                       int K, const float* x, float* y, hipStream_t st) {
+  VCall c = make_call(VCall::GEMV, f, segs_per_lane(K, f.bits), 0, st);
+  c.q = q; c.s = s; c.b = b; c.N = N; c.K = K; c.x = x; c.y = y;
+  return run_variant(c);
+}
+
+hipError_t launch_gateup(QFmt f, const GUArgs& a, int grid, hipStream_t st) {
+  VCall c = make_call(VCall::GATEUP, f, segs_per_lane(a.H, f.bits), grid, st);
+  c.gu = &a;
+  return run_variant(c);
+}
+
+hipError_t launch_down_combine(QFmt f, const DArgs& a, hipStream_t st) {
+  VCall c = make_call(VCall::DOWN_COMBINE, f, segs_per_lane(a.I, f.bits), a.nrb, st);
+  c.d = &a;
+  return run_variant(c);
+}
+
+hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
+  VCall c = make_call(VCall::DOWN_SLOTS, f, segs_per_lane(a.I, f.bits), grid, st);
+  c.d = &a;
+  return run_variant(c);
+}
+
+hipError_t launch_route(const RouteArgs& a, size_t lds_bytes, hipStream_t st) {
+  const int nj_need = (a.H + 255) / 256, v_need = (a.E + 63) / 64;
+  const int grid = a.n_router_wgs + a.n_prep_wgs;
+#define FMOE_RT(NJ, V)                                                                  \
+  if (nj_need <= NJ && v_need <= V) {                                                  \
+    hipLaunchKernelGGL((k_route<NJ, V>), dim3(grid), dim3(kThreads), lds_bytes, st, a); \
+    return hipGetLastError();                                                          \
+  }
+#define FMOE_RV(NJ) FMOE_RT(NJ, 1) FMOE_RT(NJ, 2) FMOE_RT(NJ, 4) FMOE_RT(NJ, 8) FMOE_RT(NJ, 16) FMOE_RT(NJ, 32)
+  FMOE_RV(1) FMOE_RV(2) FMOE_RV(4) FMOE_RV(8) FMOE_RV(16) FMOE_RV(32)
+#undef FMOE_RV
+#undef FMOE_RT
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ffn_prep(int bits, const float* x, int H, uint8_t* xprep, int32_t* act, int maxA,
+                           hipStream_t st) {
+  const int grid = (H / 32 + kThreads / 8 - 1) / (kThreads / 8);
+  if (bits == 4)
+    hipLaunchKernelGGL(k_ffn_prep<4>, dim3(grid), dim3(kThreads), 0, st, x, H, xprep, act, maxA);
+  else
+    hipLaunchKernelGGL(k_ffn_prep<2>, dim3(grid), dim3(kThreads), 0, st, x, H, xprep, act, maxA);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_combine_norm, dim3(a.T), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fmoe

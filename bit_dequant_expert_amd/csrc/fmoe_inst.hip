@@ -1,0 +1,80 @@
+// fmoe_inst.hip -- instantiates the format-templated kernels for one
+// (bits, group) pair, given by FMOE_BITS and FMOE_GROUP at compile time.  The
+// build compiles this file once per pair, in parallel.
+#include "fmoe_kernels.h"
+
+#if !defined(FMOE_BITS) || !defined(FMOE_GROUP)
+#error "FMOE_BITS and FMOE_GROUP must be defined"
+#endif
+
+#define FMOE_CAT2(a, b, c) a##b##_##c
+#define FMOE_CAT(a, b, c) FMOE_CAT2(a, b, c)
+#define FMOE_VARIANT FMOE_CAT(run_variant_, FMOE_BITS, FMOE_GROUP)
+
+namespace fmoe {
+
+namespace {
+
+template <int SB, int NS>
+hipError_t run_one(const VCall& c) {
+  constexpr int B = FMOE_BITS, G = FMOE_GROUP;
+  switch (c.kind) {
+    case VCall::GEMV: {
+      const int rpi = rows_per_iter(c.K, B);
+      int U = c.N / (4 * rpi * 256);
+      U = U < 1 ? 1 : (U > kUMax ? kUMax : U);
+      const int rwg = 4 * rpi * U;
+      const int grid = (c.N + rwg - 1) / rwg;
+      hipLaunchKernelGGL((k_gemv<B, G, SB, NS>), dim3(grid), dim3(kThreads), xprep_bytes(c.K),
+                         c.st, c.q, c.s, c.b, c.N, c.K, c.x, c.y, U);
+      break;
+    }
+    case VCall::GATEUP:
+      if (c.gu->U == 2)
+        hipLaunchKernelGGL((k_gateup<B, G, SB, NS, 2>), dim3(c.grid), dim3(kThreads),
+                           xprep_bytes(c.gu->H), c.st, *c.gu);
+      else
+        hipLaunchKernelGGL((k_gateup<B, G, SB, NS, 1>), dim3(c.grid), dim3(kThreads),
+                           xprep_bytes(c.gu->H), c.st, *c.gu);
+      break;
+    case VCall::DOWN_COMBINE: {
+      const size_t lds = (size_t)c.d->nbatch * xprep_bytes(c.d->I);
+      const dim3 grid(c.d->nrb), blk(kThreads);
+      if (c.d->U == 2) {
+        if (c.d->nbatch > 4)
+          hipLaunchKernelGGL((k_down_combine<B, G, SB, NS, 2, 8>), grid, blk, lds, c.st, *c.d);
+        else
+          hipLaunchKernelGGL((k_down_combine<B, G, SB, NS, 2, 4>), grid, blk, lds, c.st, *c.d);
+      } else {
+        if (c.d->nbatch > 4)
+          hipLaunchKernelGGL((k_down_combine<B, G, SB, NS, 1, 8>), grid, blk, lds, c.st, *c.d);
+        else
+          hipLaunchKernelGGL((k_down_combine<B, G, SB, NS, 1, 4>), grid, blk, lds, c.st, *c.d);
+      }
+      break;
+    }
+    case VCall::DOWN_SLOTS:
+      if (c.d->U == 2)
+        hipLaunchKernelGGL((k_down_slots<B, G, SB, NS, 2>), dim3(c.grid), dim3(kThreads),
+                           xprep_bytes(c.d->I), c.st, *c.d);
+      else
+        hipLaunchKernelGGL((k_down_slots<B, G, SB, NS, 1>), dim3(c.grid), dim3(kThreads),
+                           xprep_bytes(c.d->I), c.st, *c.d);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t FMOE_VARIANT(const VCall& c) {
+#define FMOE_SN(S, N) \
+  if (c.f.sb == S && c.ns == N) return run_one<S, N>(c);
+  FMOE_SN(4, 1) FMOE_SN(4, 2) FMOE_SN(4, 4) FMOE_SN(2, 1) FMOE_SN(2, 2) FMOE_SN(2, 4)
+#undef FMOE_SN
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fmoe

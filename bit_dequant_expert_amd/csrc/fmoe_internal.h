@@ -1,0 +1,167 @@
+// fmoe_internal.h -- kernel argument blocks and launchers shared by the C ABI
+// (fmoe_api.cpp) and the kernels (fmoe_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmoe {
+
+struct QFmt {
+  int bits;   // 2 or 4
+  int group;  // 32 or 64
+  int sb;     // bytes per scale/bias: 4 (fp32) or 2 (bf16)
+};
+
+// Where an expert's nine sections live: expert e's section j is at
+// base + e * stride + off[j].  A slab array uses base = slabs; a single
+// expert given by loose pointers uses base = 0, stride = 0, off = addresses.
+struct ExpertSrc {
+  const uint8_t* base;
+  int64_t stride;
+  int64_t off[9];
+};
+
+// Active-expert list written by the routing kernel, read by the expert kernels:
+//   act[0] = number of active experts, act[1] = number of them on the MFMA path,
+//   then act_e[maxA], act_off[maxA], act_cnt[maxA], mfma[maxA], entries[T*(k+1)].
+// Entry p = t*(k+1) + slot names token t's slot (slot k = the shared expert).
+struct ActView {
+  const int32_t* base;
+  int maxA;
+  __host__ __device__ const int32_t* e() const { return base + 2; }
+  __host__ __device__ const int32_t* off() const { return base + 2 + maxA; }
+  __host__ __device__ const int32_t* cnt() const { return base + 2 + 2 * maxA; }
+  __host__ __device__ const int32_t* mfma() const { return base + 2 + 3 * maxA; }
+  __host__ __device__ const int32_t* entries() const { return base + 2 + 4 * maxA; }
+};
+
+struct RouteArgs {
+  const float* Wr;
+  const float* wsg;        // shared-gate row (router row E) or null
+  const float* x;          // [T, H]
+  int T, H, E, k, rows;    // rows = E (+1 with wsg)
+  int n_router_wgs;
+  double* lg64;            // [T, rows]
+  float* logits_out;       // [T, E] or null
+  int32_t* idx_out;        // [T, k] or null
+  float* w_out;            // [T, k] or null
+  float* w_ws;             // [T, k] or null (internal copy for the combine)
+  float* g_ws;             // [T] or null
+  int* counter;            // self-resetting completion counter
+  int32_t* act;            // active list (layer mode) or null
+  int maxA, kp1, mfma_thr;
+  uint8_t* xprep;          // per-token prepared activations or null
+  int bits;
+  int n_prep_wgs;
+};
+
+struct GUArgs {
+  ExpertSrc src;
+  const int32_t* act;
+  int maxA, kp1, H, I;
+  const uint8_t* xprep;    // per token, xprep_bytes(H) each
+  float* abuf;             // per entry, I floats
+  uint8_t* aprep;          // per entry, xprep_bytes(I)
+  int* ccnt;               // per entry, I/32 counters
+  int nrb, U, mfma_thr;
+};
+
+struct DArgs {
+  ExpertSrc src;
+  const int32_t* act;
+  int maxA, kp1, k, H, I;
+  const uint8_t* aprep;
+  const float* w_ws;
+  const float* g_ws;
+  const float* resid;
+  float* h_out;
+  float* y_out;
+  float* moe_out;
+  const float* gamma;
+  float eps;
+  float* yslot;            // per-entry outputs (slot mode)
+  float* partials;         // per workgroup sum of squares (combine mode)
+  int* ncnt;               // self-resetting counter (combine mode)
+  int nrb, U, mfma_thr;
+  int nbatch;              // active slots staged in LDS at once (combine mode)
+};
+
+struct CombineArgs {
+  int T, H, k, kp1;
+  const float* yslot;
+  const float* w_ws;
+  const float* g_ws;
+  const float* resid;
+  float* h_out;
+  float* y_out;
+  float* moe_out;
+  const float* gamma;
+  float eps;
+};
+
+struct MfmaArgs {
+  ExpertSrc src;
+  const int32_t* act;
+  int maxA, kp1, H, I, T;
+  const uint8_t* xprep;    // gate/up input: per token
+  uint8_t* aprep;          // down input: per entry
+  float* abuf;
+  int* ccnt;
+  float* yslot;
+  int nrb;                 // row blocks per expert
+};
+
+// Bytes of the prepared image of a K-vector: K/2 fp16 pairs + K/32 float4.
+__host__ __device__ constexpr int64_t xprep_bytes(int64_t K) { return 2 * K + (K / 32) * 16; }
+
+inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane reads per row
+  const int S = K * bits / 128;
+  return S >= 64 ? S / 64 : 1;
+}
+
+// One launch of a format-templated kernel; run_variant_<bits>_<group> (one
+// translation unit per pair, compiled in parallel) instantiates the kernels.
+struct VCall {
+  enum Kind { GEMV, GATEUP, DOWN_COMBINE, DOWN_SLOTS, GATEUP_MFMA, DOWN_MFMA } kind;
+  QFmt f;
+  int ns;
+  int grid;
+  hipStream_t st;
+  const uint8_t *q, *s, *b;
+  int N, K;
+  const float* x;
+  float* y;
+  const struct GUArgs* gu;
+  const struct DArgs* d;
+  const struct MfmaArgs* mf;
+};
+hipError_t run_variant_4_32(const VCall& c);
+hipError_t run_variant_4_64(const VCall& c);
+hipError_t run_variant_2_32(const VCall& c);
+hipError_t run_variant_2_64(const VCall& c);
+
+hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t* b, int N,
+                       int K, const float* x, float* y, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, size_t lds_bytes, hipStream_t st);
+hipError_t launch_ffn_prep(int bits, const float* x, int H, uint8_t* xprep, int32_t* act,
+                           int maxA, hipStream_t st);
+hipError_t launch_gateup(QFmt f, const GUArgs& a, int grid, hipStream_t st);
+hipError_t launch_down_combine(QFmt f, const DArgs& a, hipStream_t st);
+hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st);
+hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
+hipError_t launch_gateup_mfma(QFmt f, const MfmaArgs& a, int grid, hipStream_t st);
+hipError_t launch_down_mfma(QFmt f, const MfmaArgs& a, int grid, hipStream_t st);
+
+// Row-block sizing shared by host and launchers.  RPI = rows one wave covers
+// per iteration (64 lanes / lanes per row); each wave of the expert kernels
+// runs U = 2 iterations when RPI <= 2, else 1, so a 4-wave workgroup covers
+// 8 rows (long rows), 16 rows, or 4*RPI rows (short rows).
+inline int rows_per_iter(int K, int bits) {
+  const int S = K * bits / 128;
+  return S >= 64 ? 1 : 64 / S;
+}
+inline int iters_per_wave(int K, int bits) { return rows_per_iter(K, bits) <= 2 ? 2 : 1; }
+inline int rows_per_wg(int K, int bits) { return 4 * rows_per_iter(K, bits) * iters_per_wave(K, bits); }
+
+}  // namespace fmoe

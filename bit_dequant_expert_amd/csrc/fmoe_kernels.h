@@ -1,0 +1,568 @@
+// fmoe_kernels.h -- HIP kernels of the quantised MoE decode layer (gfx950).
+//
+// Page keys:
+//   [WAS]  "Was ist Flash-MoE? 397B-Parameter-KI-Modelle auf einem Laptop
+//          laufen lassen" (a2a-mcp.org, German, and translations)
+//   [HADA] "Flash-MoE - Ein 397-Milliarden-Parameter-Modell auf einem
+//          Notebook ausfuehren" (news.hada.io)
+//
+// Kernels, in the order a layer runs them:
+//   k_route        router GEMV (fp64 accumulation) + shared gate + activation
+//                  prep; the last workgroup picks top-k, softmax weights and
+//                  builds the active-expert list (indices stay on the device)
+//   k_gateup       gathered gate/up dequant-GEMV over the active slabs, SwiGLU
+//                  epilogue; the last writer of each 32-row block prepares it
+//                  as the down projection's input
+//   k_down_combine (one token) gathered down dequant-GEMV over all active
+//                  slabs, weighted combine + sigmoid-gated shared expert +
+//                  residual in registers; last workgroup applies RMSNorm
+//   k_down_slots + k_combine_norm   the same for several tokens
+//   k_gemv         a single dequant-GEMV (fmoe_dequant_gemv)
+#pragma once
+
+#include <limits.h>
+
+#include "fmoe_device.h"
+#include "fmoe_internal.h"
+
+namespace fmoe {
+
+constexpr int kThreads = 256;
+constexpr int kUMax = 4;
+
+
+// =================================================================== gemv
+// [WAS] "3. Handoptimierte Metal Compute-Shader": a tiled 4-bit / 2-bit
+// matrix-vector product with cached inputs and a SIMD reduction.  Here: the
+// workgroup prepares x once in LDS, each lane keeps its slice of it in
+// registers, rows stream through 16-byte loads and wave shuffles reduce.
+template <int BITS, int G, int SB, int NS>
+__global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ q,
+                                                   const uint8_t* __restrict__ s,
+                                                   const uint8_t* __restrict__ b, int N, int K,
+                                                   const float* __restrict__ x,
+                                                   float* __restrict__ y, int U) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  using TileT = Tile<BITS, G, SB, NS>;
+  const RowGeo geo(K, BITS);
+  const int wave = threadIdx.x >> 6;
+  const int rpw = U * geo.RPI;
+  int64_t n = ((int64_t)blockIdx.x * 4 + wave) * rpw + geo.lane_row;
+
+  TileT cur;
+  if (n < N) cur.load(q, s, b, K, n, geo); else cur.zero();
+
+  const int nblk = K / 32;
+  for (int b0 = 0; b0 < nblk; b0 += kThreads / 8) {
+    const int blk = b0 + (threadIdx.x >> 3);
+    prep_blocks<BITS, false>(x, lds, K, blk < nblk ? blk : -1);
+  }
+  __syncthreads();
+  XRegs<BITS, NS> xr;
+  xr.load(lds, K, geo);
+
+  for (int it = 0; it < U; ++it) {
+    TileT nxt;
+    const bool more = it + 1 < U;
+    const int64_t nn = n + geo.RPI;
+    if (more) {
+      if (nn < N) nxt.load(q, s, b, K, nn, geo); else nxt.zero();
+    }
+    const float v = sum_lanes(tile_dot(cur, xr), geo.LPR);
+    if (n < N && geo.lane_seg == 0) y[n] = v;
+    if (more) { cur = nxt; n = nn; }
+  }
+}
+
+// ================================================================== route
+__device__ __forceinline__ uint64_t order_key(double v) {
+  // Monotone map of fp64 to uint64 (larger value -> larger key).
+  const uint64_t b = __double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint64_t max_lanes_u64(uint64_t v) {
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint64_t o = __shfl_xor(v, d);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Exclusive scan of per-thread values over the workgroup (256 threads).
+__device__ __forceinline__ int block_exscan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    if (w < wave) before += scratch[w];
+    total += scratch[w];
+  }
+  __syncthreads();
+  return before + inc - v;
+}
+
+// [WAS] "Verstaendnis von Mixture-of-Experts (MoE) ...": the router picks k
+// routed experts (plus the shared one) per token.  Logits accumulate in fp64
+// (exact fp32 products) so the selection does not depend on summation order;
+// ties go to the lower index; weights are the softmax over the selected
+// logits (= full softmax renormalised over the selection).
+template <int NJ, int VMAX>
+__global__ __launch_bounds__(kThreads) void k_route(RouteArgs a) {
+  extern __shared__ __align__(16) int lds_i[];
+  __shared__ int s_last;
+  __shared__ int s_scan[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if ((int)blockIdx.x >= a.n_router_wgs) {
+    // ---- activation prep for the gate/up products (independent of routing)
+    if (!a.xprep) return;
+    const int pb = blockIdx.x - a.n_router_wgs;
+    const int per_tok = a.H / 32;
+    const int gb = pb * (kThreads / 8) + (tid >> 3);
+    const bool ok = gb < a.T * per_tok;
+    const int t = ok ? gb / per_tok : 0, blk = ok ? gb % per_tok : -1;
+    const float* src = a.x + (int64_t)t * a.H;
+    uint8_t* dst = a.xprep + (int64_t)t * xprep_bytes(a.H);
+    if (a.bits == 4) prep_blocks<4, false>(src, dst, a.H, blk);
+    else prep_blocks<2, false>(src, dst, a.H, blk);
+    return;
+  }
+
+  // ---- router rows (row E is the shared-expert gate vector)
+  {
+    const int e = blockIdx.x * 4 + wave;
+    if (e < a.rows) {
+      const float* wrow = (e < a.E) ? a.Wr + (int64_t)e * a.H : a.wsg;
+      const int nf4 = a.H / 4;
+      float4 wv[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int f = j * kWave + lane;
+        wv[j] = f < nf4 ? reinterpret_cast<const float4*>(wrow)[f] : make_float4(0, 0, 0, 0);
+      }
+      for (int t = 0; t < a.T; ++t) {
+        const float4* xt = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
+        double acc = 0.0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int f = j * kWave + lane;
+          if (f < nf4) {
+            const float4 xv = xt[f];
+            acc = fma((double)wv[j].x, (double)xv.x, acc);
+            acc = fma((double)wv[j].y, (double)xv.y, acc);
+            acc = fma((double)wv[j].z, (double)xv.z, acc);
+            acc = fma((double)wv[j].w, (double)xv.w, acc);
+          }
+        }
+        acc = sum_lanes64(acc);
+        if (lane == 0) {
+          st_agent(a.lg64 + (int64_t)t * a.rows + e, acc);
+          if (a.logits_out && e < a.E) a.logits_out[(int64_t)t * a.E + e] = (float)acc;
+        }
+      }
+    }
+  }
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) s_last = (add_agent(a.counter, 1) == a.n_router_wgs - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last workgroup: top-k, weights, shared gate, active list
+  int* s_sel = lds_i;  // [T*k]
+  for (int t = wave; t < a.T; t += kThreads / kWave) {
+    const double* lg = a.lg64 + (int64_t)t * a.rows;
+    uint64_t key[VMAX];
+#pragma unroll
+    for (int v = 0; v < VMAX; ++v) {
+      const int e = lane * VMAX + v;
+      key[v] = e < a.E ? order_key(ld_agent(lg + e)) : 0ull;
+    }
+    int sel_e = 0;
+    for (int r = 0; r < a.k; ++r) {
+      uint64_t best = 0;
+      int bv = -1;
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v) {
+        if (key[v] > best) { best = key[v]; bv = v; }
+      }
+      const uint64_t m = max_lanes_u64(best);
+      const uint64_t ball = __ballot(bv >= 0 && best == m);
+      const int L = ball ? __ffsll((unsigned long long)ball) - 1 : 0;
+      const int win = __shfl(lane * VMAX + (bv < 0 ? 0 : bv), L);
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v)
+        if (lane == L && v == bv) key[v] = 0ull;
+      if (lane == r) sel_e = win;
+    }
+    double l = 0.0;
+    if (lane < a.k) l = ld_agent(lg + sel_e);
+    const double l0 = __shfl(l, 0);
+    const double ex = lane < a.k ? exp(l - l0) : 0.0;
+    const double z = sum_lanes64(ex);
+    if (lane < a.k) {
+      const float w = (float)(ex / z);
+      const int64_t o = (int64_t)t * a.k + lane;
+      if (a.idx_out) a.idx_out[o] = sel_e;
+      if (a.w_out) a.w_out[o] = w;
+      if (a.w_ws) a.w_ws[o] = w;
+      s_sel[o] = sel_e;
+    }
+    if (lane == 0 && a.g_ws && a.rows > a.E) {
+      const double gl = ld_agent(lg + a.E);
+      a.g_ws[t] = (float)(1.0 / (1.0 + exp(-gl)));
+    }
+  }
+  __syncthreads();
+
+  if (a.act) {
+    int32_t* act = a.act;
+    int32_t* act_e = act + 2;
+    int32_t* act_off = act_e + a.maxA;
+    int32_t* act_cnt = act_off + a.maxA;
+    int32_t* act_mf = act_cnt + a.maxA;
+    int32_t* entries = act_mf + a.maxA;
+    const int nsel = a.T * a.k;
+    if (a.T == 1) {
+      // One token: the k routed experts in selection order, then the shared one.
+      if (tid <= a.k) {
+        act_e[tid] = tid < a.k ? s_sel[tid] : a.E;
+        act_off[tid] = tid;
+        act_cnt[tid] = 1;
+        entries[tid] = tid;
+      }
+      if (tid == 0) {
+        int nm = 0;
+        for (int i = 0; i <= a.k; ++i)
+          if (1 >= a.mfma_thr) act_mf[nm++] = i;
+        act[0] = a.k + 1;
+        act[1] = nm;
+      }
+    } else {
+      // Group token slots by expert: histogram, exclusive scans, stable scatter.
+      int* s_cnt = s_sel + nsel;   // [E]
+      int* s_pos = s_cnt + a.E;    // [E] rank among active experts
+      int* s_off = s_pos + a.E;    // [E] first entry
+      for (int e = tid; e < a.E; e += kThreads) s_cnt[e] = 0;
+      __syncthreads();
+      for (int j = tid; j < nsel; j += kThreads) atomicAdd(&s_cnt[s_sel[j]], 1);
+      __syncthreads();
+      const int per = (a.E + kThreads - 1) / kThreads;
+      const int e0 = tid * per, e1 = min(a.E, e0 + per);
+      int nf = 0, nc = 0;
+      for (int e = e0; e < e1; ++e) { nf += s_cnt[e] > 0; nc += s_cnt[e]; }
+      int tf, tc;
+      int bf = block_exscan(nf, s_scan, tf);
+      int bc = block_exscan(nc, s_scan, tc);
+      for (int e = e0; e < e1; ++e) {
+        s_pos[e] = bf;
+        s_off[e] = bc;
+        if (s_cnt[e] > 0) {
+          act_e[bf] = e;
+          act_off[bf] = bc;
+          act_cnt[bf] = s_cnt[e];
+          ++bf;
+        }
+        bc += s_cnt[e];
+      }
+      __syncthreads();
+      for (int j = tid; j < nsel; j += kThreads) {
+        const int e = s_sel[j];
+        int rank = 0;
+        for (int jj = 0; jj < j; ++jj) rank += (s_sel[jj] == e);
+        entries[s_off[e] + rank] = (j / a.k) * a.kp1 + (j % a.k);
+      }
+      for (int t = tid; t < a.T; t += kThreads) entries[nsel + t] = t * a.kp1 + a.k;
+      if (tid == 0) {
+        act_e[tf] = a.E;
+        act_off[tf] = nsel;
+        act_cnt[tf] = a.T;
+        int nm = 0;
+        for (int e = 0; e < a.E; ++e)
+          if (s_cnt[e] >= a.mfma_thr) act_mf[nm++] = s_pos[e];
+        if (a.T >= a.mfma_thr) act_mf[nm++] = tf;
+        act[0] = tf + 1;
+        act[1] = nm;
+      }
+    }
+  }
+  if (tid == 0) st_agent(a.counter, 0);
+}
+
+// ============================================================= FFN setup
+// Prepare one activation vector and a one-expert, one-entry active list.
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void k_ffn_prep(const float* x, int H, uint8_t* xprep,
+                                                       int32_t* act, int maxA) {
+  const int nblk = H / 32;
+  const int blk = blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
+  prep_blocks<BITS, false>(x, xprep, H, blk < nblk ? blk : -1);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    act[0] = 1;
+    act[1] = 0;
+    act[2] = 0;                 // expert id 0
+    act[2 + maxA] = 0;          // entries offset
+    act[2 + 2 * maxA] = 1;      // one entry
+    act[2 + 4 * maxA] = 0;      // entry 0
+  }
+}
+
+// ================================================================ gate/up
+// [WAS] "3. Handoptimierte Metal Compute-Shader": dequant matrix-vector
+// products with the SwiGLU activation fused.  One launch covers every active
+// expert: workgroup (a, rb) reads rows rb*RWG.. of gate and up of active
+// expert a and applies them to every token routed there.
+template <int BITS, int G, int SB, int NS, int UT>
+__global__ __launch_bounds__(kThreads) void k_gateup(GUArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_flag[2];
+  using TileT = Tile<BITS, G, SB, NS>;
+  const ActView av{a.act, a.maxA};
+  const int ai = blockIdx.x / a.nrb, rb = blockIdx.x % a.nrb;
+  if (ai >= av.base[0]) return;
+  const int cnt = av.cnt()[ai];
+  if (cnt >= a.mfma_thr) return;
+  const int64_t e = av.e()[ai];
+  const int eoff = av.off()[ai];
+  const uint8_t* base = a.src.base + e * a.src.stride;
+  const uint8_t *gq = base + a.src.off[0], *gs = base + a.src.off[1], *gb = base + a.src.off[2];
+  const uint8_t *uq = base + a.src.off[3], *us = base + a.src.off[4], *ub = base + a.src.off[5];
+
+  const RowGeo geo(a.H, BITS);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rpw = UT * geo.RPI, RWG = 4 * rpw;
+  const int n0 = rb * RWG, wrow0 = n0 + wave * rpw;
+  const int64_t xb = xprep_bytes(a.H), ab = xprep_bytes(a.I);
+  const int nchunk = a.I / 32;
+
+  TileT tg[UT], tu[UT];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) {
+    const int n = wrow0 + u * geo.RPI + geo.lane_row;
+    if (n < a.I) {
+      tg[u].load(gq, gs, gb, a.H, n, geo);
+      tu[u].load(uq, us, ub, a.H, n, geo);
+    } else {
+      tg[u].zero();
+      tu[u].zero();
+    }
+  }
+
+  for (int jt = 0; jt < cnt; ++jt) {
+    const int p = av.entries()[eoff + jt];
+    const int t = p / a.kp1;
+    if (jt > 0) __syncthreads();
+    {
+      const uint4* srcv = reinterpret_cast<const uint4*>(a.xprep + (int64_t)t * xb);
+      uint4* dstv = reinterpret_cast<uint4*>(lds);
+      for (int i = tid; i < xb / 16; i += kThreads) dstv[i] = srcv[i];
+    }
+    __syncthreads();
+    XRegs<BITS, NS> xr;
+    xr.load(lds, a.H, geo);
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      {
+        const float gsum = sum_lanes(tile_dot(tg[u], xr), geo.LPR);
+        const float usum = sum_lanes(tile_dot(tu[u], xr), geo.LPR);
+        const int n = wrow0 + u * geo.RPI + geo.lane_row;
+        if (n < a.I && geo.lane_seg == 0)
+          st_agent(a.abuf + (int64_t)p * a.I + n, silu(gsum) * usum);
+      }
+    }
+    vm_drain();
+    __syncthreads();
+    if (tid == 0) {
+      const int rows_in = RWG < 32 ? RWG : 32;
+      s_flag[0] = -1;
+      s_flag[1] = -1;
+      const int nend = min(n0 + RWG, a.I);
+      for (int c = n0 / 32, qi = 0; c * 32 < nend && qi < 2; ++c, ++qi) {
+        const int old = add_agent(a.ccnt + (int64_t)p * nchunk + c, rows_in);
+        s_flag[qi] = (old + rows_in == 32) ? c : -1;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        const int c = s_flag[qi];
+        if (c >= 0) {
+          prep_blocks<BITS, true>(a.abuf + (int64_t)p * a.I, a.aprep + (int64_t)p * ab, a.I,
+                                  lane < 8 ? c : -1);
+          if (lane == 0) st_agent(a.ccnt + (int64_t)p * nchunk + c, 0);
+        }
+      }
+    }
+  }
+}
+
+// ======================================================== down + combine
+// One token.  [WAS] "3. Handoptimierte Metal Compute-Shader": MoE combine,
+// residual and sigmoid gating in one pass, and a two-phase RMSNorm (sum of
+// squares, then apply); [HADA] "Deferred GPU Expert Compute": the result goes
+// straight on to the next layer.  Workgroup rb owns output rows rb*RWG..; it
+// reads those rows of the down matrix of every active expert (a gather over
+// the slabs), combines them with the routing weights and the shared gate,
+// adds the residual, and the last workgroup to finish normalises.
+template <int BITS, int G, int SB, int NS, int UT, int MAXS>
+__global__ __launch_bounds__(kThreads) void k_down_combine(DArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float s_part[kThreads / kWave];
+  __shared__ int s_last;
+  using TileT = Tile<BITS, G, SB, NS>;
+  const ActView av{a.act, a.maxA};
+  const RowGeo geo(a.I, BITS);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rpw = UT * geo.RPI, RWG = 4 * rpw;
+  const int m0 = blockIdx.x * RWG, wrow0 = m0 + wave * rpw;
+  const int64_t ab = xprep_bytes(a.I);
+  const int nact = av.base[0];
+
+  float acc[UT];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) acc[u] = 0.f;
+
+  for (int s0 = 0; s0 < nact; s0 += a.nbatch) {
+    const int ns = min(a.nbatch, nact - s0);
+    TileT tl[MAXS][UT];
+#pragma unroll
+    for (int sl = 0; sl < MAXS; ++sl) {
+      const uint8_t* base = nullptr;
+      if (sl < ns) base = a.src.base + (int64_t)av.e()[s0 + sl] * a.src.stride;
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        const int m = wrow0 + u * geo.RPI + geo.lane_row;
+        if (sl < ns && m < a.H)
+          tl[sl][u].load(base + a.src.off[6], base + a.src.off[7], base + a.src.off[8], a.I, m,
+                         geo);
+        else
+          tl[sl][u].zero();
+      }
+    }
+    if (s0 > 0) __syncthreads();
+    for (int sl = 0; sl < ns; ++sl) {
+      const int p = av.entries()[av.off()[s0 + sl]];
+      const uint4* srcv = reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab);
+      uint4* dstv = reinterpret_cast<uint4*>(lds + sl * ab);
+      for (int i = tid; i < ab / 16; i += kThreads) dstv[i] = srcv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < MAXS; ++sl) {
+      if (sl < ns) {
+        const int p = av.entries()[av.off()[s0 + sl]];
+        const int t = p / a.kp1, i = p % a.kp1;
+        const float coef = i < a.k ? a.w_ws[(int64_t)t * a.k + i] : a.g_ws[t];
+        XRegs<BITS, NS> xr;
+        xr.load(lds + sl * ab, a.I, geo);
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+          {
+            const float v = sum_lanes(tile_dot(tl[sl][u], xr), geo.LPR);
+            acc[u] = fmaf(coef, v, acc[u]);
+          }
+        }
+      }
+    }
+  }
+
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < UT; ++u) {
+    const int m = wrow0 + u * geo.RPI + geo.lane_row;
+    if (m < a.H && geo.lane_seg == 0) {
+      const float h = a.resid[m] + acc[u];
+      st_agent(a.h_out + m, h);
+      if (a.moe_out) a.moe_out[m] = acc[u];
+      ss = fmaf(h, h, ss);
+    }
+  }
+  ss = sum_lanes(ss, kWave);
+  if (lane == 0) s_part[wave] = ss;
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+    st_agent(a.partials + blockIdx.x, tot);
+    vm_drain();
+    s_last = (add_agent(a.ncnt, 1) == (int)gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last workgroup: total sum of squares in a fixed order, then apply.
+  float part = 0.f;
+  for (int r = tid; r < (int)gridDim.x; r += kThreads) part += ld_agent(a.partials + r);
+  part = sum_lanes(part, kWave);
+  if (lane == 0) s_part[wave] = part;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+  const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
+  for (int m = tid; m < a.H; m += kThreads) a.y_out[m] = a.gamma[m] * ld_agent(a.h_out + m) * inv;
+  if (tid == 0) st_agent(a.ncnt, 0);
+}
+
+// ============================================================ down, slots
+// Several tokens: workgroup (a, rb) reads rows rb*RWG.. of active expert a's
+// down matrix once and applies them to each token routed there, writing one
+// output row block per (token, slot) entry.
+template <int BITS, int G, int SB, int NS, int UT>
+__global__ __launch_bounds__(kThreads) void k_down_slots(DArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  using TileT = Tile<BITS, G, SB, NS>;
+  const ActView av{a.act, a.maxA};
+  const int ai = blockIdx.x / a.nrb, rb = blockIdx.x % a.nrb;
+  if (ai >= av.base[0]) return;
+  const int cnt = av.cnt()[ai];
+  if (cnt >= a.mfma_thr) return;
+  const uint8_t* base = a.src.base + (int64_t)av.e()[ai] * a.src.stride;
+  const int eoff = av.off()[ai];
+  const RowGeo geo(a.I, BITS);
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int rpw = UT * geo.RPI, RWG = 4 * rpw;
+  const int wrow0 = rb * RWG + wave * rpw;
+  const int64_t ab = xprep_bytes(a.I);
+
+  TileT tl[UT];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) {
+    const int m = wrow0 + u * geo.RPI + geo.lane_row;
+    if (m < a.H)
+      tl[u].load(base + a.src.off[6], base + a.src.off[7], base + a.src.off[8], a.I, m, geo);
+    else
+      tl[u].zero();
+  }
+  for (int jt = 0; jt < cnt; ++jt) {
+    const int p = av.entries()[eoff + jt];
+    if (jt > 0) __syncthreads();
+    {
+      const uint4* srcv = reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab);
+      uint4* dstv = reinterpret_cast<uint4*>(lds);
+      for (int i = tid; i < ab / 16; i += kThreads) dstv[i] = srcv[i];
+    }
+    __syncthreads();
+    XRegs<BITS, NS> xr;
+    xr.load(lds, a.I, geo);
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      {
+        const float v = sum_lanes(tile_dot(tl[u], xr), geo.LPR);
+        const int m = wrow0 + u * geo.RPI + geo.lane_row;
+        if (m < a.H && geo.lane_seg == 0) a.yslot[(int64_t)p * a.H + m] = v;
+      }
+    }
+  }
+}
+
+}  // namespace fmoe

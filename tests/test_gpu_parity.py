@@ -1,0 +1,432 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Acceptance (from the method's statement of the target): expert index sets
+bit-exact on every token whose k-th/(k+1)-th logit gap is >= 1e-6 (closer
+tokens are excluded from the index comparison, counted, and their outputs
+checked with the oracle rerun on the GPU's own selection); routing weights
+within 1e-5; moe, h and y within relative L2 2e-3 per token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_dequant_expert_amd as fm
+import oracle
+import synth
+from qtest_util import dequant, pack_codes, rand_qmat, rel_l2, store_sb
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+GAP = 1e-6
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ gemv
+GEMV_SHAPES = [
+    (4, 128, 256), (4, 1024, 4096), (4, 4096, 1024), (4, 1000, 4096), (4, 96, 8192),
+    (4, 70, 2048), (4, 33, 64), (4, 5, 128),
+    (2, 128, 256), (2, 1024, 4096), (2, 4096, 1024), (2, 64, 16384), (2, 50, 64), (2, 3, 512),
+]
+
+
+def recipe_qmat(rng, N, K, bits, G, sb):
+    """Codes and scales drawn as in the configs: 4-bit s ~ U(0.001, 0.01),
+    b = -8s; 2-bit s ~ U(0.002, 0.02), b = -1.5s (bias from the stored scale)."""
+    lo, hi, bm = (0.001, 0.01, -8.0) if bits == 4 else (0.002, 0.02, -1.5)
+    codes = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    s32 = rng.uniform(lo, hi, size=(N, K // G)).astype(np.float32)
+    s = store_sb(s32, sb)
+    sw = synth.bf16_bits_to_f32(s) if sb == 2 else s
+    b = store_sb((sw * np.float32(bm)).astype(np.float32), sb)
+    return codes, pack_codes(codes, bits), s, b
+
+
+def gemv_bound(codes, s, b, sb, G, x):
+    """Per-row bound for fp16-rounded activations (11-bit significand, per-block
+    power-of-two scale) with fp32 accumulation: 2^-11 * sum_k |w_k x_k| plus
+    a small fp32 term."""
+    W = dequant(codes, s, b, sb, G)
+    ax = np.abs(W) @ np.abs(x.astype(np.float64))
+    return 2.0 ** -11 * ax + 1e-6 * ax
+
+
+def run_gemv(q, s, b, bits, G, sb, N, K, x):
+    qd, sd, bd, xd = dev(q), dev(s), dev(b), dev(x)     # alive across the launch
+    yd = torch.empty(N, device="cuda")
+    fm.fmoe_dequant_gemv(fm.qmat(qd, sd, bd, N, K), fm.qformat(bits, G, sb == 2), xd, yd)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("bits,N,K", GEMV_SHAPES)
+@pytest.mark.parametrize("G,sb", [(32, 4), (64, 2), (64, 4), (32, 2)])
+def test_gemv(bits, N, K, G, sb):
+    if K % G:
+        pytest.skip("k not a multiple of the group")
+    note(f"gemv bits={bits} N={N} K={K} G={G} sb={sb}")
+    rng = np.random.default_rng(N * 7 + K + bits + G + sb)
+    codes, q, s, b = recipe_qmat(rng, N, K, bits, G, sb)
+    x = rng.standard_normal(K).astype(np.float32)
+    got = run_gemv(q, s, b, bits, G, sb, N, K, x)
+    ref = oracle.gemv(q, s, b, bits, G, sb, N, K, x.astype(np.float64))
+    assert rel_l2(got, ref) <= TOL
+    assert np.all(np.abs(got - ref) <= gemv_bound(codes, s, b, sb, G, x))
+
+
+@pytest.mark.parametrize("bits,N,K", [(4, 64, 4096), (2, 3, 512), (2, 256, 1024)])
+@pytest.mark.parametrize("G,sb", [(32, 4), (64, 2)])
+def test_gemv_independent_bias(bits, N, K, G, sb):
+    # Biases unrelated to the scales give rows with heavy cancellation; the
+    # error is then judged against the rounding bound, not relative to |y|.
+    note(f"gemv free-bias bits={bits} N={N} K={K} G={G} sb={sb}")
+    rng = np.random.default_rng(N + K + bits + G)
+    codes, q, s, b = rand_qmat(rng, N, K, bits, G, sb)
+    x = rng.standard_normal(K).astype(np.float32)
+    got = run_gemv(q, s, b, bits, G, sb, N, K, x)
+    ref = oracle.gemv(q, s, b, bits, G, sb, N, K, x.astype(np.float64))
+    assert np.all(np.abs(got - ref) <= gemv_bound(codes, s, b, sb, G, x))
+
+
+@pytest.mark.parametrize("scale", [1e-30, 1e-6, 1e6, 1e25])
+def test_gemv_activation_range(scale):
+    # Per-block power-of-two scaling keeps every magnitude inside fp16.
+    note(f"gemv range scale={scale}")
+    rng = np.random.default_rng(3)
+    N, K, G, sb, bits = 256, 4096, 64, 2, 4
+    codes, q, s, b = recipe_qmat(rng, N, K, bits, G, sb)
+    x = (rng.standard_normal(K) * scale).astype(np.float32)
+    x[17] *= 1000.0                                  # an outlier inside one block
+    got = run_gemv(q, s, b, bits, G, sb, N, K, x)
+    ref = oracle.gemv(q, s, b, bits, G, sb, N, K, x.astype(np.float64))
+    assert rel_l2(got, ref) <= TOL
+    assert np.all(np.abs(got - ref) <= gemv_bound(codes, s, b, sb, G, x))
+
+
+def test_gemv_deterministic():
+    rng = np.random.default_rng(4)
+    N, K = 4096, 1024
+    _, q, s, b = recipe_qmat(rng, N, K, 4, 64, 2)
+    W = fm.qmat(dev(q), dev(s), dev(b), N, K)
+    x = dev(rng.standard_normal(K).astype(np.float32))
+    y1, y2 = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+    fm.fmoe_dequant_gemv(W, fm.qformat(4, 64, True), x, y1)
+    fm.fmoe_dequant_gemv(W, fm.qformat(4, 64, True), x, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# ----------------------------------------------------------------- route
+def _route_gpu(Wr, x, k):
+    E, H = Wr.shape
+    T = x.shape[0]
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    lg = torch.empty(T, E, device="cuda")
+    ws = torch.zeros(fm.fmoe_route_workspace_size(T, E), dtype=torch.uint8, device="cuda")
+    fm.fmoe_route_topk(dev(Wr), dev(x), k, idx, w, lg, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
+
+
+def check_routing(idx_g, w_g, ref):
+    excluded = 0
+    for t in range(idx_g.shape[0]):
+        if ref["gap"][t] < GAP:
+            excluded += 1
+            continue
+        assert sorted(idx_g[t].tolist()) == sorted(ref["idx"][t].tolist()), t
+        wr = dict(zip(ref["idx"][t].tolist(), ref["w"][t].tolist()))
+        for e, wv in zip(idx_g[t].tolist(), w_g[t].tolist()):
+            assert abs(wv - wr[e]) <= 1e-5
+    return excluded
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("layer4", 64)])
+def test_route_matches_oracle(name, T):
+    note(f"route {name} T={T}")
+    cfg = synth.CONFIGS[name]
+    Wr = synth.router(cfg, 0)
+    x = synth.activations(cfg, T)
+    idx, w, lg = _route_gpu(Wr, x, cfg.k)
+    ridx, rw, rlg, gap, st = oracle.route(Wr, x, cfg.k)
+    assert st == 0
+    excl = check_routing(idx, w, dict(idx=ridx, w=rw, gap=gap))
+    assert excl <= max(1, T // 100)
+    assert np.allclose(lg, rlg, rtol=1e-6, atol=1e-6)
+    # returned order: logit descending
+    for t in range(T):
+        sel = rlg[t][idx[t]]
+        assert np.all(np.diff(sel) <= 0)
+
+
+def test_route_ties_lower_index_wins():
+    note("route ties")
+    rng = np.random.default_rng(5)
+    E, H, k, T = 64, 256, 4, 8
+    Wr = np.tile(rng.standard_normal((1, H)).astype(np.float32), (E, 1))
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, :] = np.abs(x)
+    idx, w, _ = _route_gpu(Wr, x, k)
+    assert np.all(idx == np.arange(k)) and np.allclose(w, 1.0 / k, atol=1e-7)
+    # a tie across the k boundary: experts 9 and 30 share the 4th-largest logit
+    Wr = (rng.standard_normal((E, H)) * 0.01).astype(np.float32)
+    xx = np.abs(rng.standard_normal((1, H))).astype(np.float32)
+    for e, c in ((3, 0.5), (17, 0.4), (50, 0.3), (9, 0.2), (30, 0.2)):
+        Wr[e] = c
+    idx, w, _ = _route_gpu(Wr, xx, k)
+    assert idx[0].tolist() == [3, 17, 50, 9]
+
+
+# ------------------------------------------------------------------- ffn
+@pytest.mark.parametrize("H,I,bits,G,sb", [(256, 128, 4, 32, 4), (4096, 1024, 4, 64, 2),
+                                           (4096, 1024, 2, 64, 2), (512, 256, 2, 32, 4)])
+def test_expert_ffn(H, I, bits, G, sb):
+    note(f"ffn H={H} I={I} bits={bits} G={G} sb={sb}")
+    spec = synth.QSpec(H, I, bits, G, sb, 0.001, 0.01, -8.0 if bits == 4 else -1.5)
+    off, size = spec.layout()
+    slab = synth.slab(spec, 42, 0, 3)
+    x = synth.normal(42, 0, 7, (H,))
+    sd = dev(slab)
+    base = sd.data_ptr()
+    mats = []
+    for m, (n, k) in enumerate(spec.mats()):
+        mats.append(fm.qmat(base + off[3 * m], base + off[3 * m + 1], base + off[3 * m + 2], n, k))
+    e = fm.fmoe_expert(*mats)
+    fmt = fm.qformat(bits, G, sb == 2)
+    ws = torch.zeros(fm.fmoe_expert_ffn_workspace_size(e, fmt), dtype=torch.uint8, device="cuda")
+    y = torch.empty(H, device="cuda")
+    fm.fmoe_expert_ffn(e, fmt, dev(x), y, ws)
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn(slab, H, I, bits, G, sb, x.astype(np.float64))
+    assert rel_l2(y.cpu().numpy(), ref) <= TOL
+    # the workspace is reusable: a second call gives the same bits
+    y2 = torch.empty(H, device="cuda")
+    fm.fmoe_expert_ffn(e, fmt, dev(x), y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+# ----------------------------------------------------------------- layer
+class GpuLayer:
+    """One layer's inputs resident on the GPU (slabs generated on the device)."""
+
+    def __init__(self, cfg, layer=0, random_gamma=True, device_slabs=True):
+        self.cfg, self.layer = cfg, layer
+        sp = cfg.spec
+        self.off, self.size = sp.layout()
+        self.stride = self.size
+        nbytes = self.stride * (cfg.E + 1)
+        self.slabs = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        if device_slabs:
+            synth.fill_device_slabs(self.slabs.data_ptr(), sp, cfg.seed, layer, 0, cfg.E + 1,
+                                    self.stride)
+        else:
+            self.slabs.copy_(dev(synth.layer_slabs(sp, cfg.seed, layer, cfg.E + 1)))
+        self.Wr = synth.router(cfg, layer)
+        self.wsg = synth.shared_gate(cfg, layer)
+        self.gamma = synth.gamma(cfg, layer, random=random_gamma)
+        self.Wr_d, self.wsg_d, self.g_d = dev(self.Wr), dev(self.wsg), dev(self.gamma)
+        self.fmt = fm.qformat(sp.bits, sp.group, sp.sbytes == 2)
+        self.L = fm.fmoe_layer_desc(cfg.H, cfg.I, cfg.E, cfg.k, self.fmt, self.Wr_d, self.slabs,
+                                    self.stride, self.wsg_d, self.g_d, cfg.eps)
+        self.host_slabs = {}
+        torch.cuda.synchronize()
+
+    def forward(self, x, r, T=None, ws=None):
+        cfg = self.cfg
+        T = x.shape[0] if T is None else T
+        xd = x if torch.is_tensor(x) else dev(x)
+        rd = r if torch.is_tensor(r) else dev(r)
+        out = dict(h=torch.empty(T, cfg.H, device="cuda"), y=torch.empty(T, cfg.H, device="cuda"),
+                   moe=torch.empty(T, cfg.H, device="cuda"),
+                   idx=torch.empty(T, cfg.k, dtype=torch.int32, device="cuda"),
+                   w=torch.empty(T, cfg.k, device="cuda"))
+        if ws is None:
+            ws = torch.zeros(fm.fmoe_workspace_size(self.L, T), dtype=torch.uint8, device="cuda")
+        fm.fmoe_moe_layer_forward(self.L, T, xd, rd, out["h"], out["y"], out["idx"], out["w"],
+                                  out["moe"], ws)
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in out.items()}
+
+    def slab_host(self, e):
+        if e not in self.host_slabs:
+            self.host_slabs[e] = synth.slab(self.cfg.spec, self.cfg.seed, self.layer, e)
+        return self.host_slabs[e]
+
+    def oracle_token(self, x, r, idx, w):
+        cfg, sp = self.cfg, self.cfg.spec
+        return oracle.moe_token([self.slab_host(int(e)) for e in idx], w,
+                                self.slab_host(cfg.E), cfg.H, cfg.I, sp.bits, sp.group,
+                                sp.sbytes, self.wsg, self.gamma, cfg.eps, x, r)
+
+
+def check_layer(gl, x, r, got, tokens):
+    """Compare the GPU outputs of `tokens` with the oracle; returns exclusions."""
+    cfg = gl.cfg
+    ridx, rw, rlg, gap, st = oracle.route(gl.Wr, x[tokens], cfg.k)
+    assert st == 0
+    excluded = 0
+    for j, t in enumerate(tokens):
+        if gap[j] >= GAP:
+            assert sorted(got["idx"][t].tolist()) == sorted(ridx[j].tolist()), t
+            wr = dict(zip(ridx[j].tolist(), rw[j].tolist()))
+            for e, wv in zip(got["idx"][t].tolist(), got["w"][t].tolist()):
+                assert abs(wv - wr[e]) <= 1e-5
+            sel, ww = ridx[j], rw[j]
+        else:
+            excluded += 1
+            sel = got["idx"][t]
+            lv = rlg[j][sel]
+            ww = np.exp(lv - lv.max()) / np.exp(lv - lv.max()).sum()
+        ref = gl.oracle_token(x[t], r[t], sel, ww)
+        for name in ("moe", "h", "y"):
+            err = rel_l2(got[name][t], ref[name])
+            assert err <= TOL, (t, name, err)
+    return excluded
+
+
+def test_layer_tiny_single_tokens():
+    cfg = synth.CONFIGS["tiny"]
+    note("layer tiny T=1")
+    gl = GpuLayer(cfg)
+    x = synth.activations(cfg, 8)
+    r = synth.normal(cfg.seed, 0, 55, (8, cfg.H))
+    ws = torch.zeros(fm.fmoe_workspace_size(gl.L, 1), dtype=torch.uint8, device="cuda")
+    for t in range(8):
+        got = gl.forward(x[t:t + 1], r[t:t + 1], ws=ws)
+        check_layer(gl, x[t:t + 1], r[t:t + 1], got, [0])
+
+
+@pytest.mark.parametrize("T", [2, 5, 16, 32])
+def test_layer_tiny_batched(T):
+    cfg = synth.CONFIGS["tiny"]
+    note(f"layer tiny T={T}")
+    gl = GpuLayer(cfg)
+    x = synth.activations(cfg, T, pool=T)
+    r = synth.normal(cfg.seed, 1, 56, (T, cfg.H))
+    got = gl.forward(x, r)
+    check_layer(gl, x, r, got, list(range(T)))
+
+
+def test_device_generator_matches_host():
+    for name, slabs_to_check in (("tiny", None), ("layer4", [0, 1, 255, 511, 512]),
+                                 ("layer2", [0, 7, 512])):
+        cfg = synth.CONFIGS[name]
+        note(f"generator {name}")
+        sp = cfg.spec
+        off, size = sp.layout()
+        ids = list(range(cfg.E + 1)) if slabs_to_check is None else slabs_to_check
+        buf = torch.empty(size * len(ids), dtype=torch.uint8, device="cuda")
+        for j, e in enumerate(ids):
+            synth.fill_device_slabs(buf.data_ptr() + j * size, sp, cfg.seed, 3, e, 1, size)
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy().reshape(len(ids), size)
+        for j, e in enumerate(ids):
+            assert np.array_equal(host[j], synth.slab(sp, cfg.seed, 3, e)), (name, e)
+
+
+@pytest.fixture(scope="module")
+def layer4():
+    note("generate layer4 slabs on device")
+    return GpuLayer(synth.CONFIGS["layer4"], random_gamma=False)
+
+
+@pytest.fixture(scope="module")
+def layer2():
+    note("generate layer2 slabs on device")
+    return GpuLayer(synth.CONFIGS["layer2"], random_gamma=False)
+
+
+def test_layer4_single_token(layer4):
+    cfg = layer4.cfg
+    x = synth.activations(cfg, 6, pool=1)
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    excl = 0
+    for t in range(6):
+        note(f"layer4 T=1 token {t}")
+        got = layer4.forward(x[t:t + 1], x[t:t + 1], ws=ws)
+        excl += check_layer(layer4, x[t:t + 1], x[t:t + 1], got, [0])
+    assert excl <= 1
+
+
+def test_layer2_single_token(layer2):
+    cfg = layer2.cfg
+    x = synth.activations(cfg, 4, pool=2)
+    for t in range(4):
+        note(f"layer2 T=1 token {t}")
+        got = layer2.forward(x[t:t + 1], x[t:t + 1])
+        check_layer(layer2, x[t:t + 1], x[t:t + 1], got, [0])
+
+
+def test_layer4_batch32_subset(layer4):
+    cfg = layer4.cfg
+    note("layer4 T=32")
+    x = synth.activations(cfg, 32, pool=3)
+    r = synth.normal(cfg.seed, 0, 57, (32, cfg.H))
+    got = layer4.forward(x, r)
+    check_layer(layer4, x, r, got, [0, 13, 31])
+    # every token's routing, not only the checked subset
+    ridx, rw, rlg, gap, _ = oracle.route(layer4.Wr, x, cfg.k)
+    check_routing(got["idx"], got["w"], dict(idx=ridx, w=rw, gap=gap))
+
+
+def test_layer4_correlated_batch(layer4):
+    # Correlated tokens share experts, so some experts see many tokens.
+    cfg = layer4.cfg
+    note("layer4 T=24 correlated")
+    base = synth.activations(cfg, 1, pool=4)
+    x = (base + 0.1 * synth.activations(cfg, 24, pool=5)).astype(np.float32)
+    got = layer4.forward(x, x)
+    counts = np.bincount(got["idx"].ravel(), minlength=cfg.E)
+    assert counts.max() >= 16
+    check_layer(layer4, x, x, got, [0, 23])
+
+
+def test_layer4_deterministic_and_inplace(layer4):
+    cfg = layer4.cfg
+    note("layer4 determinism / in-place")
+    x = synth.activations(cfg, 1, pool=6)
+    a = layer4.forward(x, x)
+    b = layer4.forward(x, x)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    # residual aliases x and h_out aliases residual
+    buf = dev(x)
+    y = torch.empty(1, cfg.H, device="cuda")
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    fm.fmoe_moe_layer_forward(layer4.L, 1, buf, buf, buf, y, None, None, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), a["h"])
+    assert np.array_equal(y.cpu().numpy(), a["y"])
+
+
+def test_stack_chained_tiny():
+    # Three layers chained on the device (x <- y, r <- h), checked per layer
+    # against the oracle fed the GPU's own layer inputs.
+    cfg = synth.CONFIGS["tiny"]
+    note("tiny stack")
+    layers = [GpuLayer(cfg, layer=l) for l in range(3)]
+    T = 4
+    x = dev(synth.activations(cfg, T, pool=7))
+    r = x.clone()
+    for gl in layers:
+        h = torch.empty_like(x)
+        y = torch.empty_like(x)
+        idx = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, cfg.k, device="cuda")
+        moe = torch.empty_like(x)
+        ws = torch.zeros(fm.fmoe_workspace_size(gl.L, T), dtype=torch.uint8, device="cuda")
+        fm.fmoe_moe_layer_forward(gl.L, T, x, r, h, y, idx, w, moe, ws)
+        torch.cuda.synchronize()
+        got = dict(h=h.cpu().numpy(), y=y.cpu().numpy(), moe=moe.cpu().numpy(),
+                   idx=idx.cpu().numpy(), w=w.cpu().numpy())
+        check_layer(gl, x.cpu().numpy(), r.cpu().numpy(), got, list(range(T)))
+        x, r = y, h
