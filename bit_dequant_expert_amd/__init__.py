@@ -194,8 +194,17 @@ def fmoe_moe_layer_forward(L: fmoe_layer, T: int, x, residual, h_out, y_out, idx
         _stream(stream)))
 
 
+_raw_fwd = None
+
+
 def fmoe_moe_layer_forward_raw(Lp, T, x, residual, h_out, y_out, idx_out, w_out, moe_out,
                                ws, ws_bytes, stream) -> int:
-    """Pointer-level call (ints only) for tight loops; returns the status."""
-    return lib().fmoe_moe_layer_forward(Lp, T, x, residual, h_out, y_out, idx_out, w_out,
-                                        moe_out, ws, ws_bytes, stream)
+    """Pointer-level call (the layer descriptor's address and raw device
+    pointers as ints) for tight launch loops; returns the status."""
+    global _raw_fwd
+    if _raw_fwd is None:
+        P = C.c_void_p
+        proto = C.CFUNCTYPE(C.c_int, P, C.c_int32, P, P, P, P, P, P, P, P, C.c_size_t, P)
+        _raw_fwd = proto(C.cast(lib().fmoe_moe_layer_forward, C.c_void_p).value)
+    return _raw_fwd(Lp, T, x, residual, h_out, y_out, idx_out, w_out, moe_out, ws, ws_bytes,
+                    stream)

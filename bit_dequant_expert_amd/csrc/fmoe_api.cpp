@@ -9,10 +9,12 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "fmoe.h"
 #include "fmoe_internal.h"
+#include "fmoe_fused_args.h"
 
 namespace {
 
@@ -133,7 +135,7 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   w.nrb_d = (H + fmoe::rows_per_wg(I, bits) - 1) / fmoe::rows_per_wg(I, bits);
   const size_t ent = (size_t)T * kp1;
   size_t pos = 0;
-  w.ctr = pos; pos += 256;
+  w.ctr = pos; pos += fmoe::kFusedCtrBytes;
   w.lg64 = pos; pos = align256(pos + (size_t)T * (E + 1) * 8);
   w.w = pos; pos = align256(pos + (size_t)T * k * 4);
   w.g = pos; pos = align256(pos + (size_t)T * 4);
@@ -166,6 +168,13 @@ FfnWs ffn_ws(int H, int I) {
 }
 
 size_t route_ws(int T, int E) { return 256 + align256((size_t)T * E * 8); }
+
+// FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers (debug and
+// cross-checking only).
+bool fused_disabled() {
+  const char* v = getenv("FMOE_NO_FUSED");
+  return v && v[0] == '1';
+}
 
 fmoe_status check_router(int T, int H, int E, int k) {
   if (T < 0) return fail(FMOE_ERR_SHAPE, "T=%d must be >= 0", T);
@@ -375,6 +384,29 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
   src.base = (const uint8_t*)L->slabs;
   src.stride = L->slab_stride;
   memcpy(src.off, off, sizeof off);
+
+  if (T == 1 && fmoe::fused1_supported(H, I, E, f.bits) && !fused_disabled()) {
+    fmoe::FusedArgs fa{};
+    fa.src = src;
+    fa.Wr = L->router_w; fa.wsg = L->shared_gate_w; fa.x = x; fa.resid = residual;
+    fa.gamma = L->norm_w; fa.h_out = h_out; fa.y_out = y_out; fa.moe_out = moe_out;
+    fa.w_out = w_out; fa.idx_out = idx_out; fa.eps = L->norm_eps;
+    fa.H = H; fa.I = I; fa.E = E; fa.k = k;
+    fa.lg64 = (double*)(wsb + W.lg64);
+    fa.abuf = (float*)(wsb + W.abuf);
+    fa.aprep = wsb + W.aprep;
+    fa.ccnt = (int*)(wsb + W.ccnt);
+    fa.partials = (float*)(wsb + W.part);
+    fa.ctr = ctr;
+    fa.nR = (E + 1 + 3) / 4;
+    fa.gu_rows = 8;
+    fa.nGU = kp1 * (I / fa.gu_rows);
+    fa.d_rows = 4 * 2 * fmoe::rows_per_iter(I, f.bits);
+    fa.nD = (H + fa.d_rows - 1) / fa.d_rows;
+    hipError_t fe = fmoe::launch_fused1(f, fa, s);
+    if (fe == hipSuccess) return FMOE_OK;
+    if (fe != hipErrorNotSupported) return hip_fail(fe, "fused layer kernel");
+  }
 
   fmoe::RouteArgs ra{};
   ra.Wr = L->router_w; ra.wsg = L->shared_gate_w; ra.x = x;

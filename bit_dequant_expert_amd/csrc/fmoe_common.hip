@@ -1,6 +1,6 @@
 // fmoe_common.hip -- launchers of the format-independent kernels and the
 // dispatch of format-templated launches to their translation units.
-#include "fmoe_kernels.h"
+#include "fmoe_fused.h"
 
 namespace fmoe {
 
@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
     ss = fmaf(h, h, ss);
   }
   ss = sum_lanes(ss, kWave);
-  if (lane == 0) s_part[wave] = ss;
+  if (lane == kWave - 1) s_part[wave] = ss;
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
@@ -74,6 +74,40 @@ hipError_t launch_down_combine(QFmt f, const DArgs& a, hipStream_t st) {
 hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
   VCall c = make_call(VCall::DOWN_SLOTS, f, segs_per_lane(a.I, f.bits), grid, st);
   c.d = &a;
+  return run_variant(c);
+}
+
+bool fused1_supported(int H, int I, int E, int bits) {
+  const int sh = H * bits / 128, si = I * bits / 128;
+  return (sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64) && E <= 2048 &&
+         H <= 8192 && H % 16 == 0;
+}
+
+hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
+  if (!fused1_supported(a.H, a.I, a.E, f.bits)) return hipErrorNotSupported;
+  const size_t phase1 = (size_t)a.H * 4 + xprep_bytes(a.H) + (size_t)(a.E + 1) * 8;
+  const size_t dstage = (size_t)kFusedMaxSlots * xprep_bytes(a.I);
+  const size_t lds = phase1 > dstage ? phase1 : dstage;
+  const int ns = segs_per_lane(a.H, f.bits);
+  int occ = 1;
+  if (f.bits == 4 && f.group == 32) occ = fused_occupancy_4_32(f.sb, ns, a.E, lds);
+  if (f.bits == 4 && f.group == 64) occ = fused_occupancy_4_64(f.sb, ns, a.E, lds);
+  if (f.bits == 2 && f.group == 32) occ = fused_occupancy_2_32(f.sb, ns, a.E, lds);
+  if (f.bits == 2 && f.group == 64) occ = fused_occupancy_2_64(f.sb, ns, a.E, lds);
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu < 1)
+      n_cu = 256;
+  }
+  const int n_items = a.nR + a.nGU + a.nD;
+  int grid = occ * n_cu;
+  if (grid > n_items) grid = n_items;
+  VCall c = make_call(VCall::FUSED1, f, ns, grid, st);
+  c.fu = &a;
+  c.lds = lds;
   return run_variant(c);
 }
 

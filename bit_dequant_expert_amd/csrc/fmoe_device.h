@@ -69,13 +69,66 @@ __device__ __forceinline__ T ld_agent(const T* p) {
 __device__ __forceinline__ int add_agent(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Weights are read once per layer: nontemporal loads keep them from evicting
+// the kernel's code and the small hot data (activations, counters) from L2.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // s_waitcnt vmcnt(0): every load and store this wave issued has completed.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ------------------------------------------------------------------ shuffles
+// Cross-lane sums on DPP row operations (no LDS round trip).  After
+// sum_lanes(v, width) the group total of each aligned group of `width` lanes
+// (a power of two) is in the group's LAST lane; for width <= 16 every lane of
+// the group holds it.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16 lanes
+constexpr int kDppBcast15 = 0x142;     // lane 15 of row r -> row r+1
+constexpr int kDppBcast31 = 0x143;     // lane 31 -> rows 2 and 3
+
 __device__ __forceinline__ float sum_lanes(float v, int width) {
-  for (int d = 1; d < width; d <<= 1) v += __shfl_xor(v, d);
+  if (width >= 2) v += dpp_f<kDppXor1>(v);
+  if (width >= 4) v += dpp_f<kDppXor2>(v);
+  if (width >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (width >= 16) v += dpp_f<kDppMirror>(v);
+  if (width >= 32) v += dpp_f<kDppBcast15, 0xA>(v);
+  if (width >= 64) v += dpp_f<kDppBcast31, 0xC>(v);
   return v;
+}
+// Sum over the whole wave, returned in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                       __builtin_bit_cast(int, sum_lanes(v, kWave)), kWave - 1));
+}
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  return fmaxf(v, dpp_f<kDppHalfMirror>(v));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  return v + dpp_f<kDppHalfMirror>(v);
 }
 __device__ __forceinline__ double sum_lanes64(double v) {
   for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d);
@@ -97,34 +150,21 @@ __device__ __forceinline__ void pair_slot(int j, int& half_idx, int& p) {
   }
 }
 
-// Prepare up to 8 blocks of 32 elements with one wave: lane L works on elements
-// 4*(L&7) .. +3 of block (L>>3) of the wave's set.  Every lane of the wave must
-// call this (cross-lane shuffles).  `blk` is the block index within the vector
-// this lane group handles (or -1 for none), src points at the vector, dst at
-// its prepared image (pairs then consts) and K is the vector length.
+// Prepare blocks of 32 elements with one wave: lane L works on elements
+// 4*(L&7) .. +3 of block `blk` (the same for the 8 lanes of a group, or -1 for
+// none), whose values it already holds in x.  Every lane of the wave must call
+// this (cross-lane operations).  dst is the prepared image of a K-vector
+// (pairs, then consts).  AGENT: other workgroups will read the image.
 template <int BITS, bool AGENT>
-__device__ __forceinline__ void prep_blocks(const float* src, uint8_t* dst, int K, int blk) {
+__device__ __forceinline__ void prep_x4(const float4& xv, uint8_t* dst, int K, int blk) {
   const int sub = threadIdx.x & 7;
   const bool ok = blk >= 0;
-  float x[4] = {0.f, 0.f, 0.f, 0.f};
-  if (ok) {
-    const float* p = src + 32 * blk + 4 * sub;
-    if (AGENT) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = ld_agent(p + e);
-    } else {
-      const float4 v = *reinterpret_cast<const float4*>(p);
-      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    }
-  }
-  float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 4));
+  const float x[4] = {xv.x, xv.y, xv.z, xv.w};
+  const float m = max8(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
   int sh = 0;
   if (m > 0.f && m <= 3.402823466e38f) {
     int ex;
-    frexpf(m, &ex);                       // m = f * 2^ex, f in [0.5, 1)
+    frexpf(m, &ex);                         // m = f * 2^ex, f in [0.5, 1)
     sh = min(max(ex - 1 - 14, -100), 113);  // scaled block max in [2^14, 2^15)
   }
   uint16_t* halves = reinterpret_cast<uint16_t*>(dst);
@@ -134,20 +174,116 @@ __device__ __forceinline__ void prep_blocks(const float* src, uint8_t* dst, int 
     int hidx, p;
     pair_slot<BITS>(32 * (ok ? blk : 0) + 4 * sub + e, hidx, p);
     const _Float16 h = (_Float16)ldexpf(x[e], -sh - p);
-    if (ok) halves[hidx] = __builtin_bit_cast(uint16_t, h);
+    if (ok) {
+      if (AGENT) st_agent(halves + hidx, __builtin_bit_cast(uint16_t, h));
+      else halves[hidx] = __builtin_bit_cast(uint16_t, h);
+    }
     const float hf = (float)h;
     s1 += hf;
     s2 += ldexpf(hf, p);
   }
-  s1 += __shfl_xor(s1, 1);
-  s1 += __shfl_xor(s1, 2);
-  s1 += __shfl_xor(s1, 4);
-  s2 += __shfl_xor(s2, 1);
-  s2 += __shfl_xor(s2, 2);
-  s2 += __shfl_xor(s2, 4);
+  s1 = sum8(s1);
+  s2 = sum8(s2);
   if (ok && sub == 0) {
-    float4* consts = reinterpret_cast<float4*>(dst + 2 * (int64_t)K);
-    consts[blk] = make_float4(ldexpf(1.f, sh), ldexpf(s1, 10 + sh), ldexpf(s2, sh), 0.f);
+    float* c = reinterpret_cast<float*>(dst + 2 * (int64_t)K) + 4 * blk;
+    const float P = ldexpf(1.f, sh), C = ldexpf(s1, 10 + sh), A = ldexpf(s2, sh);
+    if (AGENT) {
+      st_agent(c + 0, P); st_agent(c + 1, C); st_agent(c + 2, A); st_agent(c + 3, 0.f);
+    } else {
+      *reinterpret_cast<float4*>(c) = make_float4(P, C, A, 0.f);
+    }
+  }
+}
+
+template <bool AGENT>
+__device__ __forceinline__ float4 prep_load(const float* src, int blk) {
+  if (blk < 0) return make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* p = src + 32 * blk + 4 * (threadIdx.x & 7);
+  if (AGENT) {
+    const uint64_t lo = ld_agent(reinterpret_cast<const uint64_t*>(p));
+    const uint64_t hi = ld_agent(reinterpret_cast<const uint64_t*>(p) + 1);
+    return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                       __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+  }
+  return *reinterpret_cast<const float4*>(p);
+}
+
+// One wave-call prepares block blk (see prep_x4), loading it first.
+template <int BITS, bool AGENT>
+__device__ __forceinline__ void prep_blocks(const float* src, uint8_t* dst, int K, int blk) {
+  prep_x4<BITS, false>(prep_load<AGENT>(src, blk), dst, K, blk);
+}
+
+// The whole workgroup (NT threads) prepares nvec K-vectors (vector v at
+// src + v*K, its image at dst + v*xprep_bytes(K), in LDS); the loads of up to
+// 8 passes are issued before any block is processed.  AGENT: the vectors were
+// written by other workgroups of this launch.
+template <int BITS, int NT, bool AGENT>
+__device__ __forceinline__ void prep_vectors(const float* src, uint8_t* dst, int K, int nvec) {
+  constexpr int kPer = NT / 8;   // blocks per pass
+  constexpr int kBatch = 8;      // passes whose loads are issued together
+  const int bpv = K / 32, nblk = bpv * nvec;
+  const int64_t xb = 2 * (int64_t)K + (int64_t)(K / 32) * 16;
+  for (int p0 = 0; p0 * kPer < nblk; p0 += kBatch) {
+    float4 xv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int gb = (p0 + j) * kPer + (threadIdx.x >> 3);
+      const int v = gb / bpv;
+      xv[j] = gb < nblk ? prep_load<AGENT>(src + (int64_t)v * K, gb - v * bpv)
+                        : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if ((p0 + j) * kPer < nblk) {   // uniform over the workgroup
+        const int gb = (p0 + j) * kPer + (threadIdx.x >> 3);
+        const int v = gb < nblk ? gb / bpv : 0;
+        prep_x4<BITS, false>(xv[j], dst + v * xb, K, gb < nblk ? gb - v * bpv : -1);
+      }
+    }
+  }
+}
+
+template <int BITS, int NT, bool AGENT = false>
+__device__ __forceinline__ void prep_vector(const float* src, uint8_t* dst, int K) {
+  prep_vectors<BITS, NT, AGENT>(src, dst, K, 1);
+}
+
+// Copy n16 16-byte words into LDS with the workgroup; each thread issues its
+// loads in batches of 4 before storing, so the round trips overlap.
+__device__ __forceinline__ void copy_to_lds(uint4* dst, const uint4* src, int n16, int nthreads) {
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n16; base += 4 * nthreads) {
+    uint4 t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * nthreads + tid;
+      if (i < n16) t[j] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * nthreads + tid;
+      if (i < n16) dst[i] = t[j];
+    }
+  }
+}
+
+// Same for data another workgroup of this launch wrote (agent-scope loads).
+__device__ __forceinline__ void copy_to_lds_agent(uint64_t* dst, const uint64_t* src, int n8,
+                                                  int nthreads) {
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n8; base += 8 * nthreads) {
+    uint64_t t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * nthreads + tid;
+      if (i < n8) t[j] = ld_agent(src + i);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * nthreads + tid;
+      if (i < n8) dst[i] = t[j];
+    }
   }
 }
 
@@ -231,23 +367,23 @@ struct Tile {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int sg = geo.seg(j);
-      q[j] = *reinterpret_cast<const uint4*>(q0 + n * rb + (int64_t)sg * 16);
+      q[j] = ld_nt(reinterpret_cast<const uint4*>(q0 + n * rb + (int64_t)sg * 16));
       const int64_t gi = n * ng + (int64_t)sg * QF<BITS>::EPS / G;
       if (SB == 2) {
         if (GPS == 1) {
-          s[j][0] = *reinterpret_cast<const uint16_t*>(s0 + 2 * gi);
-          b[j][0] = *reinterpret_cast<const uint16_t*>(b0 + 2 * gi);
+          s[j][0] = ld_nt(reinterpret_cast<const uint16_t*>(s0 + 2 * gi));
+          b[j][0] = ld_nt(reinterpret_cast<const uint16_t*>(b0 + 2 * gi));
         } else {
-          const uint32_t sv = *reinterpret_cast<const uint32_t*>(s0 + 2 * gi);
-          const uint32_t bv = *reinterpret_cast<const uint32_t*>(b0 + 2 * gi);
+          const uint32_t sv = ld_nt(reinterpret_cast<const uint32_t*>(s0 + 2 * gi));
+          const uint32_t bv = ld_nt(reinterpret_cast<const uint32_t*>(b0 + 2 * gi));
           s[j][0] = sv & 0xFFFFu; s[j][GPS - 1] = sv >> 16;
           b[j][0] = bv & 0xFFFFu; b[j][GPS - 1] = bv >> 16;
         }
       } else {
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
-          s[j][g] = *reinterpret_cast<const uint32_t*>(s0 + 4 * (gi + g));
-          b[j][g] = *reinterpret_cast<const uint32_t*>(b0 + 4 * (gi + g));
+          s[j][g] = ld_nt(reinterpret_cast<const uint32_t*>(s0 + 4 * (gi + g)));
+          b[j][g] = ld_nt(reinterpret_cast<const uint32_t*>(b0 + 4 * (gi + g)));
         }
       }
     }

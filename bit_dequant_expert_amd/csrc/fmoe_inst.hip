@@ -1,7 +1,7 @@
 // fmoe_inst.hip -- instantiates the format-templated kernels for one
 // (bits, group) pair, given by FMOE_BITS and FMOE_GROUP at compile time.  The
 // build compiles this file once per pair, in parallel.
-#include "fmoe_kernels.h"
+#include "fmoe_fused.h"
 
 #if !defined(FMOE_BITS) || !defined(FMOE_GROUP)
 #error "FMOE_BITS and FMOE_GROUP must be defined"
@@ -61,13 +61,48 @@ hipError_t run_one(const VCall& c) {
         hipLaunchKernelGGL((k_down_slots<B, G, SB, NS, 1>), dim3(c.grid), dim3(kThreads),
                            xprep_bytes(c.d->I), c.st, *c.d);
       break;
+    case VCall::FUSED1: {
+      if constexpr (NS > 2) {
+        return hipErrorNotSupported;
+      } else {
+        const dim3 blk(kThreads), grid(c.grid);
+        if (c.fu->E <= 512)
+          hipLaunchKernelGGL((k_layer1<B, G, SB, NS, 8>), grid, blk, c.lds, c.st, *c.fu);
+        else
+          hipLaunchKernelGGL((k_layer1<B, G, SB, NS, 32>), grid, blk, c.lds, c.st, *c.fu);
+      }
+      break;
+    }
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Resident workgroups of the fused kernel per CU (queried once per variant).
+template <int SB, int NS, int V>
+int fused_occupancy(size_t lds) {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&k_layer1<FMOE_BITS, FMOE_GROUP, SB, NS, V>),
+            kThreads, lds) != hipSuccess || n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
 }  // namespace
+
+int FMOE_CAT(fused_occupancy_, FMOE_BITS, FMOE_GROUP)(int sb, int ns, int E, size_t lds) {
+  if (sb == 4 && ns == 1) return E <= 512 ? fused_occupancy<4, 1, 8>(lds) : fused_occupancy<4, 1, 32>(lds);
+  if (sb == 4 && ns == 2) return E <= 512 ? fused_occupancy<4, 2, 8>(lds) : fused_occupancy<4, 2, 32>(lds);
+  if (sb == 2 && ns == 1) return E <= 512 ? fused_occupancy<2, 1, 8>(lds) : fused_occupancy<2, 1, 32>(lds);
+  if (sb == 2 && ns == 2) return E <= 512 ? fused_occupancy<2, 2, 8>(lds) : fused_occupancy<2, 2, 32>(lds);
+  return 1;
+}
 
 hipError_t FMOE_VARIANT(const VCall& c) {
 #define FMOE_SN(S, N) \

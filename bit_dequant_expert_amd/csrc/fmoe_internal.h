@@ -100,6 +100,8 @@ struct CombineArgs {
   float eps;
 };
 
+struct FusedArgs;
+
 struct MfmaArgs {
   ExpertSrc src;
   const int32_t* act;
@@ -123,7 +125,7 @@ inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane re
 // One launch of a format-templated kernel; run_variant_<bits>_<group> (one
 // translation unit per pair, compiled in parallel) instantiates the kernels.
 struct VCall {
-  enum Kind { GEMV, GATEUP, DOWN_COMBINE, DOWN_SLOTS, GATEUP_MFMA, DOWN_MFMA } kind;
+  enum Kind { GEMV, GATEUP, DOWN_COMBINE, DOWN_SLOTS, GATEUP_MFMA, DOWN_MFMA, FUSED1 } kind;
   QFmt f;
   int ns;
   int grid;
@@ -135,11 +137,17 @@ struct VCall {
   const struct GUArgs* gu;
   const struct DArgs* d;
   const struct MfmaArgs* mf;
+  const struct FusedArgs* fu;
+  size_t lds;
 };
 hipError_t run_variant_4_32(const VCall& c);
 hipError_t run_variant_4_64(const VCall& c);
 hipError_t run_variant_2_32(const VCall& c);
 hipError_t run_variant_2_64(const VCall& c);
+int fused_occupancy_4_32(int sb, int ns, int E, size_t lds);
+int fused_occupancy_4_64(int sb, int ns, int E, size_t lds);
+int fused_occupancy_2_32(int sb, int ns, int E, size_t lds);
+int fused_occupancy_2_64(int sb, int ns, int E, size_t lds);
 
 hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t* b, int N,
                        int K, const float* x, float* y, hipStream_t st);
@@ -152,6 +160,10 @@ hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st);
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
 hipError_t launch_gateup_mfma(QFmt f, const MfmaArgs& a, int grid, hipStream_t st);
 hipError_t launch_down_mfma(QFmt f, const MfmaArgs& a, int grid, hipStream_t st);
+// One-token layer in one persistent launch; returns hipErrorNotSupported when
+// the row geometry is outside what the fused kernel is instantiated for.
+hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st);
+bool fused1_supported(int H, int I, int E, int bits);
 
 // Row-block sizing shared by host and launchers.  RPI = rows one wave covers
 // per iteration (64 lanes / lanes per row); each wave of the expert kernels

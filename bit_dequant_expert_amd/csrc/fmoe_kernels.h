@@ -52,11 +52,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ q
   TileT cur;
   if (n < N) cur.load(q, s, b, K, n, geo); else cur.zero();
 
-  const int nblk = K / 32;
-  for (int b0 = 0; b0 < nblk; b0 += kThreads / 8) {
-    const int blk = b0 + (threadIdx.x >> 3);
-    prep_blocks<BITS, false>(x, lds, K, blk < nblk ? blk : -1);
-  }
+  prep_vector<BITS, kThreads>(x, lds, K);
   __syncthreads();
   XRegs<BITS, NS> xr;
   xr.load(lds, K, geo);
@@ -69,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ q
       if (nn < N) nxt.load(q, s, b, K, nn, geo); else nxt.zero();
     }
     const float v = sum_lanes(tile_dot(cur, xr), geo.LPR);
-    if (n < N && geo.lane_seg == 0) y[n] = v;
+    if (n < N && geo.lane_seg == geo.LPR - 1) y[n] = v;
     if (more) { cur = nxt; n = nn; }
   }
 }
@@ -146,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteArgs a) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int f = j * kWave + lane;
-        wv[j] = f < nf4 ? reinterpret_cast<const float4*>(wrow)[f] : make_float4(0, 0, 0, 0);
+        wv[j] = f < nf4 ? ld_nt(reinterpret_cast<const float4*>(wrow) + f) : make_float4(0, 0, 0, 0);
       }
       for (int t = 0; t < a.T; ++t) {
         const float4* xt = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
@@ -181,11 +177,14 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteArgs a) {
   for (int t = wave; t < a.T; t += kThreads / kWave) {
     const double* lg = a.lg64 + (int64_t)t * a.rows;
     uint64_t key[VMAX];
+    double lv[VMAX];
 #pragma unroll
-    for (int v = 0; v < VMAX; ++v) {
+    for (int v = 0; v < VMAX; ++v) {   // all loads first (clamped addresses)
       const int e = lane * VMAX + v;
-      key[v] = e < a.E ? order_key(ld_agent(lg + e)) : 0ull;
+      lv[v] = ld_agent(lg + (e < a.E ? e : 0));
     }
+#pragma unroll
+    for (int v = 0; v < VMAX; ++v) key[v] = (lane * VMAX + v) < a.E ? order_key(lv[v]) : 0ull;
     int sel_e = 0;
     for (int r = 0; r < a.k; ++r) {
       uint64_t best = 0;
@@ -360,11 +359,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GUArgs a) {
     const int p = av.entries()[eoff + jt];
     const int t = p / a.kp1;
     if (jt > 0) __syncthreads();
-    {
-      const uint4* srcv = reinterpret_cast<const uint4*>(a.xprep + (int64_t)t * xb);
-      uint4* dstv = reinterpret_cast<uint4*>(lds);
-      for (int i = tid; i < xb / 16; i += kThreads) dstv[i] = srcv[i];
-    }
+    copy_to_lds(reinterpret_cast<uint4*>(lds),
+                reinterpret_cast<const uint4*>(a.xprep + (int64_t)t * xb), (int)(xb / 16), kThreads);
     __syncthreads();
     XRegs<BITS, NS> xr;
     xr.load(lds, a.H, geo);
@@ -374,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GUArgs a) {
         const float gsum = sum_lanes(tile_dot(tg[u], xr), geo.LPR);
         const float usum = sum_lanes(tile_dot(tu[u], xr), geo.LPR);
         const int n = wrow0 + u * geo.RPI + geo.lane_row;
-        if (n < a.I && geo.lane_seg == 0)
+        if (n < a.I && geo.lane_seg == geo.LPR - 1)
           st_agent(a.abuf + (int64_t)p * a.I + n, silu(gsum) * usum);
       }
     }
@@ -451,9 +447,9 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(DArgs a) {
     if (s0 > 0) __syncthreads();
     for (int sl = 0; sl < ns; ++sl) {
       const int p = av.entries()[av.off()[s0 + sl]];
-      const uint4* srcv = reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab);
-      uint4* dstv = reinterpret_cast<uint4*>(lds + sl * ab);
-      for (int i = tid; i < ab / 16; i += kThreads) dstv[i] = srcv[i];
+      copy_to_lds(reinterpret_cast<uint4*>(lds + sl * ab),
+                  reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab), (int)(ab / 16),
+                  kThreads);
     }
     __syncthreads();
 #pragma unroll
@@ -479,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(DArgs a) {
 #pragma unroll
   for (int u = 0; u < UT; ++u) {
     const int m = wrow0 + u * geo.RPI + geo.lane_row;
-    if (m < a.H && geo.lane_seg == 0) {
+    if (m < a.H && geo.lane_seg == geo.LPR - 1) {
       const float h = a.resid[m] + acc[u];
       st_agent(a.h_out + m, h);
       if (a.moe_out) a.moe_out[m] = acc[u];
@@ -487,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(DArgs a) {
     }
   }
   ss = sum_lanes(ss, kWave);
-  if (lane == 0) s_part[wave] = ss;
+  if (lane == kWave - 1) s_part[wave] = ss;
   vm_drain();
   __syncthreads();
   if (tid == 0) {
@@ -504,12 +500,24 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(DArgs a) {
   float part = 0.f;
   for (int r = tid; r < (int)gridDim.x; r += kThreads) part += ld_agent(a.partials + r);
   part = sum_lanes(part, kWave);
-  if (lane == 0) s_part[wave] = part;
+  if (lane == kWave - 1) s_part[wave] = part;
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
   const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
-  for (int m = tid; m < a.H; m += kThreads) a.y_out[m] = a.gamma[m] * ld_agent(a.h_out + m) * inv;
+  for (int m0 = 0; m0 < a.H; m0 += 8 * kThreads) {
+    float hv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {   // all loads first (clamped addresses)
+      const int m = m0 + j * kThreads + tid;
+      hv[j] = ld_agent(a.h_out + (m < a.H ? m : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = m0 + j * kThreads + tid;
+      if (m < a.H) a.y_out[m] = a.gamma[m] * hv[j] * inv;
+    }
+  }
   if (tid == 0) st_agent(a.ncnt, 0);
 }
 
@@ -546,11 +554,8 @@ __global__ __launch_bounds__(kThreads) void k_down_slots(DArgs a) {
   for (int jt = 0; jt < cnt; ++jt) {
     const int p = av.entries()[eoff + jt];
     if (jt > 0) __syncthreads();
-    {
-      const uint4* srcv = reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab);
-      uint4* dstv = reinterpret_cast<uint4*>(lds);
-      for (int i = tid; i < ab / 16; i += kThreads) dstv[i] = srcv[i];
-    }
+    copy_to_lds(reinterpret_cast<uint4*>(lds),
+                reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab), (int)(ab / 16), kThreads);
     __syncthreads();
     XRegs<BITS, NS> xr;
     xr.load(lds, a.I, geo);
@@ -559,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void k_down_slots(DArgs a) {
       {
         const float v = sum_lanes(tile_dot(tl[u], xr), geo.LPR);
         const int m = wrow0 + u * geo.RPI + geo.lane_row;
-        if (m < a.H && geo.lane_seg == 0) a.yslot[(int64_t)p * a.H + m] = v;
+        if (m < a.H && geo.lane_seg == geo.LPR - 1) a.yslot[(int64_t)p * a.H + m] = v;
       }
     }
   }

@@ -430,3 +430,70 @@ def test_stack_chained_tiny():
                    idx=idx.cpu().numpy(), w=w.cpu().numpy())
         check_layer(gl, x.cpu().numpy(), r.cpu().numpy(), got, list(range(T)))
         x, r = y, h
+
+
+# ------------------------------------------------ one-launch layer kernel
+def test_fused_matches_multilaunch(layer4, monkeypatch):
+    # The one-token layer runs as one persistent launch; FMOE_NO_FUSED=1 forces
+    # the three-launch path.  Both must match the oracle and each other.
+    cfg = layer4.cfg
+    x = synth.activations(cfg, 3, pool=8)
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    for t in range(3):
+        note(f"fused vs multi token {t}")
+        a = layer4.forward(x[t:t + 1], x[t:t + 1], ws=ws)
+        monkeypatch.setenv("FMOE_NO_FUSED", "1")
+        b = layer4.forward(x[t:t + 1], x[t:t + 1], ws=ws)
+        monkeypatch.delenv("FMOE_NO_FUSED")
+        assert np.array_equal(a["idx"], b["idx"])
+        for name in ("moe", "h", "y"):
+            assert rel_l2(a[name], b[name]) <= 1e-4, name
+        check_layer(layer4, x[t:t + 1], x[t:t + 1], a, [0])
+
+
+MID = synth.Config("mid", 2048, 512, 64, 4, synth.QSpec(2048, 512, 4, 32, 4, 0.001, 0.01, -8.0),
+                   2024)
+MID2 = synth.Config("mid2", 4096, 2048, 96, 6, synth.QSpec(4096, 2048, 2, 32, 4, 0.002, 0.02, -1.5),
+                    2025)
+
+
+@pytest.mark.parametrize("cfg", [MID, MID2], ids=["mid4", "mid2"])
+def test_fused_other_shapes(cfg):
+    note(f"fused layer {cfg.name}")
+    gl = GpuLayer(cfg)
+    x = synth.activations(cfg, 4, pool=1)
+    r = synth.normal(cfg.seed, 0, 58, (4, cfg.H))
+    ws = torch.zeros(fm.fmoe_workspace_size(gl.L, 1), dtype=torch.uint8, device="cuda")
+    for t in range(4):
+        got = gl.forward(x[t:t + 1], r[t:t + 1], ws=ws)
+        check_layer(gl, x[t:t + 1], r[t:t + 1], got, [0])
+
+
+def test_layer_graph_replays_match_eager(layer4):
+    # Capture several one-token layers in a HIP graph; every replay, with eager
+    # work and synchronisation in between, must reproduce the eager results.
+    cfg = layer4.cfg
+    note("graph replay")
+    n = 6
+    x = dev(synth.activations(cfg, n, pool=10))
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    h = torch.empty(n, cfg.H, device="cuda")
+    y = torch.empty(n, cfg.H, device="cuda")
+    for t in range(n):
+        fm.fmoe_moe_layer_forward(layer4.L, 1, x[t], x[t], h[t], y[t], None, None, None, ws)
+    torch.cuda.synchronize()
+    h_ref, y_ref = h.clone(), y.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for t in range(n):
+            fm.fmoe_moe_layer_forward(layer4.L, 1, x[t], x[t], h[t], y[t], None, None, None, ws,
+                                      stream=torch.cuda.current_stream())
+    for rep in range(4):
+        h.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_ref) and torch.equal(y, y_ref), rep
+        _ = (x * 2).sum().item()      # unrelated eager work between replays
