@@ -120,7 +120,7 @@ int64_t slab_layout(int H, int I, const QFmt& f, int64_t off[9]) {
 
 // ------------------------------------------------------------- workspace
 struct LayerWs {
-  size_t ctr, lg64, w, g, act, xprep, abuf, ccnt, aprep, yslot, part, total;
+  size_t ctr, lg64, w, g, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist, total;
   int maxA, nrb_gu, nrb_d;
 };
 
@@ -145,7 +145,10 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   w.ccnt = pos; pos = align256(pos + ent * (I / 32) * 4);
   w.aprep = pos; pos = align256(pos + ent * fmoe::xprep_bytes(I));
   w.yslot = pos; pos = align256(pos + (T > 1 ? ent * H * 4 : 0));
-  w.part = pos; pos = align256(pos + (size_t)w.nrb_d * 4);
+  w.gh = pos; pos = align256(pos + (T == 1 ? (size_t)H * 4 : 0));
+  const int nd_fused = (H + fmoe::fused_d_rows(I, bits) - 1) / fmoe::fused_d_rows(I, bits);
+  w.part = pos; pos = align256(pos + (size_t)(nd_fused > w.nrb_d ? nd_fused : w.nrb_d) * 4);
+  w.dlist = pos; pos = align256(pos + (T == 1 ? (size_t)nd_fused * 4 : 0));
   w.total = pos;
   return w;
 }
@@ -394,15 +397,17 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     fa.H = H; fa.I = I; fa.E = E; fa.k = k;
     fa.lg64 = (double*)(wsb + W.lg64);
     fa.abuf = (float*)(wsb + W.abuf);
-    fa.aprep = wsb + W.aprep;
-    fa.ccnt = (int*)(wsb + W.ccnt);
+    fa.gh = (float*)(wsb + W.gh);
     fa.partials = (float*)(wsb + W.part);
+    fa.dlist = (int*)(wsb + W.dlist);
     fa.ctr = ctr;
-    fa.nR = (E + 1 + 3) / 4;
-    fa.gu_rows = 8;
-    fa.nGU = kp1 * (I / fa.gu_rows);
-    fa.d_rows = 4 * 2 * fmoe::rows_per_iter(I, f.bits);
+    fa.nR = (E + 1 + fmoe::kFusedWaves - 1) / fmoe::kFusedWaves;
+    fa.gu_rows = fmoe::fused_gu_rows(H, f.bits);
+    fa.nGUs = I / fa.gu_rows;
+    fa.d_rows = fmoe::fused_d_rows(I, f.bits);
     fa.nD = (H + fa.d_rows - 1) / fa.d_rows;
+    fa.n0 = fa.nR > fa.nGUs ? fa.nR : fa.nGUs;
+    fa.nF = k * fa.nGUs > fa.nD ? k * fa.nGUs : fa.nD;
     hipError_t fe = fmoe::launch_fused1(f, fa, s);
     if (fe == hipSuccess) return FMOE_OK;
     if (fe != hipErrorNotSupported) return hip_fail(fe, "fused layer kernel");

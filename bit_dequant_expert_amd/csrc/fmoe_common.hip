@@ -79,15 +79,16 @@ hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
 
 bool fused1_supported(int H, int I, int E, int bits) {
   const int sh = H * bits / 128, si = I * bits / 128;
-  return (sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64) && E <= 2048 &&
-         H <= 8192 && H % 16 == 0;
+  if (!((sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64) && E <= 2048 &&
+        H <= 8192 && H % 16 == 0 && I % fused_gu_rows(H, bits) == 0))
+    return false;
+  const int dr = fused_d_rows(I, bits);
+  return (H + dr - 1) / dr <= kFusedMaxNormParts;
 }
 
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
   if (!fused1_supported(a.H, a.I, a.E, f.bits)) return hipErrorNotSupported;
-  const size_t phase1 = (size_t)a.H * 4 + xprep_bytes(a.H) + (size_t)(a.E + 1) * 8;
-  const size_t dstage = (size_t)kFusedMaxSlots * xprep_bytes(a.I);
-  const size_t lds = phase1 > dstage ? phase1 : dstage;
+  const size_t lds = fused_lds_bytes(a.H, a.I);
   const int ns = segs_per_lane(a.H, f.bits);
   int occ = 1;
   if (f.bits == 4 && f.group == 32) occ = fused_occupancy_4_32(f.sb, ns, a.E, lds);
@@ -102,7 +103,7 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
         n_cu < 1)
       n_cu = 256;
   }
-  const int n_items = a.nR + a.nGU + a.nD;
+  const int n_items = a.n0 + a.nF;
   int grid = occ * n_cu;
   if (grid > n_items) grid = n_items;
   VCall c = make_call(VCall::FUSED1, f, ns, grid, st);

@@ -86,6 +86,16 @@ __device__ __forceinline__ T ld_nt(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// tid_x() behind an empty asm: values derived from it are computed where
+// they are used.  Persistent loops need this: otherwise the optimiser hoists
+// every lane-dependent address and index of every path in front of the loop
+// and keeps them all live in VGPRs across it.
+__device__ __forceinline__ int tid_x() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // s_waitcnt vmcnt(0): every load and store this wave issued has completed.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -130,6 +140,23 @@ __device__ __forceinline__ float sum8(float v) {
   v += dpp_f<kDppXor2>(v);
   return v + dpp_f<kDppHalfMirror>(v);
 }
+// fp64 sum over the wave on DPP row operations; the total lands in lane 63.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, true);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double sum_lanes_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  v += dpp_f64<kDppBcast15, 0xA>(v);
+  v += dpp_f64<kDppBcast31, 0xC>(v);
+  return v;
+}
 __device__ __forceinline__ double sum_lanes64(double v) {
   for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d);
   return v;
@@ -157,7 +184,7 @@ __device__ __forceinline__ void pair_slot(int j, int& half_idx, int& p) {
 // (pairs, then consts).  AGENT: other workgroups will read the image.
 template <int BITS, bool AGENT>
 __device__ __forceinline__ void prep_x4(const float4& xv, uint8_t* dst, int K, int blk) {
-  const int sub = threadIdx.x & 7;
+  const int sub = tid_x() & 7;
   const bool ok = blk >= 0;
   const float x[4] = {xv.x, xv.y, xv.z, xv.w};
   const float m = max8(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
@@ -195,10 +222,10 @@ __device__ __forceinline__ void prep_x4(const float4& xv, uint8_t* dst, int K, i
   }
 }
 
+// The 4 values of block blk (>= 0) this lane prepares.
 template <bool AGENT>
 __device__ __forceinline__ float4 prep_load(const float* src, int blk) {
-  if (blk < 0) return make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* p = src + 32 * blk + 4 * (threadIdx.x & 7);
+  const float* p = src + 32 * blk + 4 * (tid_x() & 7);
   if (AGENT) {
     const uint64_t lo = ld_agent(reinterpret_cast<const uint64_t*>(p));
     const uint64_t hi = ld_agent(reinterpret_cast<const uint64_t*>(p) + 1);
@@ -208,10 +235,11 @@ __device__ __forceinline__ float4 prep_load(const float* src, int blk) {
   return *reinterpret_cast<const float4*>(p);
 }
 
-// One wave-call prepares block blk (see prep_x4), loading it first.
+// One wave-call prepares block blk (see prep_x4; -1: none), loading it first
+// (block 0 is read in place of none, so the load is never predicated).
 template <int BITS, bool AGENT>
 __device__ __forceinline__ void prep_blocks(const float* src, uint8_t* dst, int K, int blk) {
-  prep_x4<BITS, false>(prep_load<AGENT>(src, blk), dst, K, blk);
+  prep_x4<BITS, false>(prep_load<AGENT>(src, blk < 0 ? 0 : blk), dst, K, blk);
 }
 
 // The whole workgroup (NT threads) prepares nvec K-vectors (vector v at
@@ -228,15 +256,15 @@ __device__ __forceinline__ void prep_vectors(const float* src, uint8_t* dst, int
     float4 xv[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int gb = (p0 + j) * kPer + (threadIdx.x >> 3);
+      const int gb0 = (p0 + j) * kPer + (tid_x() >> 3);
+      const int gb = gb0 < nblk ? gb0 : nblk - 1;   // clamped, never predicated
       const int v = gb / bpv;
-      xv[j] = gb < nblk ? prep_load<AGENT>(src + (int64_t)v * K, gb - v * bpv)
-                        : make_float4(0, 0, 0, 0);
+      xv[j] = prep_load<AGENT>(src + (int64_t)v * K, gb - v * bpv);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if ((p0 + j) * kPer < nblk) {   // uniform over the workgroup
-        const int gb = (p0 + j) * kPer + (threadIdx.x >> 3);
+        const int gb = (p0 + j) * kPer + (tid_x() >> 3);
         const int v = gb < nblk ? gb / bpv : 0;
         prep_x4<BITS, false>(xv[j], dst + v * xb, K, gb < nblk ? gb - v * bpv : -1);
       }
@@ -250,15 +278,18 @@ __device__ __forceinline__ void prep_vector(const float* src, uint8_t* dst, int 
 }
 
 // Copy n16 16-byte words into LDS with the workgroup; each thread issues its
-// loads in batches of 4 before storing, so the round trips overlap.
+// loads in batches of 4 before storing, so the round trips overlap.  Loads
+// past the end read the last word (never a predicated load: predicated loads
+// with their data used at once serialise on a wait each); only stores are
+// predicated.  n16 >= 1.
 __device__ __forceinline__ void copy_to_lds(uint4* dst, const uint4* src, int n16, int nthreads) {
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   for (int base = 0; base < n16; base += 4 * nthreads) {
     uint4 t[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + j * nthreads + tid;
-      if (i < n16) t[j] = src[i];
+      t[j] = src[i < n16 ? i : n16 - 1];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -271,13 +302,13 @@ __device__ __forceinline__ void copy_to_lds(uint4* dst, const uint4* src, int n1
 // Same for data another workgroup of this launch wrote (agent-scope loads).
 __device__ __forceinline__ void copy_to_lds_agent(uint64_t* dst, const uint64_t* src, int n8,
                                                   int nthreads) {
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   for (int base = 0; base < n8; base += 8 * nthreads) {
     uint64_t t[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = base + j * nthreads + tid;
-      if (i < n8) t[j] = ld_agent(src + i);
+      t[j] = ld_agent(src + (i < n8 ? i : n8 - 1));
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -328,6 +359,18 @@ __device__ __forceinline__ void seg_dot<2>(const uint4& w, const uint32_t* xp, f
 }
 
 // ------------------------------------------------------------- row tiles
+// Values the caller guarantees to be equal in every active lane, moved to
+// SGPRs (a pointer keeps its global address space).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const uint8_t* uniform_gptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)uniform_i64((int64_t)reinterpret_cast<uint64_t>(p));
+  return (const uint8_t*)((const __attribute__((address_space(1))) uint8_t*)v);
+}
+
 // Row geometry of a packed matrix as seen by one wave.  S = 16-byte segments
 // per row; LPR = lanes per row = min(S, 64); RPI = rows per wave iteration.
 struct RowGeo {
@@ -336,7 +379,7 @@ struct RowGeo {
     S = K * bits / 128;
     LPR = S < kWave ? S : kWave;
     RPI = kWave / LPR;
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = tid_x() & (kWave - 1);
     lane_row = lane / LPR;
     lane_seg = lane % LPR;
   }
@@ -360,30 +403,39 @@ struct Tile {
   }
 
   // Row n of a matrix with K columns: codes at q0, scales at s0, biases at b0.
+  // n = (a row index that is the same in every lane) + geo.lane_row, and the
+  // three pointers are the same in every lane: the row bases then live in
+  // SGPRs and each load takes a 32-bit per-lane offset (no 64-bit VGPR
+  // address per load).
   __device__ __forceinline__ void load(const uint8_t* q0, const uint8_t* s0, const uint8_t* b0,
                                        int K, int64_t n, const RowGeo& geo) {
-    const int64_t rb = (int64_t)K * BITS / 8;
-    const int64_t ng = K / G;
+    const int rb = K * BITS / 8;
+    const int ng = K / G;
+    const int64_t nu = uniform_i64(n - geo.lane_row);
+    const uint8_t* qr = uniform_gptr(q0 + nu * rb);
+    const uint8_t* sr = uniform_gptr(s0 + nu * ng * SB);
+    const uint8_t* br = uniform_gptr(b0 + nu * ng * SB);
+    const uint32_t lr = (uint32_t)geo.lane_row;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const int sg = geo.seg(j);
-      q[j] = ld_nt(reinterpret_cast<const uint4*>(q0 + n * rb + (int64_t)sg * 16));
-      const int64_t gi = n * ng + (int64_t)sg * QF<BITS>::EPS / G;
+      const uint32_t sg = (uint32_t)geo.seg(j);
+      q[j] = ld_nt(reinterpret_cast<const uint4*>(qr + (lr * (uint32_t)rb + sg * 16u)));
+      const uint32_t go = SB * (lr * (uint32_t)ng + sg * (uint32_t)QF<BITS>::EPS / (uint32_t)G);
       if (SB == 2) {
         if (GPS == 1) {
-          s[j][0] = ld_nt(reinterpret_cast<const uint16_t*>(s0 + 2 * gi));
-          b[j][0] = ld_nt(reinterpret_cast<const uint16_t*>(b0 + 2 * gi));
+          s[j][0] = ld_nt(reinterpret_cast<const uint16_t*>(sr + go));
+          b[j][0] = ld_nt(reinterpret_cast<const uint16_t*>(br + go));
         } else {
-          const uint32_t sv = ld_nt(reinterpret_cast<const uint32_t*>(s0 + 2 * gi));
-          const uint32_t bv = ld_nt(reinterpret_cast<const uint32_t*>(b0 + 2 * gi));
+          const uint32_t sv = ld_nt(reinterpret_cast<const uint32_t*>(sr + go));
+          const uint32_t bv = ld_nt(reinterpret_cast<const uint32_t*>(br + go));
           s[j][0] = sv & 0xFFFFu; s[j][GPS - 1] = sv >> 16;
           b[j][0] = bv & 0xFFFFu; b[j][GPS - 1] = bv >> 16;
         }
       } else {
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
-          s[j][g] = ld_nt(reinterpret_cast<const uint32_t*>(s0 + 4 * (gi + g)));
-          b[j][g] = ld_nt(reinterpret_cast<const uint32_t*>(b0 + 4 * (gi + g)));
+          s[j][g] = ld_nt(reinterpret_cast<const uint32_t*>(sr + go + 4u * g));
+          b[j][g] = ld_nt(reinterpret_cast<const uint32_t*>(br + go + 4u * g));
         }
       }
     }

@@ -4,25 +4,47 @@
 // norm and residual straight to the next layer without a host round trip, and
 // [WAS] "3. Handoptimierte Metal Compute-Shader" fuses each step into a
 // kernel.  On MI355X the one-token layer is latency-bound (tens of MB in a few
-// microseconds), so every step runs inside one launch.  Workgroups take work
-// items in dependency order
+// microseconds), so every step runs inside one launch, and the launch is laid
+// out so that all expert weights are in flight as soon as the routing is known.
 //
-//   router rows (fp64 logits) -> gate/up of the shared expert
-//   -> gate/up of the routed experts -> down + combine + residual (+ RMSNorm)
+// Work items.  Workgroup b first takes item b (no atomic on the way in); the
+// items past the grid are handed out in order from 64 interleaved sub-queues:
 //
-// from 8 interleaved sub-queues (item i lives in sub-queue i mod 8 and each
-// sub-queue hands out its items in increasing order), so the lowest unfinished
-// item is always held by a running workgroup and an item only ever waits for
-// lower items: no deadlock, whatever the number of resident workgroups.
+//   first items   item i = router part i (one fp64 logit row per wave: the E
+//                 router rows, then the shared-expert gate row), published
+//                 at once, + gate/up part i of the shared expert
+//   layer items   item f = gate/up part f of a routed expert (a block of its
+//                 gate and up rows; SwiGLU to a workspace vector)
+//               + down part f (a block of down rows of EVERY active expert,
+//                 combined with the routing weights, plus the residual)
+//
+// A gate/up part needs only x, and for a routed expert the routing.  A layer
+// item issues its gate/up loads and an L2 prefetch of its down part at once,
+// right after the routing is known; it computes its gate/up part and only
+// then needs the SwiGLU outputs of all gate/up parts (whose arrival raises the
+// item flag) for its down part, whose tiles it reloads from L2 together with
+// them.  It waits for the flag only when every item of the queue has been
+// handed out: then each gate/up part is held by a running workgroup that
+// finishes it without waiting on any down part.  Otherwise (fewer resident
+// workgroups than items) it defers its down part to a list worked off once the
+// queue is empty, and the flag also counts every defer decision, so after it
+// the list is complete.  Router parts never wait; routed parts wait for the
+// routing only after every router part was taken.  Workgroups are dispatched
+// in order of their index, so the first items (the router parts) are always
+// running before any item that waits for them, and one resident workgroup per
+// sub-queue (workgroups 0..63) is enough for progress.
 //
 // Hardware facts this layout answers (measured on MI355X): atomics on one
-// address serialise at ~10 ns each and a hot line slows every stream that
-// touches its channel, so every counter is split into 8 sub-counters plus a
-// top counter, each on its own 256-byte line, and phase completion is
+// address serialise at ~11 ns each (far slower while HBM is saturated), so
+// every counter is split into 64 sub-counters plus a top counter, each on its
+// own 256-byte line, and phase completion is
 // broadcast through 64 flags on separate lines (each waiting workgroup polls
-// its own).  Every waiting consumer recomputes the top-k from the published
-// logits (same inputs, same result) instead of waiting for a published
-// choice.  The last workgroup to leave resets counters and flags.
+// its own).  Every consumer recomputes the top-k from the published logits
+// (same inputs, same result) instead of waiting for a published choice.  A
+// load whose data is used at once behind a branch costs a full memory round
+// trip each, so every batch of loads here is unconditional (clamped
+// addresses).  The last down part computes the RMSNorm; the last workgroup to
+// leave resets counters and flags.
 #pragma once
 
 #include "fmoe_fused_args.h"
@@ -30,34 +52,46 @@
 
 namespace fmoe {
 
-constexpr int kFusedMaxSlots = 6;   // active slots whose down tiles are held at once
-constexpr int kFusedUG = 2;         // gate/up rows per wave per item (long rows)
-constexpr int kFusedUD = 2;         // down iterations per wave per item
+constexpr int kFusedMaxSlots = 6;   // active experts whose down tiles are held at once
+constexpr int kNormPer = 16;        // gamma*h values per thread loaded at once by the norm
 constexpr int kSpinLimit = 1 << 22;
 
-// Counter block layout, in 256-byte lines (64 ints) of the workspace.
+// Counter block layout, in 256-byte lines (64 ints) of the workspace.  Every
+// counter is split into kSubs sub-counters on lines of their own (a device-
+// scope atomic on one address serialises at ~11 ns, and far worse while HBM
+// is saturated), then a top counter.
+constexpr int kSubs = 64;
 constexpr int kLine = 64;
-constexpr int kQHeadLine = 0;       // 8 sub-queue heads
-constexpr int kRouterSubLine = 8;   // 8 router arrive sub-counters, then the top counter
-constexpr int kGuSubLine = 17;
-constexpr int kDownSubLine = 26;
-constexpr int kExitSubLine = 35;
-constexpr int kTimeoutLine = 44;
-constexpr int kRouterFlagLine = 48;   // 64 flags
-constexpr int kGuFlagLine = 112;      // 64 flags
+constexpr int kQHeadLine = 0;                         // kSubs sub-queue heads
+constexpr int kStartLine = kQHeadLine + kSubs;        // kSubs started counters
+constexpr int kRouterSubLine = kStartLine + kSubs;    // kSubs subs + top
+constexpr int kItemSubLine = kRouterSubLine + kSubs + 1;
+constexpr int kDownSubLine = kItemSubLine + kSubs + 1;
+constexpr int kExitSubLine = kDownSubLine + kSubs + 1;
+constexpr int kTimeoutLine = kExitSubLine + kSubs + 1;
+constexpr int kDefHeadLine = kTimeoutLine + 1;      // deferred down parts: next one to take
+constexpr int kDefTailLine = kTimeoutLine + 2;      // deferred down parts: how many
+constexpr int kRouterFlagLine = kTimeoutLine + 4;   // 64 flags
+constexpr int kItemFlagLine = kRouterFlagLine + 64; // 64 flags
+static_assert(kItemFlagLine + 64 <= kFusedCtrLines, "counter block too small");
+
+// LDS of one workgroup: [x fp32 | x prepared | down-stage activations].
+inline size_t fused_lds_bytes(int H, int I) {
+  return (size_t)H * 4 + (size_t)xprep_bytes(H) + (size_t)kFusedMaxSlots * xprep_bytes(I);
+}
 
 __device__ __forceinline__ int* ctr_line(int* base, int line) { return base + kLine * line; }
 
 // Arrival number idx of n at a hierarchical counter; true for the very last.
 // Each sub-counter resets itself once its last arrival is in.
 __device__ __forceinline__ bool arrive(int* ctr, int sub_line, int idx, int n) {
-  const int s = idx & 7;
-  const int sub_total = n / 8 + ((s < n % 8) ? 1 : 0);
-  const int nsub = n < 8 ? n : 8;
+  const int s = idx % kSubs;
+  const int sub_total = n / kSubs + ((s < n % kSubs) ? 1 : 0);
+  const int nsub = n < kSubs ? n : kSubs;
   int* sub = ctr_line(ctr, sub_line + s);
   if (add_agent(sub, 1) != sub_total - 1) return false;
   st_agent(sub, 0);
-  int* top = ctr_line(ctr, sub_line + 8);
+  int* top = ctr_line(ctr, sub_line + kSubs);
   if (add_agent(top, 1) != nsub - 1) return false;
   st_agent(top, 0);
   return true;
@@ -73,7 +107,7 @@ __device__ __forceinline__ void wait_flag(int* ctr, int flag_line) {
   int* f = ctr_line(ctr, flag_line + (blockIdx.x & 63));
   int spins = 0;
   while (ld_agent(f) == 0) {
-    __builtin_amdgcn_s_sleep(4);
+    __builtin_amdgcn_s_sleep(2);
     if (++spins > kSpinLimit) {
       st_agent(ctr_line(ctr, kTimeoutLine), 1);
       break;
@@ -81,27 +115,54 @@ __device__ __forceinline__ void wait_flag(int* ctr, int flag_line) {
   }
 }
 
-// ------------------------------------------------------------ wave max (u64)
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, true);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+// Whether every item of the queue is held by a running workgroup: every
+// workgroup has started (so holds its first item, item blockIdx.x) and every
+// later item (n_main - gridDim.x of them, in kSubs sub-queues) was handed out.
+// One wave: lane s reads started counter s and sub-queue head s.
+struct QueueView {
+  int started, head;
+};
+__device__ __forceinline__ QueueView load_queue(int* ctr) {
+  const int s = tid_x() & 63;
+  return {ld_agent(ctr_line(ctr, kStartLine + s)), ld_agent(ctr_line(ctr, kQHeadLine + s))};
 }
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ bool queue_drained(QueueView q, int n_main) {
+  const int s = tid_x() & 63, g = (int)gridDim.x, nd = n_main - g;
+  const int want_started = g / kSubs + (s < g % kSubs ? 1 : 0);
+  const int want_head = nd > 0 ? nd / kSubs + (s < nd % kSubs ? 1 : 0) : 0;
+  return __ballot(q.started < want_started || q.head < want_head) == 0;
+}
 
-// Maximum over the wave, returned in every lane (keys are unsigned; the DPP
-// lanes outside a row mask read 0, which never wins).
+// ------------------------------------------------------------ wave max (u64)
+// Maximum over the wave, returned in every lane, on 32-bit DPP maxima: the
+// high halves first, then the low halves of the lanes holding the highest
+// high half (exact for unsigned keys).  DPP lanes outside a row mask read 0,
+// which never wins.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast15, 0xA, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast31, 0xC, 0xF, true));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = umax64(v, dpp_u64<kDppXor1>(v));
-  v = umax64(v, dpp_u64<kDppXor2>(v));
-  v = umax64(v, dpp_u64<kDppHalfMirror>(v));
-  v = umax64(v, dpp_u64<kDppMirror>(v));
-  v = umax64(v, dpp_u64<kDppBcast15, 0xA>(v));
-  v = umax64(v, dpp_u64<kDppBcast31, 0xC>(v));
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+  const uint32_t hi = (uint32_t)(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+  return ((uint64_t)mh << 32) | ml;
+}
+// The logit a key of order_key was made from.
+__device__ __forceinline__ double key_value(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // Per-workgroup cache of the routing decision.
@@ -111,19 +172,23 @@ struct RouteCache {
   float coef[17];   // routing weights, then the shared gate
 };
 
-// Wave 0: top-k over the logits staged in LDS (ties: lower index), weights =
-// softmax over the selected logits, shared gate = sigmoid of logit E.
+// One wave: top-k of the published logits (ties: lower index), weights =
+// softmax over the selected logits, shared gate = sigmoid of logit E.  Lane
+// L holds logits L*VMAX .. L*VMAX+VMAX-1 in registers (agent-scope loads:
+// other workgroups wrote them).
 template <int VMAX>
-__device__ __forceinline__ void fused_topk(const FusedArgs& a, const double* lg, RouteCache& rc) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void fused_topk(const FusedArgs& a, RouteCache& rc) {
+  const int lane = tid_x() & 63;
   uint64_t key[VMAX];
 #pragma unroll
   for (int v = 0; v < VMAX; ++v) {
     const int e = lane * VMAX + v;
-    const uint64_t kk = order_key(lg[e < a.E ? e : 0]);
-    key[v] = e < a.E ? kk : 0ull;
+    const double l = ld_agent(a.lg64 + (e < a.E ? e : a.E - 1));
+    key[v] = e < a.E ? order_key(l) : 0ull;
   }
+  const double lgE = ld_agent(a.lg64 + a.E);
   int sel_e = 0;
+  uint64_t sel_k = 0;
   for (int r = 0; r < a.k; ++r) {
     uint64_t best = 0;
     int bv = 0;
@@ -138,256 +203,477 @@ __device__ __forceinline__ void fused_topk(const FusedArgs& a, const double* lg,
 #pragma unroll
     for (int v = 0; v < VMAX; ++v)
       if (lane == L && v == bv) key[v] = 0ull;
-    if (lane == r) sel_e = win;
+    if (lane == r) { sel_e = win; sel_k = m; }
   }
-  const double l = lg[lane < a.k ? sel_e : 0];
-  const double l0 = lg[__builtin_amdgcn_readlane(sel_e, 0)];
-  const float ex = lane < a.k ? expf((float)(l - l0)) : 0.f;
+  const double sel_l = key_value(sel_k);
+  const double l0 = readlane_f64(sel_l, 0);
+  const float ex = lane < a.k ? expf((float)(sel_l - l0)) : 0.f;
   const float z = wave_sum(ex);
   if (lane < a.k) {
     rc.sel[lane] = sel_e;
     rc.coef[lane] = ex / z;
   }
-  if (lane == 0) rc.coef[a.k] = 1.f / (1.f + expf(-(float)lg[a.E]));
+  if (lane == 0) rc.coef[a.k] = 1.f / (1.f + expf(-(float)lgE));
 }
 
-template <int BITS, int G, int SB, int NSH, int VMAX>
-__global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_item;
-  __shared__ int s_flag;
-  __shared__ float s_part[kThreads / kWave];
-  __shared__ RouteCache rc;
-  using TileH = Tile<BITS, G, SB, NSH>;
-  using TileI = Tile<BITS, G, SB, 1>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kp1 = a.k + 1;
-  const int64_t xbH = xprep_bytes(a.H), xbI = xprep_bytes(a.I);
-  // LDS: phase-1 regions [x fp32 | x prepared | logits]; the down stage reuses
-  // the first two (a workgroup never returns to phase 1 after a down item).
-  float* lds_x = reinterpret_cast<float*>(lds);
-  uint8_t* lds_xp = lds + (int64_t)a.H * 4;
-  uint8_t* lds_lg = lds_xp + xbH;
-  uint8_t* lds_ap = lds;
-  const int nGUs = a.I / a.gu_rows;               // gate/up items per slot
-  const int n_items = a.nR + a.nGU + a.nD;
-  int* ctr = a.ctr;
-  const int subq = blockIdx.x & 7;
-  bool have_x = false, have_xp = false;
-  if (tid == 0) rc.ready = 0;
+// ------------------------------------------------------------ down parts
+// Tiles of down rows wrow0 + u*RPI + lane_row (u < kFusedUD) of the active
+// experts s0 .. s0+ns-1 (slot k = the shared expert).
+template <int BITS, int G, int SB>
+__device__ __forceinline__ void down_load(Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSlots][kFusedUD],
+                                          const FusedArgs& a, const RouteCache& rc, int wrow0,
+                                          int s0, int ns, const RowGeo& geo) {
+#pragma unroll
+  for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
+    const int slot = s0 + sl;
+    const int64_t e = slot < a.k ? rc.sel[slot < a.k ? slot : 0] : a.E;
+    const uint8_t* base = a.src.base + e * a.src.stride;
+#pragma unroll
+    for (int u = 0; u < kFusedUD; ++u) {
+      const int m = wrow0 + u * geo.RPI + geo.lane_row;
+      if (sl < ns && m < a.H)
+        tl[sl][u].load(base + a.src.off[6], base + a.src.off[7], base + a.src.off[8], a.I, m, geo);
+      else
+        tl[sl][u].zero();
+    }
+  }
+}
 
-  auto ensure_routing = [&]() {
-    if (rc.ready) return;  // workgroup-uniform (shared, read after a barrier)
-    if (tid == 0) wait_flag(ctr, kRouterFlagLine);
-    __syncthreads();
-    copy_to_lds_agent(reinterpret_cast<uint64_t*>(lds_lg),
-                      reinterpret_cast<const uint64_t*>(a.lg64), a.E + 1, kThreads);
-    __syncthreads();
-    if (wave == 0) fused_topk<VMAX>(a, reinterpret_cast<const double*>(lds_lg), rc);
-    __syncthreads();
-    if (tid == 0) rc.ready = 1;
-    __syncthreads();
-  };
-
-  for (;;) {
-    __syncthreads();
-    if (tid == 0) s_item = subq + 8 * add_agent(ctr_line(ctr, kQHeadLine + subq), 1);
-    __syncthreads();
-    const int item = s_item;
-    if (item >= n_items) break;
-
-    if (item < a.nR) {
-      // ------------------------------------------------ router rows (fp64)
-      const int e = item * 4 + wave;
-      const bool live = e <= a.E;
-      const float* wrow = (live && e < a.E) ? a.Wr + (int64_t)e * a.H : a.wsg;
-      const int nf4 = a.H / 4;
-      double acc = 0.0;
-      for (int c0 = 0; c0 < nf4; c0 += 16 * kWave) {
-        float4 wv[16];
+// acc[u] += sum over the batch's experts of coef * (down row . SwiGLU output).
+// The batch's SwiGLU outputs are prepared in LDS first (all threads).
+template <int BITS, int G, int SB>
+__device__ __forceinline__ void down_dot(const Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSlots][kFusedUD],
+                                         float (&acc)[kFusedUD], const FusedArgs& a,
+                                         const RouteCache& rc, uint8_t* lds_ap, int s0, int ns,
+                                         const RowGeo& geo) {
+  const int64_t xbI = xprep_bytes(a.I);
+  prep_vectors<BITS, kThreads, true>(a.abuf + (int64_t)s0 * a.I, lds_ap, a.I, ns);
+  __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int f = c0 + j * kWave + lane;
-          wv[j] = (live && f < nf4) ? ld_nt(reinterpret_cast<const float4*>(wrow) + f)
-                                    : make_float4(0, 0, 0, 0);
-        }
-        if (!have_x) {   // x staging overlaps the row loads
-          copy_to_lds(reinterpret_cast<uint4*>(lds_x), reinterpret_cast<const uint4*>(a.x),
-                      nf4, kThreads);
-          have_x = true;
-          __syncthreads();
-        }
-        if (live) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int f = c0 + j * kWave + lane;
-            if (f < nf4) {
-              const float4 xv = reinterpret_cast<const float4*>(lds_x)[f];
-              acc = fma((double)wv[j].x, (double)xv.x, acc);
-              acc = fma((double)wv[j].y, (double)xv.y, acc);
-              acc = fma((double)wv[j].z, (double)xv.z, acc);
-              acc = fma((double)wv[j].w, (double)xv.w, acc);
-            }
-          }
-        }
-      }
-      acc = sum_lanes64(acc);
-      if (live && lane == 0) st_agent(a.lg64 + e, acc);
-      vm_drain();
-      __syncthreads();
-      if (tid == 0 && arrive(ctr, kRouterSubLine, item, a.nR)) raise_flags(ctr, kRouterFlagLine);
-    } else if (item < a.nR + a.nGU) {
-      // ------------------------------------------------ gate/up + SwiGLU
-      const int g = item - a.nR;
-      const int so = g / nGUs, rb = g % nGUs;
-      const int slot = so == 0 ? a.k : so - 1;          // shared expert first
-      if (slot < a.k) ensure_routing();
-      const int64_t e = slot < a.k ? rc.sel[slot] : a.E;
-      const uint8_t* base = a.src.base + e * a.src.stride;
-      const RowGeo geo(a.H, BITS);
-      const int n0 = rb * a.gu_rows + wave * kFusedUG;
-      TileH tg[kFusedUG], tu[kFusedUG];
-#pragma unroll
-      for (int u = 0; u < kFusedUG; ++u) {
-        tg[u].load(base + a.src.off[0], base + a.src.off[1], base + a.src.off[2], a.H, n0 + u, geo);
-        tu[u].load(base + a.src.off[3], base + a.src.off[4], base + a.src.off[5], a.H, n0 + u, geo);
-      }
-      if (!have_xp) {
-        prep_vector<BITS, kThreads, false>(a.x, lds_xp, a.H);
-        have_xp = true;
-        __syncthreads();
-      }
-      XRegs<BITS, NSH> xr;
-      xr.load(lds_xp, a.H, geo);
-      float* arow = a.abuf + (int64_t)slot * a.I;
-#pragma unroll
-      for (int u = 0; u < kFusedUG; ++u) {
-        const float gs = sum_lanes(tile_dot(tg[u], xr), kWave);
-        const float us = sum_lanes(tile_dot(tu[u], xr), kWave);
-        if (lane == kWave - 1) st_agent(arow + n0 + u, silu(gs) * us);
-      }
-      vm_drain();
-      __syncthreads();
-      if (tid == 0 && arrive(ctr, kGuSubLine, g, a.nGU)) raise_flags(ctr, kGuFlagLine);
-    } else {
-      // ------------------------------------------------ down + combine
-      const int d = item - a.nR - a.nGU;
-      ensure_routing();
-      const RowGeo geo(a.I, BITS);
-      const int rpw = kFusedUD * geo.RPI;
-      const int wrow0 = d * a.d_rows + wave * rpw;
-      float acc[kFusedUD];
-#pragma unroll
-      for (int u = 0; u < kFusedUD; ++u) acc[u] = 0.f;
-      for (int s0 = 0; s0 < kp1; s0 += kFusedMaxSlots) {
-        const int ns = min(kFusedMaxSlots, kp1 - s0);
-        TileI tl[kFusedMaxSlots][kFusedUD];
-#pragma unroll
-        for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
-          const int slot = s0 + sl;
-          const int64_t e = slot < a.k ? rc.sel[slot < a.k ? slot : 0] : a.E;
-          const uint8_t* base = a.src.base + e * a.src.stride;
-#pragma unroll
-          for (int u = 0; u < kFusedUD; ++u) {
-            const int m = wrow0 + u * geo.RPI + geo.lane_row;
-            if (sl < ns && m < a.H)
-              tl[sl][u].load(base + a.src.off[6], base + a.src.off[7], base + a.src.off[8], a.I,
-                             m, geo);
-            else
-              tl[sl][u].zero();
-          }
-        }
-        if (s0 == 0 && tid == 0) wait_flag(ctr, kGuFlagLine);
-        __syncthreads();
-        // prepare this batch's SwiGLU outputs (written by other workgroups)
-        prep_vectors<BITS, kThreads, true>(a.abuf + (int64_t)s0 * a.I, lds_ap, a.I, ns);
-        __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
-          if (sl < ns) {
-            const float coef = rc.coef[s0 + sl];
-            XRegs<BITS, 1> xr;
-            xr.load(lds_ap + sl * xbI, a.I, geo);
-#pragma unroll
-            for (int u = 0; u < kFusedUD; ++u) {
-              const float v = sum_lanes(tile_dot(tl[sl][u], xr), geo.LPR);
-              acc[u] = fmaf(coef, v, acc[u]);
-            }
-          }
-        }
-      }
-      float ss = 0.f;
+  for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
+    if (sl < ns) {
+      const float coef = rc.coef[s0 + sl];
+      XRegs<BITS, 1> xr;
+      xr.load(lds_ap + sl * xbI, a.I, geo);
 #pragma unroll
       for (int u = 0; u < kFusedUD; ++u) {
-        const int m = wrow0 + u * geo.RPI + geo.lane_row;
-        if (m < a.H && geo.lane_seg == geo.LPR - 1) {
-          const float h = a.resid[m] + acc[u];
-          st_agent(a.h_out + m, h);
-          if (a.moe_out) a.moe_out[m] = acc[u];
-          ss = fmaf(h, h, ss);
-        }
-      }
-      ss = sum_lanes(ss, kWave);
-      if (lane == kWave - 1) s_part[wave] = ss;
-      vm_drain();
-      __syncthreads();
-      if (tid == 0) {
-        float tot = 0.f;
-        for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
-        st_agent(a.partials + d, tot);
-        vm_drain();
-        s_flag = arrive(ctr, kDownSubLine, d, a.nD);
-      }
-      __syncthreads();
-      if (s_flag) {
-        // Last down item: RMSNorm over the whole row, routing outputs.
-        float part = 0.f;
-        for (int r0 = 0; r0 < a.nD; r0 += 4 * kThreads) {
-          float pv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = r0 + j * kThreads + tid;
-            pv[j] = ld_agent(a.partials + (r < a.nD ? r : 0));
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (r0 + j * kThreads + tid < a.nD) part += pv[j];
-        }
-        part = sum_lanes(part, kWave);
-        if (lane == kWave - 1) s_part[wave] = part;
-        __syncthreads();
-        float tot = 0.f;
-        for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
-        const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
-        for (int m0 = 0; m0 < a.H; m0 += 8 * kThreads) {
-          float hv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {   // all loads first (clamped addresses)
-            const int m = m0 + j * kThreads + tid;
-            hv[j] = ld_agent(a.h_out + (m < a.H ? m : 0));
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int m = m0 + j * kThreads + tid;
-            if (m < a.H) a.y_out[m] = a.gamma[m] * hv[j] * inv;
-          }
-        }
-        if (tid < a.k) {
-          if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
-          if (a.w_out) a.w_out[tid] = rc.coef[tid];
-        }
+        const float v = sum_lanes(tile_dot(tl[sl][u], xr), geo.LPR);
+        acc[u] = fmaf(coef, v, acc[u]);
       }
     }
   }
+  __syncthreads();   // lds_ap is reused by the next batch
+}
 
-  // Leave; the last workgroup out resets queue heads and flags.
+// The experts from s_begin on, tiles loaded here (deferred parts, and experts
+// past the first kFusedMaxSlots).
+template <int BITS, int G, int SB>
+__device__ __forceinline__ void down_batches(float (&acc)[kFusedUD], const FusedArgs& a,
+                                             const RouteCache& rc, uint8_t* lds_ap, int wrow0,
+                                             int s_begin, const RowGeo& geo) {
+  const int kp1 = a.k + 1;
+  for (int s0 = s_begin; s0 < kp1; s0 += kFusedMaxSlots) {
+    const int ns = min(kFusedMaxSlots, kp1 - s0);
+    Tile<BITS, G, SB, 1> tl[kFusedMaxSlots][kFusedUD];
+    down_load<BITS, G, SB>(tl, a, rc, wrow0, s0, ns, geo);
+    down_dot<BITS, G, SB>(tl, acc, a, rc, lds_ap, s0, ns, geo);
+  }
+}
+
+// Residual and gamma of the part's rows (clamped loads).
+__device__ __forceinline__ void down_vectors(const FusedArgs& a, int wrow0, int rpi, int lane_row,
+                                             float (&rv)[kFusedUD], float (&gv)[kFusedUD]) {
+#pragma unroll
+  for (int u = 0; u < kFusedUD; ++u) {
+    const int m = wrow0 + u * rpi + lane_row;
+    const int mc = m < a.H ? m : a.H - 1;
+    rv[u] = a.resid[mc];
+    gv[u] = a.gamma[mc];
+  }
+}
+
+// h = residual + combined expert output for the part's rows; gamma*h and the
+// part's sum of h^2 are published, and the last part to arrive finishes the
+// RMSNorm and the routing outputs.  Called by the whole workgroup.
+__device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache& rc, int d,
+                                            const float (&acc)[kFusedUD],
+                                            const float (&rv)[kFusedUD],
+                                            const float (&gv)[kFusedUD], int wrow0, int rpi,
+                                            int lane_row, bool writer, float* s_part,
+                                            int& s_flag) {
+  const int tid = tid_x(), wave = tid >> 6, lane = tid & 63;
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < kFusedUD; ++u) {
+    const int m = wrow0 + u * rpi + lane_row;
+    if (m < a.H && writer) {
+      const float h = rv[u] + acc[u];
+      a.h_out[m] = h;
+      st_agent(a.gh + m, gv[u] * h);
+      if (a.moe_out) a.moe_out[m] = acc[u];
+      ss = fmaf(h, h, ss);
+    }
+  }
+  ss = sum_lanes(ss, kWave);
+  if (lane == kWave - 1) s_part[wave] = ss;
+  __syncthreads();
   if (tid == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+    st_agent(a.partials + d, tot);
+  }
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) s_flag = arrive(a.ctr, kDownSubLine, d, a.nD);
+  __syncthreads();
+  if (!s_flag) return;
+  // Last down part: y = (gamma*h) * rms^-1.  The first kNormPer*kThreads values
+  // of gamma*h are loaded together with the partial sums.
+  float hv[kNormPer], pv[kFusedMaxNormParts / kThreads];
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int m = j * kThreads + tid;
+    hv[j] = ld_agent(a.gh + (m < a.H ? m : a.H - 1));
+  }
+#pragma unroll
+  for (int j = 0; j < kFusedMaxNormParts / kThreads; ++j) {
+    const int r = j * kThreads + tid;
+    pv[j] = ld_agent(a.partials + (r < a.nD ? r : a.nD - 1));
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < kFusedMaxNormParts / kThreads; ++j)
+    if (j * kThreads + tid < a.nD) part += pv[j];
+  part = sum_lanes(part, kWave);
+  __syncthreads();
+  if (lane == kWave - 1) s_part[wave] = part;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+  const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
+#pragma unroll
+  for (int j = 0; j < kNormPer; ++j) {
+    const int m = j * kThreads + tid;
+    if (m < a.H) a.y_out[m] = hv[j] * inv;
+  }
+  for (int m0 = kNormPer * kThreads; m0 < a.H; m0 += kNormPer * kThreads) {
+#pragma unroll
+    for (int j = 0; j < kNormPer; ++j) {
+      const int m = m0 + j * kThreads + tid;
+      hv[j] = ld_agent(a.gh + (m < a.H ? m : a.H - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < kNormPer; ++j) {
+      const int m = m0 + j * kThreads + tid;
+      if (m < a.H) a.y_out[m] = hv[j] * inv;
+    }
+  }
+  if (tid < a.k) {
+    if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
+    if (a.w_out) a.w_out[tid] = rc.coef[tid];
+  }
+}
+
+// Touch every 128-byte line of down part d (codes, scales and biases of its
+// rows, every active expert, and its residual and gamma values; at most 128
+// rows per part) with one 4-byte load per line, so that the loads after the
+// item flag hit in L2 (same workgroup, same XCD).  Nothing is
+// held in registers meanwhile; the loads' values are folded into the result,
+// which the caller consumes late.
+template <int BITS, int G, int SB>
+__device__ __forceinline__ uint32_t down_prefetch(const FusedArgs& a, const RouteCache& rc, int d) {
+  const int m0 = d * a.d_rows;
+  const int nrows = min(a.d_rows, a.H - m0);
+  const int64_t rb = (int64_t)a.I * BITS / 8, sbr = (int64_t)(a.I / G) * SB;
+  const int lq = (int)((nrows * rb + 127) / 128), ls = (int)((nrows * sbr + 127) / 128);
+  const int per = lq + 2 * ls, nw = per * (a.k + 1), total = nw + 2;
+  uint32_t acc = 0;
+  for (int l0 = 0; l0 < total; l0 += kThreads) {
+    const int l = l0 + tid_x();
+    if (l >= nw && l < total) {   // residual and gamma of the part's rows
+      acc ^= __float_as_uint((l == nw ? a.resid : a.gamma)[m0]);
+    } else if (l < nw) {
+      const int slot = l / per, r = l - slot * per;
+      const int64_t e = slot < a.k ? rc.sel[slot] : a.E;
+      const uint8_t* base = a.src.base + e * a.src.stride;
+      const uint8_t* p;
+      if (r < lq)
+        p = base + a.src.off[6] + m0 * rb + min((int64_t)r * 128, nrows * rb - 4);
+      else if (r < lq + ls)
+        p = base + a.src.off[7] + m0 * sbr + min((int64_t)(r - lq) * 128, nrows * sbr - 4);
+      else
+        p = base + a.src.off[8] + m0 * sbr + min((int64_t)(r - lq - ls) * 128, nrows * sbr - 4);
+      acc ^= *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  return acc;
+}
+
+// The persistent loop's body is large and its address arithmetic depends on
+// nothing but the arguments and the lane, so the compiler would hoist all of it
+// in front of the loop and keep it live in VGPRs across every path (well over a
+// hundred registers).  Re-reading the arguments through an empty asm at the top
+// of each item makes them opaque there, so that arithmetic stays inside the
+// path that needs it.  (The asm moves nothing: the values live in SGPRs.)
+// Pointers keep their global address space through the asm (a generic pointer
+// would turn every access into a FLAT one, which may alias LDS).
+template <typename T>
+__device__ __forceinline__ void opaque_s(T& v) {
+  asm volatile("" : "+s"(v));
+}
+template <typename T>
+__device__ __forceinline__ void opaque_g(T*& p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  p = (T*)((__attribute__((address_space(1))) T*)v);
+}
+__device__ __forceinline__ void opaque_args(FusedArgs& a) {
+  opaque_g(a.src.base);
+  opaque_g(a.Wr); opaque_g(a.wsg); opaque_g(a.x); opaque_g(a.resid); opaque_g(a.gamma);
+  opaque_g(a.h_out); opaque_g(a.y_out); opaque_g(a.moe_out); opaque_g(a.w_out);
+  opaque_g(a.idx_out); opaque_g(a.lg64); opaque_g(a.abuf); opaque_g(a.gh);
+  opaque_g(a.partials); opaque_g(a.dlist); opaque_g(a.ctr);
+  opaque_s(a.H); opaque_s(a.I); opaque_s(a.E); opaque_s(a.k); opaque_s(a.eps);
+  opaque_s(a.nR); opaque_s(a.nGUs); opaque_s(a.nD); opaque_s(a.n0); opaque_s(a.nF);
+  opaque_s(a.gu_rows); opaque_s(a.d_rows);
+  opaque_s(a.src.stride);
+#pragma unroll
+  for (int m = 0; m < 9; ++m) opaque_s(a.src.off[m]);
+}
+
+template <int BITS, int G, int SB, int NSH, int VMAX>
+__global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_item;
+  __shared__ int s_flag;
+  __shared__ int s_defer;
+  __shared__ uint32_t s_sink;
+  __shared__ float s_part[kThreads / kWave];
+  __shared__ RouteCache rc;
+  using TileH = Tile<BITS, G, SB, NSH>;
+  constexpr int kUG = fused_ug(NSH);
+  const int subq = blockIdx.x % kSubs;
+  bool have_x = false, have_xp = false;   // LDS already holds x / prepared x
+  bool drained = false;                   // wave 0: every queue item handed out
+  bool first = true;                      // thread 0: first item not yet taken
+  bool listing = false;                   // thread 0: now taking deferred down parts
+  int ndef = 0;                           // thread 0: length of the deferred list
+  if (tid_x() == 0) rc.ready = 0;
+
+  for (;;) {
+    FusedArgs a = a_in;
+    opaque_args(a);
+    const int tid = tid_x(), lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kp1 = a.k + 1;
+    float* lds_x = reinterpret_cast<float*>(lds);
+    uint8_t* lds_xp = lds + (int64_t)a.H * 4;
+    uint8_t* lds_ap = lds_xp + xprep_bytes(a.H);
+    const int n_main = a.n0 + a.nF;
+    int* ctr = a.ctr;
+
+    auto ensure_routing = [&]() {
+      if (rc.ready) return;  // workgroup-uniform (shared, read after a barrier)
+      if (wave == 0) {
+        if (lane == 0) wait_flag(ctr, kRouterFlagLine);
+        fused_topk<VMAX>(a, rc);
+        if (lane == 0) rc.ready = 1;
+      }
+      __syncthreads();
+    };
+
+    // Next piece of work: first item blockIdx.x, then item < n_main from the
+    // queue of the items past the grid; once that is empty, n_main + d for
+    // deferred down part d (after the item flag, when the list is complete);
+    // -1 when there is nothing left.
+    __syncthreads();
+    if (tid == 0) {
+      int it = -1;
+      if (first) {
+        first = false;
+        it = blockIdx.x;
+        __hip_atomic_fetch_add(ctr_line(ctr, kStartLine + subq), 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);   // result unused: no round trip
+      } else if (!listing) {
+        it = (int)gridDim.x + subq + kSubs * add_agent(ctr_line(ctr, kQHeadLine + subq), 1);
+        if (it >= n_main) {
+          listing = true;
+          wait_flag(ctr, kItemFlagLine);
+          ndef = ld_agent(ctr_line(ctr, kDefTailLine));
+        }
+      }
+      if (listing) {
+        it = -1;
+        if (ndef > 0) {
+          const int j = add_agent(ctr_line(ctr, kDefHeadLine), 1);
+          if (j < ndef) it = n_main + ld_agent(a.dlist + j);
+        }
+      }
+      s_item = it;
+    }
+    __syncthreads();
+    const int item = s_item;
+    if (item < 0) break;
+
+    int dpart = -1;   // the down part this iteration computes
+    if (item < n_main) {
+      // What the item holds (all workgroup-uniform).  First items: router
+      // part item and shared-expert gate/up part item.  Layer items f: routed
+      // gate/up part f (expert slot f / nGUs) and down part f.
+      int rpart = -1, gslot = -1, gpart = 0, garr = -1;
+      if (item < a.n0) {
+        if (item < a.nR) rpart = item;
+        if (item < a.nGUs) { gslot = a.k; gpart = item; garr = a.nF + item; }
+      } else {
+        const int f = item - a.n0;
+        if (f < a.k * a.nGUs) { gslot = f / a.nGUs; gpart = f - gslot * a.nGUs; }
+        garr = f;
+        if (f < a.nD) dpart = f;
+      }
+      const bool has_gu = gslot >= 0, has_d = dpart >= 0;
+
+      if (rpart >= 0) {
+        // ---------------------------------------------- router rows (fp64)
+        const int e = rpart * kFusedWaves + wave;
+        const bool live = e <= a.E;
+        const float* wrow = (live && e < a.E) ? a.Wr + (int64_t)e * a.H : a.wsg;
+        const int nf4 = a.H / 4;
+        double acc = 0.0;
+        for (int c0 = 0; c0 < nf4; c0 += 16 * kWave) {
+          float4 wv[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int fi = c0 + j * kWave + lane;
+            wv[j] = ld_nt(reinterpret_cast<const float4*>(wrow) + (fi < nf4 ? fi : nf4 - 1));
+          }
+          if (!have_x) {   // x staging overlaps the row loads
+            copy_to_lds(reinterpret_cast<uint4*>(lds_x), reinterpret_cast<const uint4*>(a.x),
+                        nf4, kThreads);
+            have_x = true;
+            __syncthreads();
+          }
+          if (live) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int fi = c0 + j * kWave + lane;
+              if (fi < nf4) {
+                const float4 xv = reinterpret_cast<const float4*>(lds_x)[fi];
+                acc = fma((double)wv[j].x, (double)xv.x, acc);
+                acc = fma((double)wv[j].y, (double)xv.y, acc);
+                acc = fma((double)wv[j].z, (double)xv.z, acc);
+                acc = fma((double)wv[j].w, (double)xv.w, acc);
+              }
+            }
+          }
+        }
+          acc = sum_lanes_f64(acc);
+        if (live && lane == kWave - 1) st_agent(a.lg64 + e, acc);
+        vm_drain();
+        __syncthreads();
+        if (tid == 0 && arrive(ctr, kRouterSubLine, rpart, a.nR))
+          raise_flags(ctr, kRouterFlagLine);
+      }
+
+      // -------------------------------------------- gate/up part + SwiGLU
+      const RowGeo geoH(a.H, BITS);
+      const int n0 = gpart * a.gu_rows + wave * kUG;
+      if (has_gu && !have_xp) {
+        prep_vector<BITS, kThreads, false>(a.x, lds_xp, a.H);
+        have_xp = true;
+      }
+      // Routed gate/up rows and down parts need the routing before any load
+      // (the shared expert's gate/up rows do not).
+      if ((has_gu && gslot < a.k) || has_d) ensure_routing();
+      TileH tg[kUG], tu[kUG];
+      if (has_gu) {
+        const int64_t e = gslot < a.k ? rc.sel[gslot] : a.E;
+        const uint8_t* base = a.src.base + e * a.src.stride;
+#pragma unroll
+        for (int u = 0; u < kUG; ++u) {
+          tg[u].load(base + a.src.off[0], base + a.src.off[1], base + a.src.off[2], a.H, n0 + u,
+                     geoH);
+          tu[u].load(base + a.src.off[3], base + a.src.off[4], base + a.src.off[5], a.H, n0 + u,
+                     geoH);
+        }
+      }
+      QueueView qv{0, 0};
+      const bool check = wave == 0 && has_d && !drained;
+      uint32_t pf = 0;
+      if (has_d) {
+        if (check) qv = load_queue(ctr);   // consumed once the tile loads are out
+        pf = down_prefetch<BITS, G, SB>(a, rc, dpart);
+      }
+      if (check) drained = queue_drained(qv, n_main);
+      if (has_gu) {
+        __syncthreads();   // prepared x visible
+        XRegs<BITS, NSH> xr;
+        xr.load(lds_xp, a.H, geoH);
+        float* arow = a.abuf + (int64_t)gslot * a.I;
+#pragma unroll
+        for (int u = 0; u < kUG; ++u) {
+          const float gs = sum_lanes(tile_dot(tg[u], xr), kWave);
+          const float us = sum_lanes(tile_dot(tu[u], xr), kWave);
+          if (lane == kWave - 1) st_agent(arow + n0 + u, silu(gs) * us);
+        }
+        vm_drain();
+      }
+      if (pf == 0x9E3779B9u) s_sink = pf;   // keeps the prefetch loads (LDS only)
+      if (garr < 0) continue;
+      __syncthreads();
+      if (wave == 0) {
+        bool defer = false;
+        if (has_d && !drained) {
+          drained = queue_drained(load_queue(ctr), n_main);
+          defer = !drained;
+        }
+        if (lane == 0) {
+          s_defer = defer;
+          if (defer) {
+            const int j = add_agent(ctr_line(ctr, kDefTailLine), 1);
+            st_agent(a.dlist + j, dpart);
+            vm_drain();
+          }
+          if (arrive(ctr, kItemSubLine, garr, a.nF + a.nGUs)) raise_flags(ctr, kItemFlagLine);
+        }
+      }
+      __syncthreads();
+      if (!has_d || s_defer) continue;
+      if (tid == 0) wait_flag(ctr, kItemFlagLine);
+      __syncthreads();
+    } else {
+      dpart = item - n_main;   // deferred: the item flag is up already
+      ensure_routing();
+    }
+
+    // -------------------------------------------------- down part
+    {
+      const RowGeo geoI(a.I, BITS);
+      const int wrow0 = dpart * a.d_rows + wave * (kFusedUD * geoI.RPI);
+      float acc[kFusedUD], rv[kFusedUD], gv[kFusedUD];
+#pragma unroll
+      for (int u = 0; u < kFusedUD; ++u) acc[u] = 0.f;
+      down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
+      down_batches<BITS, G, SB>(acc, a, rc, lds_ap, wrow0, 0, geoI);
+      down_finish(a, rc, dpart, acc, rv, gv, wrow0, geoI.RPI, geoI.lane_row,
+                  geoI.lane_seg == geoI.LPR - 1, s_part, s_flag);
+    }
+  }
+
+  // Leave; the last workgroup out resets queue heads, flags and the list.
+  if (tid_x() == 0) {
+    FusedArgs a = a_in;
+    int* ctr = a.ctr;
     vm_drain();
     if (arrive(ctr, kExitSubLine, blockIdx.x, gridDim.x)) {
-      for (int s = 0; s < 8; ++s) st_agent(ctr_line(ctr, kQHeadLine + s), 0);
+      for (int s = 0; s < kSubs; ++s) {
+        st_agent(ctr_line(ctr, kQHeadLine + s), 0);
+        st_agent(ctr_line(ctr, kStartLine + s), 0);
+      }
+      st_agent(ctr_line(ctr, kDefHeadLine), 0);
+      st_agent(ctr_line(ctr, kDefTailLine), 0);
       for (int j = 0; j < 64; ++j) {
         st_agent(ctr_line(ctr, kRouterFlagLine + j), 0);
-        st_agent(ctr_line(ctr, kGuFlagLine + j), 0);
+        st_agent(ctr_line(ctr, kItemFlagLine + j), 0);
       }
     }
   }

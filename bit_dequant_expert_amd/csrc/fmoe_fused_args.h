@@ -8,9 +8,21 @@
 
 namespace fmoe {
 
-// Counter and flag block at the start of the workspace (176 lines of 256 B).
-constexpr int kFusedCtrLines = 176;
+// Counter and flag block at the start of the workspace (520 lines of 256 B).
+constexpr int kFusedCtrLines = 520;
 constexpr size_t kFusedCtrBytes = (size_t)kFusedCtrLines * 256;
+
+// Work-item sizes (4 waves per workgroup).  A gate/up part is UG rows of gate
+// and of up per wave (one expert): UG = 4 when a lane reads one 16-byte
+// segment of a hidden-size row, 2 when it reads two (register budget of two
+// workgroups per CU).  A down part is kFusedUD row iterations per wave over
+// every active expert.
+constexpr int kFusedWaves = 4;
+constexpr int kFusedUD = 1;
+constexpr int kFusedMaxNormParts = 4 * 256;   // down parts the final norm sums
+__host__ __device__ constexpr int fused_ug(int nsh) { return nsh == 1 ? 4 : 2; }
+inline int fused_gu_rows(int H, int bits) { return kFusedWaves * fused_ug(segs_per_lane(H, bits)); }
+inline int fused_d_rows(int I, int bits) { return kFusedWaves * kFusedUD * rows_per_iter(I, bits); }
 
 struct FusedArgs {
   ExpertSrc src;
@@ -27,14 +39,18 @@ struct FusedArgs {
   float eps;
   int H, I, E, k;
   double* lg64;      // [E+1]
-  float* abuf;       // [(k+1) * I]
-  uint8_t* aprep;    // [(k+1) * xprep_bytes(I)]
-  int* ccnt;         // [(k+1) * I/32]
-  float* partials;   // [nD]
-  int* ctr;          // FusedCtr
-  int nR, nGU, nD;   // item counts per phase
-  int gu_rows;       // gate/up rows per item
-  int d_rows;        // down rows per item
+  float* abuf;       // [(k+1) * I]  SwiGLU outputs, slot-major
+  float* gh;         // [H]  gamma * h, read by the final norm
+  float* partials;   // [nD]  sum of h^2 per down part
+  int* dlist;        // [nD]  down parts deferred to the end of the queue
+  int* ctr;          // counter and flag block (kFusedCtrBytes)
+  int nR;            // router parts (kFusedWaves logit rows each)
+  int nGUs;          // gate/up parts per expert (I / gu_rows)
+  int nD;            // down parts
+  int n0;            // first items: router part i and shared gate/up part i
+  int nF;            // layer items: routed gate/up part f and down part f
+  int gu_rows;       // gate/up rows per part
+  int d_rows;        // down rows per part
 };
 
 }  // namespace fmoe

@@ -158,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteArgs a) {
             acc = fma((double)wv[j].w, (double)xv.w, acc);
           }
         }
-        acc = sum_lanes64(acc);
-        if (lane == 0) {
+        acc = sum_lanes_f64(acc);
+        if (lane == kWave - 1) {
           st_agent(a.lg64 + (int64_t)t * a.rows + e, acc);
           if (a.logits_out && e < a.E) a.logits_out[(int64_t)t * a.E + e] = (float)acc;
         }
