@@ -401,12 +401,10 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     fa.partials = (float*)(wsb + W.part);
     fa.dlist = (int*)(wsb + W.dlist);
     fa.ctr = ctr;
-    fa.nR = (E + 1 + fmoe::kFusedWaves - 1) / fmoe::kFusedWaves;
     fa.gu_rows = fmoe::fused_gu_rows(H, f.bits);
     fa.nGUs = I / fa.gu_rows;
     fa.d_rows = fmoe::fused_d_rows(I, f.bits);
     fa.nD = (H + fa.d_rows - 1) / fa.d_rows;
-    fa.n0 = fa.nR > fa.nGUs ? fa.nR : fa.nGUs;
     fa.nF = k * fa.nGUs > fa.nD ? k * fa.nGUs : fa.nD;
     hipError_t fe = fmoe::launch_fused1(f, fa, s);
     if (fe == hipSuccess) return FMOE_OK;

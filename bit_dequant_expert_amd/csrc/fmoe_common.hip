@@ -80,7 +80,9 @@ hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
 bool fused1_supported(int H, int I, int E, int bits) {
   const int sh = H * bits / 128, si = I * bits / 128;
   if (!((sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64) && E <= 2048 &&
-        H <= 8192 && H % 16 == 0 && I % fused_gu_rows(H, bits) == 0))
+        H <= 8192 && H % 16 == 0 && I % fused_gu_rows(H, bits) == 0 &&
+        fused_gu_rows(H, bits) % (32 / bits) == 0 &&
+        wimg_bytes(I, bits) <= (int64_t)kFusedImgPer * kThreads * 8))
     return false;
   const int dr = fused_d_rows(I, bits);
   return (H + dr - 1) / dr <= kFusedMaxNormParts;
@@ -88,7 +90,7 @@ bool fused1_supported(int H, int I, int E, int bits) {
 
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
   if (!fused1_supported(a.H, a.I, a.E, f.bits)) return hipErrorNotSupported;
-  const size_t lds = fused_lds_bytes(a.H, a.I);
+  const size_t lds = fused_lds_bytes(a.H, a.I, f.bits);
   const int ns = segs_per_lane(a.H, f.bits);
   int occ = 1;
   if (f.bits == 4 && f.group == 32) occ = fused_occupancy_4_32(f.sb, ns, a.E, lds);
@@ -103,11 +105,14 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
         n_cu < 1)
       n_cu = 256;
   }
-  const int n_items = a.n0 + a.nF;
-  int grid = occ * n_cu;
-  if (grid > n_items) grid = n_items;
+  // Router rows go to the first min(grid, E + 1) items (rows f, f + nRr, ...),
+  // so every one of them is the first item of a running workgroup.
+  FusedArgs b = a;
+  const int g = occ * n_cu;
+  const int grid = g < a.nF ? g : a.nF;
+  b.nRr = grid < a.E + 1 ? grid : a.E + 1;
   VCall c = make_call(VCall::FUSED1, f, ns, grid, st);
-  c.fu = &a;
+  c.fu = &b;
   c.lds = lds;
   return run_variant(c);
 }

@@ -96,6 +96,20 @@ __device__ __forceinline__ int tid_x() {
   return t;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (its release fence
+// covers all address spaces, and on this architecture one counter tracks
+// loads and stores alike), which would stall weight loads issued well ahead
+// of their use.  Global data handed to other waves or workgroups is published
+// with an explicit vm_drain() first.
+// The acquire side covers every address space (it costs no wait), so no
+// later global access is moved above the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // s_waitcnt vmcnt(0): every load and store this wave issued has completed.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -177,12 +191,30 @@ __device__ __forceinline__ void pair_slot(int j, int& half_idx, int& p) {
   }
 }
 
+// LDS copies of prepared images are chunk-transposed: with S segments per
+// row and C = PPS/4 16-byte chunks of slots per segment, chunk v of segment
+// sg sits at chunk index v*S + sg, and constant chunk c of segment sg (CC per
+// segment) at S*C + c*S + sg.  A wave then reads consecutive 16-byte chunks
+// in consecutive lanes (no bank conflicts) where the linear layout (used in
+// global memory) puts lanes 64 bytes apart.
+template <int BITS, int CC>
+__device__ __forceinline__ int lds_chunk(int g, int S) {
+  constexpr int C = QF<BITS>::PPS / 4;
+  if (g < S * C) {
+    const int sg = g / C, v = g - sg * C;
+    return v * S + sg;
+  }
+  const int h = g - S * C, sg = h / CC, c = h - sg * CC;
+  return S * C + c * S + sg;
+}
+
 // Prepare blocks of 32 elements with one wave: lane L works on elements
 // 4*(L&7) .. +3 of block `blk` (the same for the 8 lanes of a group, or -1 for
 // none), whose values it already holds in x.  Every lane of the wave must call
 // this (cross-lane operations).  dst is the prepared image of a K-vector
-// (pairs, then consts).  AGENT: other workgroups will read the image.
-template <int BITS, bool AGENT>
+// (pairs, then consts), linear (global) or chunk-transposed (LDS_T, an LDS
+// copy).  AGENT: other workgroups will read the image.
+template <int BITS, bool AGENT, bool LDS_T = false>
 __device__ __forceinline__ void prep_x4(const float4& xv, uint8_t* dst, int K, int blk) {
   const int sub = tid_x() & 7;
   const bool ok = blk >= 0;
@@ -200,6 +232,10 @@ __device__ __forceinline__ void prep_x4(const float4& xv, uint8_t* dst, int K, i
   for (int e = 0; e < 4; ++e) {
     int hidx, p;
     pair_slot<BITS>(32 * (ok ? blk : 0) + 4 * sub + e, hidx, p);
+    if (LDS_T) {
+      const int dw = hidx >> 1, S = K * BITS / 128;
+      hidx = (((lds_chunk<BITS, QF<BITS>::CPS>(dw >> 2, S)) << 2 | (dw & 3)) << 1) | (hidx & 1);
+    }
     const _Float16 h = (_Float16)ldexpf(x[e], -sh - p);
     if (ok) {
       if (AGENT) st_agent(halves + hidx, __builtin_bit_cast(uint16_t, h));
@@ -212,7 +248,11 @@ __device__ __forceinline__ void prep_x4(const float4& xv, uint8_t* dst, int K, i
   s1 = sum8(s1);
   s2 = sum8(s2);
   if (ok && sub == 0) {
-    float* c = reinterpret_cast<float*>(dst + 2 * (int64_t)K) + 4 * blk;
+    constexpr int CPS = QF<BITS>::CPS;
+    const int S = K * BITS / 128;
+    float* c = LDS_T ? reinterpret_cast<float*>(dst) +
+                           4 * lds_chunk<BITS, CPS>(S * (QF<BITS>::PPS / 4) + blk, S)
+                     : reinterpret_cast<float*>(dst + 2 * (int64_t)K) + 4 * blk;
     const float P = ldexpf(1.f, sh), C = ldexpf(s1, 10 + sh), A = ldexpf(s2, sh);
     if (AGENT) {
       st_agent(c + 0, P); st_agent(c + 1, C); st_agent(c + 2, A); st_agent(c + 3, 0.f);
@@ -243,7 +283,8 @@ __device__ __forceinline__ void prep_blocks(const float* src, uint8_t* dst, int 
 }
 
 // The whole workgroup (NT threads) prepares nvec K-vectors (vector v at
-// src + v*K, its image at dst + v*xprep_bytes(K), in LDS); the loads of up to
+// src + v*K, its chunk-transposed image at dst + v*xprep_bytes(K), in LDS);
+// the loads of up to
 // 8 passes are issued before any block is processed.  AGENT: the vectors were
 // written by other workgroups of this launch.
 template <int BITS, int NT, bool AGENT>
@@ -266,7 +307,7 @@ __device__ __forceinline__ void prep_vectors(const float* src, uint8_t* dst, int
       if ((p0 + j) * kPer < nblk) {   // uniform over the workgroup
         const int gb = (p0 + j) * kPer + (tid_x() >> 3);
         const int v = gb < nblk ? gb / bpv : 0;
-        prep_x4<BITS, false>(xv[j], dst + v * xb, K, gb < nblk ? gb - v * bpv : -1);
+        prep_x4<BITS, false, true>(xv[j], dst + v * xb, K, gb < nblk ? gb - v * bpv : -1);
       }
     }
   }
@@ -314,6 +355,66 @@ __device__ __forceinline__ void copy_to_lds_agent(uint64_t* dst, const uint64_t*
     for (int j = 0; j < 8; ++j) {
       const int i = base + j * nthreads + tid;
       if (i < n8) dst[i] = t[j];
+    }
+  }
+}
+
+// A linear prepared image (K-vector, BITS-bit consumer, CC constant chunks per
+// segment: QF<BITS>::CPS for xprep, 4 for word-blocked images) copied into LDS
+// chunk-transposed; loads in batches of 4 (clamped), stores placed.
+template <int BITS, int CC>
+__device__ __forceinline__ void copy_image_to_lds(uint4* dst, const uint4* src, int K,
+                                                  int nthreads) {
+  const int S = K * BITS / 128;
+  const int n16 = S * (QF<BITS>::PPS / 4 + CC);
+  const int tid = tid_x();
+  for (int base = 0; base < n16; base += 4 * nthreads) {
+    uint4 t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * nthreads + tid;
+      t[j] = src[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * nthreads + tid;
+      if (i < n16) dst[lds_chunk<BITS, CC>(i, S)] = t[j];
+    }
+  }
+}
+
+// nimg word-blocked images (contiguous in global, written by other workgroups
+// of this launch: agent-scope loads) copied into LDS chunk-transposed, image
+// after image.  Every load is issued before any is stored: MAXIMG images of at
+// most PER*NT 8-byte words each.
+template <int BITS, int NT, int MAXIMG, int PER>
+__device__ __forceinline__ void copy_wimgs_to_lds_agent(uint64_t* dst, const uint64_t* src,
+                                                        int K, int nimg) {
+  const int S = K * BITS / 128;
+  const int n8 = (2 * K + (K / (32 / BITS)) * 16) / 8;   // 8-byte words per image
+  const int tid = tid_x();
+  uint64_t t[MAXIMG][PER];
+#pragma unroll
+  for (int im = 0; im < MAXIMG; ++im) {
+    if (im < nimg) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (j * NT < n8) {
+          const int i = j * NT + tid;
+          t[im][j] = ld_agent(src + (int64_t)im * n8 + (i < n8 ? i : n8 - 1));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int im = 0; im < MAXIMG; ++im) {
+    if (im < nimg) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = j * NT + tid;
+        if (j * NT < n8 && i < n8)
+          dst[(int64_t)im * n8 + 2 * lds_chunk<BITS, 4>(i >> 1, S) + (i & 1)] = t[im][j];
+      }
     }
   }
 }
@@ -454,22 +555,23 @@ struct XRegs {
   uint32_t p[NS][PPS];
   float P[NS][CPS], C[NS][CPS], A[NS][CPS];
 
-  // src: prepared image of a K-vector (LDS or global).
+  // src: chunk-transposed LDS copy of the prepared image of a K-vector.
   __device__ __forceinline__ void load(const uint8_t* src, int K, const RowGeo& geo) {
+    const int S = geo.S;
     const uint4* pr = reinterpret_cast<const uint4*>(src);
-    const float4* cs = reinterpret_cast<const float4*>(src + 2 * (int64_t)K);
+    const float4* cs = reinterpret_cast<const float4*>(src) + S * (PPS / 4);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int sg = geo.seg(j);
 #pragma unroll
       for (int v = 0; v < PPS / 4; ++v) {
-        const uint4 u = pr[sg * (PPS / 4) + v];
+        const uint4 u = pr[v * S + sg];
         p[j][4 * v + 0] = u.x; p[j][4 * v + 1] = u.y;
         p[j][4 * v + 2] = u.z; p[j][4 * v + 3] = u.w;
       }
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
-        const float4 k4 = cs[sg * CPS + c];
+        const float4 k4 = cs[c * S + sg];
         P[j][c] = k4.x; C[j][c] = k4.y; A[j][c] = k4.z;
       }
     }
@@ -498,5 +600,132 @@ __device__ __forceinline__ float tile_dot(const Tile<BITS, G, SB, NS>& t, const 
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
+
+// ------------------------------------------------ word-blocked activations
+// The same prepared form with one power-of-two scale per 32-bit code word
+// (W = 32/BITS elements: 8 for 4-bit codes, 16 for 2-bit), so that a producer
+// of W consecutive values can publish its block on its own.  A block's fp16
+// slots are contiguous (W/2 pair dwords at dword index block*W/2) and its
+// constants are the float4 {P, C, A, 0} at byte 2*K + 16*block.
+//
+// One lane per element: lanes L .. L+W-1 (L a multiple of W) hold the W
+// values of block `blk` (element j = blk*W + lane%W); every lane of the wave
+// calls this (cross-lane sums); `live` selects the lanes that hold a value.
+// The image is written with agent-scope stores (read by other workgroups).
+template <int BITS>
+__device__ __forceinline__ void wimg_publish(float x, bool live, uint8_t* img, int K, int j) {
+  constexpr int W = 32 / BITS;
+  const float ax = live ? fabsf(x) : 0.f;
+  float m = fmaxf(ax, dpp_f<kDppXor1>(ax));
+  m = fmaxf(m, dpp_f<kDppXor2>(m));
+  m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+  if (W == 16) m = fmaxf(m, dpp_f<kDppMirror>(m));
+  int sh = 0;
+  if (m > 0.f && m <= 3.402823466e38f) {
+    int ex;
+    frexpf(m, &ex);                         // m = f * 2^ex, f in [0.5, 1)
+    sh = min(max(ex - 1 - 14, -100), 113);  // scaled block max in [2^14, 2^15)
+  }
+  int hidx, p;
+  pair_slot<BITS>(j, hidx, p);
+  const _Float16 h = (_Float16)ldexpf(live ? x : 0.f, -sh - p);
+  if (live) st_agent(reinterpret_cast<uint16_t*>(img) + hidx, __builtin_bit_cast(uint16_t, h));
+  const float hf = (float)h;
+  float s1 = hf, s2 = ldexpf(hf, p);
+  s1 += dpp_f<kDppXor1>(s1);  s2 += dpp_f<kDppXor1>(s2);
+  s1 += dpp_f<kDppXor2>(s1);  s2 += dpp_f<kDppXor2>(s2);
+  s1 += dpp_f<kDppHalfMirror>(s1);  s2 += dpp_f<kDppHalfMirror>(s2);
+  if (W == 16) { s1 += dpp_f<kDppMirror>(s1); s2 += dpp_f<kDppMirror>(s2); }
+  if (live && j % W == 0) {
+    float* c = reinterpret_cast<float*>(img + 2 * (int64_t)K) + 4 * (j / W);
+    st_agent(c + 0, ldexpf(1.f, sh));
+    st_agent(c + 1, ldexpf(s1, 10 + sh));
+    st_agent(c + 2, ldexpf(s2, sh));
+    st_agent(c + 3, 0.f);
+  }
+}
+
+// D_w = sum over code word w's elements of (1024 + q*2^p) * slot, for the 4
+// words of a 16-byte segment.
+template <int BITS>
+__device__ __forceinline__ void seg_dot_words(const uint4& w, const uint32_t* xp, float* d);
+
+template <>
+__device__ __forceinline__ void seg_dot_words<4>(const uint4& w, const uint32_t* xp, float* d) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t v0 = v[i], v1 = v0 >> 8;
+    float a = dot2((v0 & 0x000F000Fu) | kMagic, xp[4 * i + 0], 0.f);
+    a = dot2((v0 & 0x00F000F0u) | kMagic, xp[4 * i + 1], a);
+    a = dot2((v1 & 0x000F000Fu) | kMagic, xp[4 * i + 2], a);
+    d[i] = dot2((v1 & 0x00F000F0u) | kMagic, xp[4 * i + 3], a);
+  }
+}
+
+template <>
+__device__ __forceinline__ void seg_dot_words<2>(const uint4& w, const uint32_t* xp, float* d) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t v0 = v[i], v1 = v0 >> 10;
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) a = dot2((v0 & (0x00030003u << (2 * j))) | kMagic, xp[8 * i + j], a);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      a = dot2((v1 & (0x00030003u << (2 * j))) | kMagic, xp[8 * i + 5 + j], a);
+    d[i] = a;
+  }
+}
+
+// A word-blocked image's slots and constants for one lane's segment (one
+// segment per lane: the down rows of the layer have at most 64 segments).
+template <int BITS>
+struct XRegsW {
+  static constexpr int PPS = QF<BITS>::PPS;
+  uint32_t p[PPS];
+  float P[4], C[4], A[4];
+
+  // src: chunk-transposed LDS copy of a word-blocked image.
+  __device__ __forceinline__ void load(const uint8_t* src, int K, const RowGeo& geo) {
+    const int S = geo.S;
+    const uint4* pr = reinterpret_cast<const uint4*>(src);
+    const float4* cs = reinterpret_cast<const float4*>(src) + S * (PPS / 4);
+    const int sg = geo.seg(0);
+#pragma unroll
+    for (int v = 0; v < PPS / 4; ++v) {
+      const uint4 u = pr[v * S + sg];
+      p[4 * v + 0] = u.x; p[4 * v + 1] = u.y; p[4 * v + 2] = u.z; p[4 * v + 3] = u.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 k4 = cs[i * S + sg];
+      P[i] = k4.x; C[i] = k4.y; A[i] = k4.z;
+    }
+  }
+};
+
+// This lane's share of sum_k deq(W)[n,k] * x_k for a one-segment row tile
+// against a word-blocked image.
+template <int BITS, int G, int SB>
+__device__ __forceinline__ float tile_dot_w(const Tile<BITS, G, SB, 1>& t, const XRegsW<BITS>& x) {
+  constexpr int GPS = Tile<BITS, G, SB, 1>::GPS;   // groups per segment
+  float d[4];
+  seg_dot_words<BITS>(t.q[0], x.p, d);
+  float acc = 0.f;
+#pragma unroll
+  for (int g = 0; g < GPS; ++g) {
+    float u = 0.f, as = 0.f;
+#pragma unroll
+    for (int i = g * 4 / GPS; i < (g + 1) * 4 / GPS; ++i) {
+      u += fmaf(d[i], x.P[i], -x.C[i]);
+      as += x.A[i];
+    }
+    acc = fmaf(sb_value<SB>(t.s[0][g]), u, acc);
+    acc = fmaf(sb_value<SB>(t.b[0][g]), as, acc);
+  }
+  return acc;
+}
 
 }  // namespace fmoe

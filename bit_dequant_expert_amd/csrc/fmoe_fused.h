@@ -8,31 +8,33 @@
 // out so that all expert weights are in flight as soon as the routing is known.
 //
 // Work items.  Workgroup b first takes item b (no atomic on the way in); the
-// items past the grid are handed out in order from 64 interleaved sub-queues:
+// items past the grid are handed out in order from 64 interleaved sub-queues.
+// Item f carries up to four parts:
 //
-//   first items   item i = router part i (one fp64 logit row per wave: the E
-//                 router rows, then the shared-expert gate row), published
-//                 at once, + gate/up part i of the shared expert
-//   layer items   item f = gate/up part f of a routed expert (a block of its
-//                 gate and up rows; SwiGLU to a workspace vector)
-//               + down part f (a block of down rows of EVERY active expert,
-//                 combined with the routing weights, plus the residual)
+//   router rows f, f + nRr, ...   fp64 logits (the E router rows, then the
+//                        shared-expert gate row; a quarter row per wave),
+//                        published at once; nRr = min(grid, E + 1), so every
+//                        router row belongs to a first item
+//   shared gate/up part f   a block of the shared expert's gate and up rows
+//   routed gate/up part f   the same for routed expert slot f / nGUs
+//   down part f          a block of down rows of EVERY active expert,
+//                        combined with the routing weights, plus the residual
 //
-// A gate/up part needs only x, and for a routed expert the routing.  A layer
-// item issues its gate/up loads and an L2 prefetch of its down part at once,
-// right after the routing is known; it computes its gate/up part and only
-// then needs the SwiGLU outputs of all gate/up parts (whose arrival raises the
-// item flag) for its down part, whose tiles it reloads from L2 together with
-// them.  It waits for the flag only when every item of the queue has been
-// handed out: then each gate/up part is held by a running workgroup that
-// finishes it without waiting on any down part.  Otherwise (fewer resident
-// workgroups than items) it defers its down part to a list worked off once the
-// queue is empty, and the flag also counts every defer decision, so after it
-// the list is complete.  Router parts never wait; routed parts wait for the
-// routing only after every router part was taken.  Workgroups are dispatched
-// in order of their index, so the first items (the router parts) are always
-// running before any item that waits for them, and one resident workgroup per
-// sub-queue (workgroups 0..63) is enough for progress.
+// A gate/up part publishes its SwiGLU outputs as prepared fp16 blocks (one
+// power-of-two scale per code word of the down rows), so no consumer converts
+// them.  An item requests its router row, its shared gate/up rows and x at
+// once, computes the logits and publishes them, computes its shared part,
+// then (the routing known) issues its routed gate/up loads and its down tiles
+// together, keeps the down tiles in registers while it computes its gate/up
+// part, and only then needs every SwiGLU output (the item flag) for its down
+// part.  It waits for the flag only when every item of the queue is held by a
+// running workgroup: each gate/up part then finishes without waiting on any
+// down part.  Otherwise (fewer resident workgroups than items) it defers its
+// down part to a list worked off once the queue is empty; the flag counts
+// every item's decision, so after it the list is complete.  Router rows only
+// sit in first items, which never wait before publishing them, so the routing
+// always completes; one resident workgroup per sub-queue (workgroups 0..63,
+// dispatched first) is enough for the rest to progress.
 //
 // Hardware facts this layout answers (measured on MI355X): atomics on one
 // address serialise at ~11 ns each (far slower while HBM is saturated), so
@@ -52,7 +54,8 @@
 
 namespace fmoe {
 
-constexpr int kFusedMaxSlots = 6;   // active experts whose down tiles are held at once
+constexpr int kFusedMaxSlots = 5;   // active experts whose down tiles are held at once
+constexpr int kFusedImgPer = 4;     // 8-byte words per thread of one SwiGLU image
 constexpr int kNormPer = 16;        // gamma*h values per thread loaded at once by the norm
 constexpr int kSpinLimit = 1 << 22;
 
@@ -75,9 +78,9 @@ constexpr int kRouterFlagLine = kTimeoutLine + 4;   // 64 flags
 constexpr int kItemFlagLine = kRouterFlagLine + 64; // 64 flags
 static_assert(kItemFlagLine + 64 <= kFusedCtrLines, "counter block too small");
 
-// LDS of one workgroup: [x fp32 | x prepared | down-stage activations].
-inline size_t fused_lds_bytes(int H, int I) {
-  return (size_t)H * 4 + (size_t)xprep_bytes(H) + (size_t)kFusedMaxSlots * xprep_bytes(I);
+// LDS of one workgroup: [x fp32 | x prepared | down-stage activation images].
+inline size_t fused_lds_bytes(int H, int I, int bits) {
+  return (size_t)H * 4 + (size_t)xprep_bytes(H) + (size_t)kFusedMaxSlots * wimg_bytes(I, bits);
 }
 
 __device__ __forceinline__ int* ctr_line(int* base, int line) { return base + kLine * line; }
@@ -172,48 +175,74 @@ struct RouteCache {
   float coef[17];   // routing weights, then the shared gate
 };
 
-// One wave: top-k of the published logits (ties: lower index), weights =
-// softmax over the selected logits, shared gate = sigmoid of logit E.  Lane
-// L holds logits L*VMAX .. L*VMAX+VMAX-1 in registers (agent-scope loads:
-// other workgroups wrote them).
-template <int VMAX>
-__device__ __forceinline__ void fused_topk(const FusedArgs& a, RouteCache& rc) {
-  const int lane = tid_x() & 63;
-  uint64_t key[VMAX];
+// Top-k of the published logits (ties: lower index) by the whole workgroup:
+// wave w holds logits w*64*VW .. (w+1)*64*VW-1 (VW per lane, agent-scope
+// loads: other workgroups wrote them) and picks its own top-k; wave 0 then
+// merges the 4k candidates (candidate w*k + r in lane w*k + r, so equal keys
+// still resolve to the lower index).  Weights = softmax over the selected
+// logits, shared gate = sigmoid of logit E.  Called by all threads.
+struct TopkCand {
+  uint64_t key[4][16];
+  int idx[4][16];
+};
+__device__ __forceinline__ void topk_round(uint64_t best, int best_e, int& win_e, uint64_t& win_k,
+                                           int& lane_out) {
+  const uint64_t m = wave_max_u64(best);
+  const uint64_t ball = __ballot(best == m);
+  const int L = __ffsll((unsigned long long)ball) - 1;
+  win_e = __builtin_amdgcn_readlane(best_e, L);
+  win_k = m;
+  lane_out = L;
+}
+template <int VW>
+__device__ __forceinline__ void fused_topk(const FusedArgs& a, RouteCache& rc, TopkCand& tc) {
+  const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
+  uint64_t key[VW];
 #pragma unroll
-  for (int v = 0; v < VMAX; ++v) {
-    const int e = lane * VMAX + v;
+  for (int v = 0; v < VW; ++v) {
+    const int e = (wave * 64 + lane) * VW + v;
     const double l = ld_agent(a.lg64 + (e < a.E ? e : a.E - 1));
     key[v] = e < a.E ? order_key(l) : 0ull;
   }
-  const double lgE = ld_agent(a.lg64 + a.E);
-  int sel_e = 0;
-  uint64_t sel_k = 0;
   for (int r = 0; r < a.k; ++r) {
     uint64_t best = 0;
     int bv = 0;
 #pragma unroll
-    for (int v = 0; v < VMAX; ++v) {
+    for (int v = 0; v < VW; ++v) {
       if (key[v] > best) { best = key[v]; bv = v; }
     }
-    const uint64_t m = wave_max_u64(best);
-    const uint64_t ball = __ballot(best == m);
-    const int L = __ffsll((unsigned long long)ball) - 1;
-    const int win = __builtin_amdgcn_readlane(lane * VMAX + bv, L);
+    int win_e, L;
+    uint64_t win_k;
+    topk_round(best, (wave * 64 + lane) * VW + bv, win_e, win_k, L);
 #pragma unroll
-    for (int v = 0; v < VMAX; ++v)
+    for (int v = 0; v < VW; ++v)
       if (lane == L && v == bv) key[v] = 0ull;
-    if (lane == r) { sel_e = win; sel_k = m; }
+    if (lane == 0) { tc.key[wave][r] = win_k; tc.idx[wave][r] = win_e; }
   }
-  const double sel_l = key_value(sel_k);
-  const double l0 = readlane_f64(sel_l, 0);
-  const float ex = lane < a.k ? expf((float)(sel_l - l0)) : 0.f;
-  const float z = wave_sum(ex);
-  if (lane < a.k) {
-    rc.sel[lane] = sel_e;
-    rc.coef[lane] = ex / z;
+  lds_barrier();
+  if (wave == 0) {
+    const bool c = lane < 4 * a.k;
+    uint64_t ck = c ? tc.key[lane / a.k][lane % a.k] : 0ull;
+    const int ce = c ? tc.idx[lane / a.k][lane % a.k] : 0;
+    int sel_e = 0;
+    uint64_t sel_k = 0;
+    for (int r = 0; r < a.k; ++r) {
+      int win_e, L;
+      uint64_t win_k;
+      topk_round(ck, ce, win_e, win_k, L);
+      if (lane == L) ck = 0ull;
+      if (lane == r) { sel_e = win_e; sel_k = win_k; }
+    }
+    const double sel_l = key_value(sel_k);
+    const double l0 = readlane_f64(sel_l, 0);
+    const float ex = lane < a.k ? expf((float)(sel_l - l0)) : 0.f;
+    const float z = wave_sum(ex);
+    if (lane < a.k) {
+      rc.sel[lane] = sel_e;
+      rc.coef[lane] = ex / z;
+    }
+    if (lane == 0) rc.coef[a.k] = 1.f / (1.f + expf(-(float)ld_agent(a.lg64 + a.E)));
   }
-  if (lane == 0) rc.coef[a.k] = 1.f / (1.f + expf(-(float)lgE));
 }
 
 // ------------------------------------------------------------ down parts
@@ -240,29 +269,34 @@ __device__ __forceinline__ void down_load(Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSl
 }
 
 // acc[u] += sum over the batch's experts of coef * (down row . SwiGLU output).
-// The batch's SwiGLU outputs are prepared in LDS first (all threads).
+// The batch's word-blocked SwiGLU images (published by the gate/up parts) are
+// copied to LDS first (all threads).
 template <int BITS, int G, int SB>
 __device__ __forceinline__ void down_dot(const Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSlots][kFusedUD],
                                          float (&acc)[kFusedUD], const FusedArgs& a,
                                          const RouteCache& rc, uint8_t* lds_ap, int s0, int ns,
                                          const RowGeo& geo) {
-  const int64_t xbI = xprep_bytes(a.I);
-  prep_vectors<BITS, kThreads, true>(a.abuf + (int64_t)s0 * a.I, lds_ap, a.I, ns);
-  __syncthreads();
+  const int64_t ib = wimg_bytes(a.I, BITS);
+  copy_wimgs_to_lds_agent<BITS, kThreads, kFusedMaxSlots, kFusedImgPer>(
+      reinterpret_cast<uint64_t*>(lds_ap),
+      reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.abuf) + s0 * ib), a.I,
+      ns);
+  lds_barrier();
 #pragma unroll
   for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
     if (sl < ns) {
       const float coef = rc.coef[s0 + sl];
-      XRegs<BITS, 1> xr;
-      xr.load(lds_ap + sl * xbI, a.I, geo);
+      XRegsW<BITS> xr;
+      xr.load(lds_ap + sl * ib, a.I, geo);
 #pragma unroll
       for (int u = 0; u < kFusedUD; ++u) {
-        const float v = sum_lanes(tile_dot(tl[sl][u], xr), geo.LPR);
+        const float v = sum_lanes(tile_dot_w(tl[sl][u], xr), geo.LPR);
         acc[u] = fmaf(coef, v, acc[u]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // one expert's activations in registers at a time
   }
-  __syncthreads();   // lds_ap is reused by the next batch
+  lds_barrier();   // lds_ap is reused by the next batch
 }
 
 // The experts from s_begin on, tiles loaded here (deferred parts, and experts
@@ -316,16 +350,16 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache
   }
   ss = sum_lanes(ss, kWave);
   if (lane == kWave - 1) s_part[wave] = ss;
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     float tot = 0.f;
     for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
     st_agent(a.partials + d, tot);
   }
   vm_drain();
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) s_flag = arrive(a.ctr, kDownSubLine, d, a.nD);
-  __syncthreads();
+  lds_barrier();
   if (!s_flag) return;
   // Last down part: y = (gamma*h) * rms^-1.  The first kNormPer*kThreads values
   // of gamma*h are loaded together with the partial sums.
@@ -345,9 +379,9 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache
   for (int j = 0; j < kFusedMaxNormParts / kThreads; ++j)
     if (j * kThreads + tid < a.nD) part += pv[j];
   part = sum_lanes(part, kWave);
-  __syncthreads();
+  lds_barrier();
   if (lane == kWave - 1) s_part[wave] = part;
-  __syncthreads();
+  lds_barrier();
   float tot = 0.f;
   for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
   const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
@@ -372,41 +406,6 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache
     if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
     if (a.w_out) a.w_out[tid] = rc.coef[tid];
   }
-}
-
-// Touch every 128-byte line of down part d (codes, scales and biases of its
-// rows, every active expert, and its residual and gamma values; at most 128
-// rows per part) with one 4-byte load per line, so that the loads after the
-// item flag hit in L2 (same workgroup, same XCD).  Nothing is
-// held in registers meanwhile; the loads' values are folded into the result,
-// which the caller consumes late.
-template <int BITS, int G, int SB>
-__device__ __forceinline__ uint32_t down_prefetch(const FusedArgs& a, const RouteCache& rc, int d) {
-  const int m0 = d * a.d_rows;
-  const int nrows = min(a.d_rows, a.H - m0);
-  const int64_t rb = (int64_t)a.I * BITS / 8, sbr = (int64_t)(a.I / G) * SB;
-  const int lq = (int)((nrows * rb + 127) / 128), ls = (int)((nrows * sbr + 127) / 128);
-  const int per = lq + 2 * ls, nw = per * (a.k + 1), total = nw + 2;
-  uint32_t acc = 0;
-  for (int l0 = 0; l0 < total; l0 += kThreads) {
-    const int l = l0 + tid_x();
-    if (l >= nw && l < total) {   // residual and gamma of the part's rows
-      acc ^= __float_as_uint((l == nw ? a.resid : a.gamma)[m0]);
-    } else if (l < nw) {
-      const int slot = l / per, r = l - slot * per;
-      const int64_t e = slot < a.k ? rc.sel[slot] : a.E;
-      const uint8_t* base = a.src.base + e * a.src.stride;
-      const uint8_t* p;
-      if (r < lq)
-        p = base + a.src.off[6] + m0 * rb + min((int64_t)r * 128, nrows * rb - 4);
-      else if (r < lq + ls)
-        p = base + a.src.off[7] + m0 * sbr + min((int64_t)(r - lq) * 128, nrows * sbr - 4);
-      else
-        p = base + a.src.off[8] + m0 * sbr + min((int64_t)(r - lq - ls) * 128, nrows * sbr - 4);
-      acc ^= *reinterpret_cast<const uint32_t*>(p);
-    }
-  }
-  return acc;
 }
 
 // The persistent loop's body is large and its address arithmetic depends on
@@ -434,7 +433,7 @@ __device__ __forceinline__ void opaque_args(FusedArgs& a) {
   opaque_g(a.idx_out); opaque_g(a.lg64); opaque_g(a.abuf); opaque_g(a.gh);
   opaque_g(a.partials); opaque_g(a.dlist); opaque_g(a.ctr);
   opaque_s(a.H); opaque_s(a.I); opaque_s(a.E); opaque_s(a.k); opaque_s(a.eps);
-  opaque_s(a.nR); opaque_s(a.nGUs); opaque_s(a.nD); opaque_s(a.n0); opaque_s(a.nF);
+  opaque_s(a.nRr); opaque_s(a.nGUs); opaque_s(a.nD); opaque_s(a.nF);
   opaque_s(a.gu_rows); opaque_s(a.d_rows);
   opaque_s(a.src.stride);
 #pragma unroll
@@ -447,13 +446,19 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
   __shared__ int s_item;
   __shared__ int s_flag;
   __shared__ int s_defer;
-  __shared__ uint32_t s_sink;
+  __shared__ float s_act[kWave];
   __shared__ float s_part[kThreads / kWave];
   __shared__ RouteCache rc;
+  __shared__ TopkCand s_tc;
+  __shared__ double s_rp[kFusedWaves];
   using TileH = Tile<BITS, G, SB, NSH>;
+  using TileI = Tile<BITS, G, SB, 1>;
   constexpr int kUG = fused_ug(NSH);
+  // float4 per lane of a quarter hidden row, and of x per thread: the hidden
+  // size is NSH*8192/BITS (the launcher admits 64 or 128 segments per row).
+  constexpr int kQ = 8 * NSH / BITS;
   const int subq = blockIdx.x % kSubs;
-  bool have_x = false, have_xp = false;   // LDS already holds x / prepared x
+  bool have_x = false;                    // LDS already holds x (fp32 and prepared)
   bool drained = false;                   // wave 0: every queue item handed out
   bool first = true;                      // thread 0: first item not yet taken
   bool listing = false;                   // thread 0: now taking deferred down parts
@@ -469,24 +474,23 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     float* lds_x = reinterpret_cast<float*>(lds);
     uint8_t* lds_xp = lds + (int64_t)a.H * 4;
     uint8_t* lds_ap = lds_xp + xprep_bytes(a.H);
-    const int n_main = a.n0 + a.nF;
+    const int n_main = a.nF;
     int* ctr = a.ctr;
 
     auto ensure_routing = [&]() {
       if (rc.ready) return;  // workgroup-uniform (shared, read after a barrier)
-      if (wave == 0) {
-        if (lane == 0) wait_flag(ctr, kRouterFlagLine);
-        fused_topk<VMAX>(a, rc);
-        if (lane == 0) rc.ready = 1;
-      }
-      __syncthreads();
+      if (tid == 0) wait_flag(ctr, kRouterFlagLine);
+      lds_barrier();
+      fused_topk<VMAX / 4>(a, rc, s_tc);
+      if (tid == 0) rc.ready = 1;
+      lds_barrier();
     };
 
     // Next piece of work: first item blockIdx.x, then item < n_main from the
     // queue of the items past the grid; once that is empty, n_main + d for
     // deferred down part d (after the item flag, when the list is complete);
     // -1 when there is nothing left.
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
       int it = -1;
       if (first) {
@@ -511,118 +515,142 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       }
       s_item = it;
     }
-    __syncthreads();
+    lds_barrier();
     const int item = s_item;
     if (item < 0) break;
 
-    int dpart = -1;   // the down part this iteration computes
-    if (item < n_main) {
-      // What the item holds (all workgroup-uniform).  First items: router
-      // part item and shared-expert gate/up part item.  Layer items f: routed
-      // gate/up part f (expert slot f / nGUs) and down part f.
-      int rpart = -1, gslot = -1, gpart = 0, garr = -1;
-      if (item < a.n0) {
-        if (item < a.nR) rpart = item;
-        if (item < a.nGUs) { gslot = a.k; gpart = item; garr = a.nF + item; }
-      } else {
-        const int f = item - a.n0;
-        if (f < a.k * a.nGUs) { gslot = f / a.nGUs; gpart = f - gslot * a.nGUs; }
-        garr = f;
-        if (f < a.nD) dpart = f;
-      }
-      const bool has_gu = gslot >= 0, has_d = dpart >= 0;
+    // What the item holds (all workgroup-uniform): router rows item,
+    // item + nRr, ... (item < nRr), shared gate/up part item, routed gate/up
+    // part item (expert slot item / nGUs), down part item.
+    int spart = -1, gslot = -1, gpart = 0, dpart = -1;
+    const bool deferred = item >= n_main;
+    const bool routes = !deferred && item < a.nRr;
+    if (deferred) {
+      dpart = item - n_main;
+    } else {
+      if (item < a.nGUs) spart = item;
+      if (item < a.k * a.nGUs) { gslot = item / a.nGUs; gpart = item - gslot * a.nGUs; }
+      if (item < a.nD) dpart = item;
+    }
+    const RowGeo geoH(a.H, BITS), geoI(a.I, BITS);
 
-      if (rpart >= 0) {
-        // ---------------------------------------------- router rows (fp64)
-        const int e = rpart * kFusedWaves + wave;
-        const bool live = e <= a.E;
-        const float* wrow = (live && e < a.E) ? a.Wr + (int64_t)e * a.H : a.wsg;
-        const int nf4 = a.H / 4;
-        double acc = 0.0;
-        for (int c0 = 0; c0 < nf4; c0 += 16 * kWave) {
-          float4 wv[16];
+    // Gate/up part (slot, part): SwiGLU of its rows, published as one block
+    // of word-blocked prepared image per code word of the down rows.
+    auto gu_load = [&](TileH (&tg)[kUG], TileH (&tu)[kUG], int slot, int part) {
+      const int64_t e = slot < a.k ? rc.sel[slot] : a.E;
+      const uint8_t* base = a.src.base + e * a.src.stride;
+      const int n0 = part * a.gu_rows + wave * kUG;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int fi = c0 + j * kWave + lane;
-            wv[j] = ld_nt(reinterpret_cast<const float4*>(wrow) + (fi < nf4 ? fi : nf4 - 1));
-          }
-          if (!have_x) {   // x staging overlaps the row loads
-            copy_to_lds(reinterpret_cast<uint4*>(lds_x), reinterpret_cast<const uint4*>(a.x),
-                        nf4, kThreads);
-            have_x = true;
-            __syncthreads();
-          }
-          if (live) {
+      for (int u = 0; u < kUG; ++u) {
+        tg[u].load(base + a.src.off[0], base + a.src.off[1], base + a.src.off[2], a.H, n0 + u,
+                   geoH);
+        tu[u].load(base + a.src.off[3], base + a.src.off[4], base + a.src.off[5], a.H, n0 + u,
+                   geoH);
+      }
+    };
+    auto gu_finish = [&](const TileH (&tg)[kUG], const TileH (&tu)[kUG], int slot, int part) {
+      lds_barrier();   // prepared x visible; s_act free
+      XRegs<BITS, NSH> xr;
+      xr.load(lds_xp, a.H, geoH);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int fi = c0 + j * kWave + lane;
-              if (fi < nf4) {
-                const float4 xv = reinterpret_cast<const float4*>(lds_x)[fi];
-                acc = fma((double)wv[j].x, (double)xv.x, acc);
-                acc = fma((double)wv[j].y, (double)xv.y, acc);
-                acc = fma((double)wv[j].z, (double)xv.z, acc);
-                acc = fma((double)wv[j].w, (double)xv.w, acc);
-              }
+      for (int u = 0; u < kUG; ++u) {
+        const float gs = sum_lanes(tile_dot(tg[u], xr), kWave);
+        const float us = sum_lanes(tile_dot(tu[u], xr), kWave);
+        if (lane == kWave - 1) s_act[wave * kUG + u] = silu(gs) * us;
+      }
+      lds_barrier();
+      if (wave == 0) {   // the part's rows are whole code-word blocks of the image
+        uint8_t* img = reinterpret_cast<uint8_t*>(a.abuf) + slot * wimg_bytes(a.I, BITS);
+        const bool live = lane < a.gu_rows;
+        wimg_publish<BITS>(s_act[live ? lane : 0], live, img, a.I, part * a.gu_rows + lane);
+      }
+      vm_drain();
+    };
+    // A quarter of router row e per wave (row E is the shared-expert gate).
+    auto router_load = [&](float4 (&wv)[kQ], int e) {
+      const float4* row = reinterpret_cast<const float4*>(e < a.E ? a.Wr + (int64_t)e * a.H : a.wsg);
+      const int q0 = wave * (a.H / 16) + lane;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) wv[q] = ld_nt(row + q0 + q * 64);
+    };
+
+    // Two passes over the item's gate/up parts (one copy of that code): pass 0
+    // the shared expert's part, which needs no routing, with the router rows
+    // and x staging between its loads and its compute; pass 1 the routed part
+    // after the routing, with the down tiles loaded alongside and held in
+    // registers until every SwiGLU output is in.
+    TileI tl[kFusedMaxSlots][kFusedUD];
+    float acc[kFusedUD], rv[kFusedUD], gv[kFusedUD];
+    const int wrow0 = (dpart >= 0 ? dpart : 0) * a.d_rows + wave * (kFusedUD * geoI.RPI);
+#pragma unroll
+    for (int u = 0; u < kFusedUD; ++u) acc[u] = 0.f;
+    if (!deferred) {
+      float4 wv[kQ];
+      if (routes) router_load(wv, item);
+#pragma unroll 1
+      for (int pass = 0; pass < 2; ++pass) {
+        const bool has = pass == 0 ? spart >= 0 : gslot >= 0;
+        const int slot = pass == 0 ? a.k : gslot, part = pass == 0 ? spart : gpart;
+        if (pass == 1 && (gslot >= 0 || dpart >= 0)) ensure_routing();
+        TileH tg[kUG], tu[kUG];
+        if (has) gu_load(tg, tu, slot, part);
+        if (pass == 0) {
+          // x staged in LDS (fp32 for the router rows, prepared for the
+          // gate/up rows) from registers, then the router rows (fp64)
+          if (!have_x) {
+            float4 xq[kQ];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) xq[q] = reinterpret_cast<const float4*>(a.x)[q * kThreads + tid];
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+              reinterpret_cast<float4*>(lds_x)[q * kThreads + tid] = xq[q];
+              prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
             }
+            have_x = true;
+            lds_barrier();
           }
-        }
-          acc = sum_lanes_f64(acc);
-        if (live && lane == kWave - 1) st_agent(a.lg64 + e, acc);
-        vm_drain();
-        __syncthreads();
-        if (tid == 0 && arrive(ctr, kRouterSubLine, rpart, a.nR))
-          raise_flags(ctr, kRouterFlagLine);
-      }
-
-      // -------------------------------------------- gate/up part + SwiGLU
-      const RowGeo geoH(a.H, BITS);
-      const int n0 = gpart * a.gu_rows + wave * kUG;
-      if (has_gu && !have_xp) {
-        prep_vector<BITS, kThreads, false>(a.x, lds_xp, a.H);
-        have_xp = true;
-      }
-      // Routed gate/up rows and down parts need the routing before any load
-      // (the shared expert's gate/up rows do not).
-      if ((has_gu && gslot < a.k) || has_d) ensure_routing();
-      TileH tg[kUG], tu[kUG];
-      if (has_gu) {
-        const int64_t e = gslot < a.k ? rc.sel[gslot] : a.E;
-        const uint8_t* base = a.src.base + e * a.src.stride;
+          if (routes) {
+            for (int e = item;;) {
+              const float4* xl = reinterpret_cast<const float4*>(lds_x) + wave * (a.H / 16) + lane;
+              double racc = 0.0;
 #pragma unroll
-        for (int u = 0; u < kUG; ++u) {
-          tg[u].load(base + a.src.off[0], base + a.src.off[1], base + a.src.off[2], a.H, n0 + u,
-                     geoH);
-          tu[u].load(base + a.src.off[3], base + a.src.off[4], base + a.src.off[5], a.H, n0 + u,
-                     geoH);
+              for (int q = 0; q < kQ; ++q) {
+                const float4 xv = xl[q * 64];
+                racc = fma((double)wv[q].x, (double)xv.x, racc);
+                racc = fma((double)wv[q].y, (double)xv.y, racc);
+                racc = fma((double)wv[q].z, (double)xv.z, racc);
+                racc = fma((double)wv[q].w, (double)xv.w, racc);
+              }
+              racc = sum_lanes_f64(racc);
+              if (lane == kWave - 1) s_rp[wave] = racc;
+              lds_barrier();
+              if (tid == 0) st_agent(a.lg64 + e, ((s_rp[0] + s_rp[1]) + s_rp[2]) + s_rp[3]);
+              e += a.nRr;
+              if (e > a.E) break;
+              router_load(wv, e);
+              lds_barrier();   // s_rp is reused
+            }
+            vm_drain();
+            lds_barrier();
+            if (tid == 0 && arrive(ctr, kRouterSubLine, item, a.nRr))
+              raise_flags(ctr, kRouterFlagLine);
+          }
+        } else if (dpart >= 0) {
+          QueueView qv{0, 0};
+          const bool check = wave == 0 && !drained;
+          if (check) qv = load_queue(ctr);   // consumed once the tile loads are out
+          down_load<BITS, G, SB>(tl, a, rc, wrow0, 0, min(kFusedMaxSlots, kp1), geoI);
+          down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
+          if (check) drained = queue_drained(qv, n_main);
         }
+        if (has) gu_finish(tg, tu, slot, part);
       }
-      QueueView qv{0, 0};
-      const bool check = wave == 0 && has_d && !drained;
-      uint32_t pf = 0;
-      if (has_d) {
-        if (check) qv = load_queue(ctr);   // consumed once the tile loads are out
-        pf = down_prefetch<BITS, G, SB>(a, rc, dpart);
-      }
-      if (check) drained = queue_drained(qv, n_main);
-      if (has_gu) {
-        __syncthreads();   // prepared x visible
-        XRegs<BITS, NSH> xr;
-        xr.load(lds_xp, a.H, geoH);
-        float* arow = a.abuf + (int64_t)gslot * a.I;
-#pragma unroll
-        for (int u = 0; u < kUG; ++u) {
-          const float gs = sum_lanes(tile_dot(tg[u], xr), kWave);
-          const float us = sum_lanes(tile_dot(tu[u], xr), kWave);
-          if (lane == kWave - 1) st_agent(arow + n0 + u, silu(gs) * us);
-        }
-        vm_drain();
-      }
-      if (pf == 0x9E3779B9u) s_sink = pf;   // keeps the prefetch loads (LDS only)
-      if (garr < 0) continue;
-      __syncthreads();
+      // Every item arrives once, after its gate/up parts and its decision to
+      // wait for the item flag or to defer its down part.
+      lds_barrier();
       if (wave == 0) {
         bool defer = false;
-        if (has_d && !drained) {
+        if (dpart >= 0 && !drained) {
           drained = queue_drained(load_queue(ctr), n_main);
           defer = !drained;
         }
@@ -633,30 +661,23 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
             st_agent(a.dlist + j, dpart);
             vm_drain();
           }
-          if (arrive(ctr, kItemSubLine, garr, a.nF + a.nGUs)) raise_flags(ctr, kItemFlagLine);
+          if (arrive(ctr, kItemSubLine, item, n_main)) raise_flags(ctr, kItemFlagLine);
         }
       }
-      __syncthreads();
-      if (!has_d || s_defer) continue;
+      lds_barrier();
+      if (dpart < 0 || s_defer) continue;
       if (tid == 0) wait_flag(ctr, kItemFlagLine);
-      __syncthreads();
+      lds_barrier();
+      down_dot<BITS, G, SB>(tl, acc, a, rc, lds_ap, 0, min(kFusedMaxSlots, kp1), geoI);
+      if (kp1 > kFusedMaxSlots)
+        down_batches<BITS, G, SB>(acc, a, rc, lds_ap, wrow0, kFusedMaxSlots, geoI);
     } else {
-      dpart = item - n_main;   // deferred: the item flag is up already
-      ensure_routing();
-    }
-
-    // -------------------------------------------------- down part
-    {
-      const RowGeo geoI(a.I, BITS);
-      const int wrow0 = dpart * a.d_rows + wave * (kFusedUD * geoI.RPI);
-      float acc[kFusedUD], rv[kFusedUD], gv[kFusedUD];
-#pragma unroll
-      for (int u = 0; u < kFusedUD; ++u) acc[u] = 0.f;
+      // deferred (the item flag is up already): tiles loaded here
       down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
       down_batches<BITS, G, SB>(acc, a, rc, lds_ap, wrow0, 0, geoI);
-      down_finish(a, rc, dpart, acc, rv, gv, wrow0, geoI.RPI, geoI.lane_row,
-                  geoI.lane_seg == geoI.LPR - 1, s_part, s_flag);
     }
+    down_finish(a, rc, dpart, acc, rv, gv, wrow0, geoI.RPI, geoI.lane_row,
+                geoI.lane_seg == geoI.LPR - 1, s_part, s_flag);
   }
 
   // Leave; the last workgroup out resets queue heads, flags and the list.

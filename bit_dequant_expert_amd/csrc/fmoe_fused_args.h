@@ -44,11 +44,12 @@ struct FusedArgs {
   float* partials;   // [nD]  sum of h^2 per down part
   int* dlist;        // [nD]  down parts deferred to the end of the queue
   int* ctr;          // counter and flag block (kFusedCtrBytes)
-  int nR;            // router parts (kFusedWaves logit rows each)
   int nGUs;          // gate/up parts per expert (I / gu_rows)
   int nD;            // down parts
-  int n0;            // first items: router part i and shared gate/up part i
-  int nF;            // layer items: routed gate/up part f and down part f
+  int nF;            // items: item f holds shared gate/up part f, routed gate/up
+                     // part f (expert slot f / nGUs) and down part f
+  int nRr;           // items holding router rows (rows f, f + nRr, ...); set by
+                     // the launcher to min(grid, E + 1), so they are all first items
   int gu_rows;       // gate/up rows per part
   int d_rows;        // down rows per part
 };

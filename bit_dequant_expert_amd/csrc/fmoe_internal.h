@@ -116,6 +116,12 @@ struct MfmaArgs {
 
 // Bytes of the prepared image of a K-vector: K/2 fp16 pairs + K/32 float4.
 __host__ __device__ constexpr int64_t xprep_bytes(int64_t K) { return 2 * K + (K / 32) * 16; }
+// Word-blocked prepared image (the down projection's input inside the one-
+// launch layer): pairs as in xprep, then one float4 {P, C, A, 0} per block of
+// one 32-bit code word (32/bits elements).
+__host__ __device__ constexpr int64_t wimg_bytes(int64_t K, int bits) {
+  return 2 * K + (K / (32 / bits)) * 16;
+}
 
 inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane reads per row
   const int S = K * bits / 128;

@@ -359,8 +359,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GUArgs a) {
     const int p = av.entries()[eoff + jt];
     const int t = p / a.kp1;
     if (jt > 0) __syncthreads();
-    copy_to_lds(reinterpret_cast<uint4*>(lds),
-                reinterpret_cast<const uint4*>(a.xprep + (int64_t)t * xb), (int)(xb / 16), kThreads);
+    copy_image_to_lds<BITS, QF<BITS>::CPS>(reinterpret_cast<uint4*>(lds),
+                                            reinterpret_cast<const uint4*>(a.xprep + (int64_t)t * xb),
+                                            a.H, kThreads);
     __syncthreads();
     XRegs<BITS, NS> xr;
     xr.load(lds, a.H, geo);
@@ -447,9 +448,9 @@ __global__ __launch_bounds__(kThreads) void k_down_combine(DArgs a) {
     if (s0 > 0) __syncthreads();
     for (int sl = 0; sl < ns; ++sl) {
       const int p = av.entries()[av.off()[s0 + sl]];
-      copy_to_lds(reinterpret_cast<uint4*>(lds + sl * ab),
-                  reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab), (int)(ab / 16),
-                  kThreads);
+      copy_image_to_lds<BITS, QF<BITS>::CPS>(reinterpret_cast<uint4*>(lds + sl * ab),
+                                              reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab),
+                                              a.I, kThreads);
     }
     __syncthreads();
 #pragma unroll
@@ -554,8 +555,9 @@ __global__ __launch_bounds__(kThreads) void k_down_slots(DArgs a) {
   for (int jt = 0; jt < cnt; ++jt) {
     const int p = av.entries()[eoff + jt];
     if (jt > 0) __syncthreads();
-    copy_to_lds(reinterpret_cast<uint4*>(lds),
-                reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab), (int)(ab / 16), kThreads);
+    copy_image_to_lds<BITS, QF<BITS>::CPS>(reinterpret_cast<uint4*>(lds),
+                                            reinterpret_cast<const uint4*>(a.aprep + (int64_t)p * ab),
+                                            a.I, kThreads);
     __syncthreads();
     XRegs<BITS, NS> xr;
     xr.load(lds, a.I, geo);
