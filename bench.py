@@ -40,10 +40,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=640)
     p.add_argument("--workload", default="layer4", choices=["layer4", "layer2"])
     p.add_argument("--replicas", type=int, default=32)
-    p.add_argument("--cpu-sample", type=int, default=12, help="tokens timed on the oracle")
+    p.add_argument("--cpu-sample", type=int, default=40, help="tokens timed on the oracle")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-steps", type=int, default=0,
                    help="launch only this many plain (non-graph) steps, for profilers")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="run only a plain device copy of this many bytes (calibrates the HBM "
+                        "byte counters of a profiler) and exit")
+    p.add_argument("--no-stream-probe", action="store_true",
+                   help="skip measuring the streaming-read ceiling")
     return p.parse_args()
 
 
@@ -67,19 +72,24 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_hash):
-    """HBM bytes per launch measured with rocprofv3 counters for this exact
-    kernel source (profiles/hbm_traffic_<workload>.json), else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_layer4.json")
+def traffic_from_profiles(kernel_hash, workload):
+    """HBM bytes per launch of the layer kernel, from the rocprofv3 counter
+    summary profiles/k_layer1_<workload>_traffic.txt when it was taken on this
+    exact kernel source (its `source_hash:` line), else None."""
+    path = os.path.join(ROOT, "profiles", f"k_layer1_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path))
-    except Exception:
-        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("source_hash") != kernel_hash:
         return None
-    return rec.get("bytes_per_layer")
+    try:
+        return int(float(rec["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, n_tokens):
@@ -118,6 +128,19 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_bytes:
+        # Plain copy of known size: a profiler's FETCH/WRITE counters over this
+        # dispatch give the scale from counter units to bytes.
+        n = args.copy_bytes
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "dispatches": 3}))
+        return
 
     import bit_dequant_expert_amd as fm
     import synth
@@ -218,7 +241,14 @@ def main():
     nbytes, ebytes = layer_bytes(cfg)
     gbps = nbytes / (us * 1e-6) / 1e9
     khash = source_hash()
-    traffic = traffic_from_profiles(khash)
+    traffic = traffic_from_profiles(khash, args.workload)
+    stream = None
+    if not args.no_stream_probe:
+        try:
+            import probes
+            stream = round(probes.stream_read_gbps(torch), 1)
+        except Exception as exc:  # the probe is context only
+            print(f"[bench] stream probe skipped: {exc}", file=sys.stderr)
     out = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -249,6 +279,8 @@ def main():
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
         "kernel_source_hash": khash,
+        "context": {"hbm_stream_read_gbps_measured": stream,
+                    "note": "best of 10 passes of a plain 4 GiB streaming read on this GPU"},
     }
     if not args.no_cpu_baseline:
         import multiprocessing
