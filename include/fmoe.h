@@ -141,7 +141,7 @@ int64_t fmoe_slab_layout(int32_t hidden, int32_t inter, const fmoe_qformat *fmt,
  * logits) and sums to 1.  logits_out ([T,E] fp32) may be NULL.
  *   router_w [E,H] fp32, x [T,H] fp32, idx [T,k] int32, w [T,k] fp32.
  *   H a multiple of 4, all pointers 16-byte aligned, 1 <= k <= min(E, 16),
- *   E <= 8192.  T == 0 is a no-op.
+ *   E <= 2048, H <= 8192 (FMOE_ERR_UNSUPPORTED beyond).  T == 0 is a no-op.
  *   ws: fmoe_route_workspace_size(T, E) bytes. */
 fmoe_status fmoe_route_topk(const float *router_w, const float *x, int32_t T, int32_t H,
                             int32_t E, int32_t k, int32_t *idx, float *w, float *logits_out,
