@@ -135,7 +135,7 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   w.nrb_d = (H + fmoe::rows_per_wg(I, bits) - 1) / fmoe::rows_per_wg(I, bits);
   const size_t ent = (size_t)T * kp1;
   size_t pos = 0;
-  w.ctr = pos; pos += fmoe::kFusedCtrBytes;
+  w.ctr = pos; pos += fmoe::kWsReserved;   // counters (the one-launch path's block)
   w.lg64 = pos; pos = align256(pos + (size_t)T * (E + 1) * 8);
   w.w = pos; pos = align256(pos + (size_t)T * k * 4);
   w.g = pos; pos = align256(pos + (size_t)T * 4);
@@ -160,7 +160,7 @@ struct FfnWs {
 FfnWs ffn_ws(int H, int I) {
   FfnWs w{};
   size_t pos = 0;
-  w.ctr = pos; pos += 256;
+  w.ctr = pos; pos += fmoe::kWsReserved;   // same reserved head as every layout
   w.act = pos; pos = align256(pos + act_ints(1, 1, 1) * 4);
   w.xprep = pos; pos = align256(pos + fmoe::xprep_bytes(H));
   w.abuf = pos; pos = align256(pos + (size_t)I * 4);
@@ -170,7 +170,7 @@ FfnWs ffn_ws(int H, int I) {
   return w;
 }
 
-size_t route_ws(int T, int E) { return 256 + align256((size_t)T * E * 8); }
+size_t route_ws(int T, int E) { return fmoe::kWsReserved + align256((size_t)T * E * 8); }
 
 // FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers (debug and
 // cross-checking only).
@@ -237,7 +237,7 @@ fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, in
   a.x = x;
   a.T = T; a.H = H; a.E = E; a.k = k; a.rows = E;
   a.n_router_wgs = (E + 3) / 4;
-  a.lg64 = (double*)(wsb + 256);
+  a.lg64 = (double*)(wsb + fmoe::kWsReserved);
   a.logits_out = logits_out;
   a.idx_out = idx;
   a.w_out = w;

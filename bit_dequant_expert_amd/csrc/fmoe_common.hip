@@ -81,7 +81,7 @@ bool fused1_supported(int H, int I, int E, int bits) {
   const int sh = H * bits / 128, si = I * bits / 128;
   if (!((sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64) && E <= 2048 &&
         H <= 8192 && H % 16 == 0 && I % fused_gu_rows(H, bits) == 0 &&
-        fused_gu_rows(H, bits) % (32 / bits) == 0 &&
+        fused_gu_rows(H, bits) % (32 / bits) == 0 && H % fused_d_rows(I, bits) == 0 &&
         wimg_bytes(I, bits) <= (int64_t)kFusedImgPer * kThreads * 8))
     return false;
   const int dr = fused_d_rows(I, bits);
@@ -105,12 +105,13 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
         n_cu < 1)
       n_cu = 256;
   }
-  // Router rows go to the first min(grid, E + 1) items (rows f, f + nRr, ...),
-  // so every one of them is the first item of a running workgroup.
+  // Router rows go to the first min(grid, E) items (rows f, f + nRr, ... below
+  // E, and the shared-expert gate row E to item E mod nRr), so every one of
+  // them is the first item of a running workgroup.
   FusedArgs b = a;
   const int g = occ * n_cu;
   const int grid = g < a.nF ? g : a.nF;
-  b.nRr = grid < a.E + 1 ? grid : a.E + 1;
+  b.nRr = grid < a.E ? grid : a.E;
   VCall c = make_call(VCall::FUSED1, f, ns, grid, st);
   c.fu = &b;
   c.lds = lds;

@@ -386,7 +386,9 @@ __device__ __forceinline__ void copy_image_to_lds(uint4* dst, const uint4* src, 
 // nimg word-blocked images (contiguous in global, written by other workgroups
 // of this launch: agent-scope loads) copied into LDS chunk-transposed, image
 // after image.  Every load is issued before any is stored: MAXIMG images of at
-// most PER*NT 8-byte words each.
+// most PER*NT 8-byte words each.  Only the pass count is a branch (uniform);
+// image and word indices are clamped, so a lane past the end re-copies the
+// last word to its own place.
 template <int BITS, int NT, int MAXIMG, int PER>
 __device__ __forceinline__ void copy_wimgs_to_lds_agent(uint64_t* dst, const uint64_t* src,
                                                         int K, int nimg) {
@@ -395,26 +397,21 @@ __device__ __forceinline__ void copy_wimgs_to_lds_agent(uint64_t* dst, const uin
   const int tid = tid_x();
   uint64_t t[MAXIMG][PER];
 #pragma unroll
-  for (int im = 0; im < MAXIMG; ++im) {
-    if (im < nimg) {
+  for (int j = 0; j < PER; ++j) {
+    if (j * NT < n8) {
+      const int i = min(j * NT + tid, n8 - 1);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (j * NT < n8) {
-          const int i = j * NT + tid;
-          t[im][j] = ld_agent(src + (int64_t)im * n8 + (i < n8 ? i : n8 - 1));
-        }
-      }
+      for (int im = 0; im < MAXIMG; ++im)
+        t[im][j] = ld_agent(src + (int64_t)min(im, nimg - 1) * n8 + i);
     }
   }
 #pragma unroll
-  for (int im = 0; im < MAXIMG; ++im) {
-    if (im < nimg) {
+  for (int j = 0; j < PER; ++j) {
+    if (j * NT < n8) {
+      const int i = min(j * NT + tid, n8 - 1);
+      const int o = 2 * lds_chunk<BITS, 4>(i >> 1, S) + (i & 1);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int i = j * NT + tid;
-        if (j * NT < n8 && i < n8)
-          dst[(int64_t)im * n8 + 2 * lds_chunk<BITS, 4>(i >> 1, S) + (i & 1)] = t[im][j];
-      }
+      for (int im = 0; im < MAXIMG; ++im) dst[(int64_t)min(im, nimg - 1) * n8 + o] = t[im][j];
     }
   }
 }

@@ -7,14 +7,14 @@
 // microseconds), so every step runs inside one launch, and the launch is laid
 // out so that all expert weights are in flight as soon as the routing is known.
 //
-// Work items.  Workgroup b first takes item b (no atomic on the way in); the
-// items past the grid are handed out in order from 64 interleaved sub-queues.
-// Item f carries up to four parts:
+// Work items.  Workgroup b first takes item b (no atomic on the way in); items
+// past the grid, if any, are handed out in order from 64 interleaved
+// sub-queues.  Item f carries up to four parts:
 //
-//   router rows f, f + nRr, ...   fp64 logits (the E router rows, then the
-//                        shared-expert gate row; a quarter row per wave),
-//                        published at once; nRr = min(grid, E + 1), so every
-//                        router row belongs to a first item
+//   router rows f, f + nRr, ... below E   fp64 logits, a quarter row per wave;
+//                        nRr = min(grid, E), so every router row belongs to a
+//                        first item; item E mod nRr also computes row E, the
+//                        shared-expert gate, after the routing is published
 //   shared gate/up part f   a block of the shared expert's gate and up rows
 //   routed gate/up part f   the same for routed expert slot f / nGUs
 //   down part f          a block of down rows of EVERY active expert,
@@ -22,31 +22,29 @@
 //
 // A gate/up part publishes its SwiGLU outputs as prepared fp16 blocks (one
 // power-of-two scale per code word of the down rows), so no consumer converts
-// them.  An item requests its router row, its shared gate/up rows and x at
-// once, computes the logits and publishes them, computes its shared part,
-// then (the routing known) issues its routed gate/up loads and its down tiles
-// together, keeps the down tiles in registers while it computes its gate/up
-// part, and only then needs every SwiGLU output (the item flag) for its down
-// part.  It waits for the flag only when every item of the queue is held by a
-// running workgroup: each gate/up part then finishes without waiting on any
-// down part.  Otherwise (fewer resident workgroups than items) it defers its
-// down part to a list worked off once the queue is empty; the flag counts
-// every item's decision, so after it the list is complete.  Router rows only
-// sit in first items, which never wait before publishing them, so the routing
-// always completes; one resident workgroup per sub-queue (workgroups 0..63,
-// dispatched first) is enough for the rest to progress.
+// them.  An item requests its router row and x, publishes the logits, computes
+// its shared gate/up part while the routing completes, recomputes the top-k
+// from the published logits (same inputs, same result in every workgroup),
+// computes and publishes its routed gate/up part, arrives, and only then
+// requests its down tiles, which load while the other parts finish; the item
+// flag (every item arrived) releases the down parts.  A down part waits for
+// the flag only when every item of the queue is held by a running workgroup:
+// each gate/up part then finishes without waiting on any down part.
+// Otherwise (fewer resident workgroups than items) it defers its down part to
+// a list worked off once the queue is empty; the flag counts every item's
+// decision, so after it the list is complete.  The last down part computes
+// the RMSNorm; the last workgroup to leave resets counters and flags.
 //
 // Hardware facts this layout answers (measured on MI355X): atomics on one
 // address serialise at ~11 ns each (far slower while HBM is saturated), so
 // every counter is split into 64 sub-counters plus a top counter, each on its
-// own 256-byte line, and phase completion is
-// broadcast through 64 flags on separate lines (each waiting workgroup polls
-// its own).  Every consumer recomputes the top-k from the published logits
-// (same inputs, same result) instead of waiting for a published choice.  A
-// load whose data is used at once behind a branch costs a full memory round
-// trip each, so every batch of loads here is unconditional (clamped
-// addresses).  The last down part computes the RMSNorm; the last workgroup to
-// leave resets counters and flags.
+// own 256-byte line, and phase completion is broadcast through 64 flags on
+// separate lines (each waiting workgroup polls its own).  A wave's loads
+// complete in issue order, so a small load the critical path needs is never
+// issued behind bulk loads it does not need (the down tiles go out after the
+// gate/up part is published).  A load whose data is used at once behind a
+// branch costs a full memory round trip each, so every batch of loads here is
+// issued on every path (clamped addresses).
 #pragma once
 
 #include "fmoe_fused_args.h"
@@ -56,7 +54,6 @@ namespace fmoe {
 
 constexpr int kFusedMaxSlots = 5;   // active experts whose down tiles are held at once
 constexpr int kFusedImgPer = 4;     // 8-byte words per thread of one SwiGLU image
-constexpr int kNormPer = 16;        // gamma*h values per thread loaded at once by the norm
 constexpr int kSpinLimit = 1 << 22;
 
 // Counter block layout, in 256-byte lines (64 ints) of the workspace.  Every
@@ -77,6 +74,7 @@ constexpr int kDefTailLine = kTimeoutLine + 2;      // deferred down parts: how 
 constexpr int kRouterFlagLine = kTimeoutLine + 4;   // 64 flags
 constexpr int kItemFlagLine = kRouterFlagLine + 64; // 64 flags
 static_assert(kItemFlagLine + 64 <= kFusedCtrLines, "counter block too small");
+constexpr int kNormPer = 16;   // gamma*h values per thread loaded at once by the norm
 
 // LDS of one workgroup: [x fp32 | x prepared | down-stage activation images].
 inline size_t fused_lds_bytes(int H, int I, int bits) {
@@ -136,11 +134,9 @@ __device__ __forceinline__ bool queue_drained(QueueView q, int n_main) {
   return __ballot(q.started < want_started || q.head < want_head) == 0;
 }
 
-// ------------------------------------------------------------ wave max (u64)
-// Maximum over the wave, returned in every lane, on 32-bit DPP maxima: the
-// high halves first, then the low halves of the lanes holding the highest
-// high half (exact for unsigned keys).  DPP lanes outside a row mask read 0,
-// which never wins.
+// ------------------------------------------------------------ wave max (u32)
+// Maximum over the wave, returned in every lane, on DPP maxima.  DPP lanes
+// outside a row mask read 0, which never wins (unsigned keys).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, true));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xF, 0xF, true));
@@ -149,12 +145,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast15, 0xA, 0xF, true));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast31, 0xC, 0xF, true));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  const uint32_t hi = (uint32_t)(v >> 32);
-  const uint32_t mh = wave_max_u32(hi);
-  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
-  return ((uint64_t)mh << 32) | ml;
 }
 // The logit a key of order_key was made from.
 __device__ __forceinline__ double key_value(uint64_t k) {
@@ -168,42 +158,48 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// Per-workgroup cache of the routing decision.
+// Per-workgroup cache of the routing decision.  Down slot 0 is the shared
+// expert, slot 1 + i the i-th selected expert; coef follows the slots.
 struct RouteCache {
   int ready;
   int sel[16];
-  float coef[17];   // routing weights, then the shared gate
+  float coef[17];   // shared gate (set by the first down batch), then routing weights
 };
 
-// Top-k of the published logits (ties: lower index) by the whole workgroup:
-// wave w holds logits w*64*VW .. (w+1)*64*VW-1 (VW per lane, agent-scope
-// loads: other workgroups wrote them) and picks its own top-k; wave 0 then
-// merges the 4k candidates (candidate w*k + r in lane w*k + r, so equal keys
-// still resolve to the lower index).  Weights = softmax over the selected
-// logits, shared gate = sigmoid of logit E.  Called by all threads.
+// Top-k of the published logits (ties: lower index) by the whole workgroup.
+// Wave w holds logits w*64*VW .. (w+1)*64*VW-1 (VW per lane, agent-scope
+// loads: other workgroups wrote them) and takes its k largest in k rounds of
+// a wave maximum; a round compares the high 32 bits of the keys only, unless
+// several lanes share the largest high half.  Wave 0 then ranks the 4k
+// candidates against each other (lane c holds candidate c and counts those
+// that beat it), so the merge takes no serial rounds.  Weights = softmax over
+// the selected logits.  Called by all threads, in two halves: the loads, then
+// (with other loads possibly issued in between) the selection.
 struct TopkCand {
-  uint64_t key[4][16];
-  int idx[4][16];
+  uint64_t key[64];
+  int idx[64];
 };
-__device__ __forceinline__ void topk_round(uint64_t best, int best_e, int& win_e, uint64_t& win_k,
-                                           int& lane_out) {
-  const uint64_t m = wave_max_u64(best);
-  const uint64_t ball = __ballot(best == m);
-  const int L = __ffsll((unsigned long long)ball) - 1;
-  win_e = __builtin_amdgcn_readlane(best_e, L);
-  win_k = m;
-  lane_out = L;
-}
 template <int VW>
-__device__ __forceinline__ void fused_topk(const FusedArgs& a, RouteCache& rc, TopkCand& tc) {
+__device__ __forceinline__ void topk_keys(const FusedArgs& a, double (&l)[VW]) {
   const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
-  uint64_t key[VW];
 #pragma unroll
   for (int v = 0; v < VW; ++v) {
     const int e = (wave * 64 + lane) * VW + v;
-    const double l = ld_agent(a.lg64 + (e < a.E ? e : a.E - 1));
-    key[v] = e < a.E ? order_key(l) : 0ull;
+    l[v] = ld_agent(a.lg64 + (e < a.E ? e : a.E - 1));
   }
+}
+template <int VW>
+__device__ __forceinline__ void topk_select(const FusedArgs& a, const double (&l)[VW],
+                                            RouteCache& rc, TopkCand& tc) {
+  const int tid = tid_x(), lane = tid & 63, wave = tid >> 6;
+  // 1 <= k <= 16 (checked on the host); without it the compiler keeps a path
+  // where the logit loads stay unconsumed and then waits for them much later.
+  __builtin_assume(a.k >= 1);
+  __builtin_assume(a.k <= 16);
+  uint64_t key[VW];
+#pragma unroll
+  for (int v = 0; v < VW; ++v)
+    key[v] = (wave * 64 + lane) * VW + v < a.E ? order_key(l[v]) : 0ull;
   for (int r = 0; r < a.k; ++r) {
     uint64_t best = 0;
     int bv = 0;
@@ -211,77 +207,103 @@ __device__ __forceinline__ void fused_topk(const FusedArgs& a, RouteCache& rc, T
     for (int v = 0; v < VW; ++v) {
       if (key[v] > best) { best = key[v]; bv = v; }
     }
-    int win_e, L;
-    uint64_t win_k;
-    topk_round(best, (wave * 64 + lane) * VW + bv, win_e, win_k, L);
+    const uint32_t hi = (uint32_t)(best >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    uint64_t ball = __ballot(hi == mh);
+    if (__popcll(ball) != 1) {   // the high halves tie: full keys of those lanes
+      const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)best : 0u);
+      ball = __ballot(best == (((uint64_t)mh << 32) | ml));
+    }
+    const int L = __ffsll((unsigned long long)ball) - 1;
+    const uint32_t wl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, L);
+    const int we = __builtin_amdgcn_readlane((wave * 64 + lane) * VW + bv, L);
 #pragma unroll
     for (int v = 0; v < VW; ++v)
       if (lane == L && v == bv) key[v] = 0ull;
-    if (lane == 0) { tc.key[wave][r] = win_k; tc.idx[wave][r] = win_e; }
+    if (lane == 0) {
+      tc.key[wave * a.k + r] = ((uint64_t)mh << 32) | wl;
+      tc.idx[wave * a.k + r] = we;
+    }
   }
   lds_barrier();
   if (wave == 0) {
-    const bool c = lane < 4 * a.k;
-    uint64_t ck = c ? tc.key[lane / a.k][lane % a.k] : 0ull;
-    const int ce = c ? tc.idx[lane / a.k][lane % a.k] : 0;
-    int sel_e = 0;
-    uint64_t sel_k = 0;
-    for (int r = 0; r < a.k; ++r) {
-      int win_e, L;
-      uint64_t win_k;
-      topk_round(ck, ce, win_e, win_k, L);
-      if (lane == L) ck = 0ull;
-      if (lane == r) { sel_e = win_e; sel_k = win_k; }
+    const int nc = 4 * a.k;
+    const bool c = lane < nc;
+    const uint64_t ck = c ? tc.key[lane] : 0ull;
+    const int ce = c ? tc.idx[lane] : 0;
+    int rank = 0;
+    for (int j0 = 0; j0 < nc; j0 += 16) {
+      uint64_t kk[16];
+      int ee[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int j = min(j0 + t, nc - 1);
+        kk[t] = tc.key[j];
+        ee[t] = tc.idx[j];
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if (j0 + t < nc) rank += (kk[t] > ck || (kk[t] == ck && ee[t] < ce)) ? 1 : 0;
     }
-    const double sel_l = key_value(sel_k);
-    const double l0 = readlane_f64(sel_l, 0);
-    const float ex = lane < a.k ? expf((float)(sel_l - l0)) : 0.f;
+    const bool sel = c && rank < a.k;
+    const int L0 = __ffsll((unsigned long long)__ballot(c && rank == 0)) - 1;
+    const double l = key_value(ck);
+    const double l0 = readlane_f64(l, L0);
+    const float ex = sel ? expf((float)(l - l0)) : 0.f;
     const float z = wave_sum(ex);
-    if (lane < a.k) {
-      rc.sel[lane] = sel_e;
-      rc.coef[lane] = ex / z;
+    if (sel) {
+      rc.sel[rank] = ce;
+      rc.coef[1 + rank] = ex / z;
     }
-    if (lane == 0) rc.coef[a.k] = 1.f / (1.f + expf(-(float)ld_agent(a.lg64 + a.E)));
   }
 }
 
 // ------------------------------------------------------------ down parts
-// Tiles of down rows wrow0 + u*RPI + lane_row (u < kFusedUD) of the active
-// experts s0 .. s0+ns-1 (slot k = the shared expert).
-template <int BITS, int G, int SB>
+// Tiles of down rows wrow0 + u*RPI + lane_row (u < kFusedUD) of down slots
+// s0 + sl for sl in [SL0, SL1) (slot 0 = the shared expert, slot 1 + i =
+// selected expert i); slots past the last active one repeat it (never read).
+// The launcher admits only hidden sizes that are a multiple of the part's
+// rows, so every row exists.  Every load is issued on every path: the
+// compiler's waits count the loads issued after the one waited for, and a
+// load skipped on some path makes it wait for everything on all of them.
+template <int BITS, int G, int SB, int SL0, int SL1>
 __device__ __forceinline__ void down_load(Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSlots][kFusedUD],
                                           const FusedArgs& a, const RouteCache& rc, int wrow0,
-                                          int s0, int ns, const RowGeo& geo) {
+                                          int s0, const RowGeo& geo) {
 #pragma unroll
-  for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
-    const int slot = s0 + sl;
-    const int64_t e = slot < a.k ? rc.sel[slot < a.k ? slot : 0] : a.E;
+  for (int sl = SL0; sl < SL1; ++sl) {
+    const int ds = min(s0 + sl, a.k);
+    const int64_t e = ds == 0 ? a.E : rc.sel[ds > 0 ? ds - 1 : 0];
     const uint8_t* base = a.src.base + e * a.src.stride;
 #pragma unroll
     for (int u = 0; u < kFusedUD; ++u) {
       const int m = wrow0 + u * geo.RPI + geo.lane_row;
-      if (sl < ns && m < a.H)
-        tl[sl][u].load(base + a.src.off[6], base + a.src.off[7], base + a.src.off[8], a.I, m, geo);
-      else
-        tl[sl][u].zero();
+      tl[sl][u].load(base + a.src.off[6], base + a.src.off[7], base + a.src.off[8], a.I, m, geo);
     }
   }
 }
 
-// acc[u] += sum over the batch's experts of coef * (down row . SwiGLU output).
-// The batch's word-blocked SwiGLU images (published by the gate/up parts) are
-// copied to LDS first (all threads).
+// acc[u] += sum over the batch's down slots of coef * (down row . SwiGLU
+// output).  The batch's word-blocked SwiGLU images (published by the gate/up
+// parts before the item flag) are copied to LDS first (all threads); the first
+// batch also takes the shared-expert gate from its logit.
 template <int BITS, int G, int SB>
 __device__ __forceinline__ void down_dot(const Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSlots][kFusedUD],
                                          float (&acc)[kFusedUD], const FusedArgs& a,
-                                         const RouteCache& rc, uint8_t* lds_ap, int s0, int ns,
+                                         RouteCache& rc, uint8_t* lds_ap, int s0, int ns,
                                          const RowGeo& geo) {
   const int64_t ib = wimg_bytes(a.I, BITS);
+  const double gl = ld_agent(a.lg64 + a.E);
   copy_wimgs_to_lds_agent<BITS, kThreads, kFusedMaxSlots, kFusedImgPer>(
       reinterpret_cast<uint64_t*>(lds_ap),
       reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.abuf) + s0 * ib), a.I,
       ns);
+  if (s0 == 0 && tid_x() == 0) rc.coef[0] = 1.f / (1.f + expf(-(float)gl));
   lds_barrier();
+  // Lane shares weighted by coef first, one cross-lane sum per row at the end.
+  float part[kFusedUD];
+#pragma unroll
+  for (int u = 0; u < kFusedUD; ++u) part[u] = 0.f;
 #pragma unroll
   for (int sl = 0; sl < kFusedMaxSlots; ++sl) {
     if (sl < ns) {
@@ -289,13 +311,12 @@ __device__ __forceinline__ void down_dot(const Tile<BITS, G, SB, 1> (&tl)[kFused
       XRegsW<BITS> xr;
       xr.load(lds_ap + sl * ib, a.I, geo);
 #pragma unroll
-      for (int u = 0; u < kFusedUD; ++u) {
-        const float v = sum_lanes(tile_dot_w(tl[sl][u], xr), geo.LPR);
-        acc[u] = fmaf(coef, v, acc[u]);
-      }
+      for (int u = 0; u < kFusedUD; ++u) part[u] = fmaf(coef, tile_dot_w(tl[sl][u], xr), part[u]);
     }
     __builtin_amdgcn_sched_barrier(0);   // one expert's activations in registers at a time
   }
+#pragma unroll
+  for (int u = 0; u < kFusedUD; ++u) acc[u] += sum_lanes(part[u], geo.LPR);
   lds_barrier();   // lds_ap is reused by the next batch
 }
 
@@ -303,34 +324,32 @@ __device__ __forceinline__ void down_dot(const Tile<BITS, G, SB, 1> (&tl)[kFused
 // past the first kFusedMaxSlots).
 template <int BITS, int G, int SB>
 __device__ __forceinline__ void down_batches(float (&acc)[kFusedUD], const FusedArgs& a,
-                                             const RouteCache& rc, uint8_t* lds_ap, int wrow0,
+                                             RouteCache& rc, uint8_t* lds_ap, int wrow0,
                                              int s_begin, const RowGeo& geo) {
   const int kp1 = a.k + 1;
   for (int s0 = s_begin; s0 < kp1; s0 += kFusedMaxSlots) {
     const int ns = min(kFusedMaxSlots, kp1 - s0);
     Tile<BITS, G, SB, 1> tl[kFusedMaxSlots][kFusedUD];
-    down_load<BITS, G, SB>(tl, a, rc, wrow0, s0, ns, geo);
+    down_load<BITS, G, SB, 0, kFusedMaxSlots>(tl, a, rc, wrow0, s0, geo);
     down_dot<BITS, G, SB>(tl, acc, a, rc, lds_ap, s0, ns, geo);
   }
 }
 
-// Residual and gamma of the part's rows (clamped loads).
+// Residual and gamma of the part's rows.
 __device__ __forceinline__ void down_vectors(const FusedArgs& a, int wrow0, int rpi, int lane_row,
                                              float (&rv)[kFusedUD], float (&gv)[kFusedUD]) {
 #pragma unroll
   for (int u = 0; u < kFusedUD; ++u) {
     const int m = wrow0 + u * rpi + lane_row;
-    const int mc = m < a.H ? m : a.H - 1;
-    rv[u] = a.resid[mc];
-    gv[u] = a.gamma[mc];
+    rv[u] = a.resid[m];
+    gv[u] = a.gamma[m];
   }
 }
 
 // h = residual + combined expert output for the part's rows; gamma*h and the
 // part's sum of h^2 are published, and the last part to arrive finishes the
-// RMSNorm and the routing outputs.  Called by the whole workgroup.
-__device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache& rc, int d,
-                                            const float (&acc)[kFusedUD],
+// RMSNorm.  Called by the whole workgroup.
+__device__ __forceinline__ void down_finish(const FusedArgs& a, int d, const float (&acc)[kFusedUD],
                                             const float (&rv)[kFusedUD],
                                             const float (&gv)[kFusedUD], int wrow0, int rpi,
                                             int lane_row, bool writer, float* s_part,
@@ -340,7 +359,7 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache
 #pragma unroll
   for (int u = 0; u < kFusedUD; ++u) {
     const int m = wrow0 + u * rpi + lane_row;
-    if (m < a.H && writer) {
+    if (writer) {
       const float h = rv[u] + acc[u];
       a.h_out[m] = h;
       st_agent(a.gh + m, gv[u] * h);
@@ -401,10 +420,6 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, const RouteCache
       const int m = m0 + j * kThreads + tid;
       if (m < a.H) a.y_out[m] = hv[j] * inv;
     }
-  }
-  if (tid < a.k) {
-    if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
-    if (a.w_out) a.w_out[tid] = rc.coef[tid];
   }
 }
 
@@ -475,30 +490,26 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     uint8_t* lds_xp = lds + (int64_t)a.H * 4;
     uint8_t* lds_ap = lds_xp + xprep_bytes(a.H);
     const int n_main = a.nF;
+    const bool queued = n_main > (int)gridDim.x;   // items past the grid: queue and deferral
     int* ctr = a.ctr;
-
-    auto ensure_routing = [&]() {
-      if (rc.ready) return;  // workgroup-uniform (shared, read after a barrier)
-      if (tid == 0) wait_flag(ctr, kRouterFlagLine);
-      lds_barrier();
-      fused_topk<VMAX / 4>(a, rc, s_tc);
-      if (tid == 0) rc.ready = 1;
-      lds_barrier();
-    };
 
     // Next piece of work: first item blockIdx.x, then item < n_main from the
     // queue of the items past the grid; once that is empty, n_main + d for
     // deferred down part d (after the item flag, when the list is complete);
-    // -1 when there is nothing left.
+    // -1 when there is nothing left.  (Nothing of the last item is still in
+    // flight here; the wait says so to the compiler, which otherwise assumes
+    // loads of skipped paths pending and waits for them inside the phases.)
+    vm_drain();
     lds_barrier();
     if (tid == 0) {
       int it = -1;
       if (first) {
         first = false;
         it = blockIdx.x;
-        __hip_atomic_fetch_add(ctr_line(ctr, kStartLine + subq), 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);   // result unused: no round trip
-      } else if (!listing) {
+        if (queued)
+          __hip_atomic_fetch_add(ctr_line(ctr, kStartLine + subq), 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);   // result unused: no round trip
+      } else if (queued && !listing) {
         it = (int)gridDim.x + subq + kSubs * add_agent(ctr_line(ctr, kQHeadLine + subq), 1);
         if (it >= n_main) {
           listing = true;
@@ -520,8 +531,9 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     if (item < 0) break;
 
     // What the item holds (all workgroup-uniform): router rows item,
-    // item + nRr, ... (item < nRr), shared gate/up part item, routed gate/up
-    // part item (expert slot item / nGUs), down part item.
+    // item + nRr, ... below E (item < nRr) and, for item E mod nRr, the
+    // shared-expert gate row E; shared gate/up part item; routed gate/up part
+    // item (expert slot item / nGUs); down part item.
     int spart = -1, gslot = -1, gpart = 0, dpart = -1;
     const bool deferred = item >= n_main;
     const bool routes = !deferred && item < a.nRr;
@@ -534,10 +546,10 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     }
     const RowGeo geoH(a.H, BITS), geoI(a.I, BITS);
 
-    // Gate/up part (slot, part): SwiGLU of its rows, published as one block
-    // of word-blocked prepared image per code word of the down rows.
-    auto gu_load = [&](TileH (&tg)[kUG], TileH (&tu)[kUG], int slot, int part) {
-      const int64_t e = slot < a.k ? rc.sel[slot] : a.E;
+    // Gate/up part `part` of expert e: SwiGLU of its rows, published as one
+    // block of word-blocked prepared image per code word of the down rows
+    // (image slot = down slot: 0 shared, 1 + i selected expert i).
+    auto gu_load = [&](TileH (&tg)[kUG], TileH (&tu)[kUG], int64_t e, int part) {
       const uint8_t* base = a.src.base + e * a.src.stride;
       const int n0 = part * a.gu_rows + wave * kUG;
 #pragma unroll
@@ -548,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
                    geoH);
       }
     };
-    auto gu_finish = [&](const TileH (&tg)[kUG], const TileH (&tu)[kUG], int slot, int part) {
+    auto gu_finish = [&](const TileH (&tg)[kUG], const TileH (&tu)[kUG], int islot, int part) {
       lds_barrier();   // prepared x visible; s_act free
       XRegs<BITS, NSH> xr;
       xr.load(lds_xp, a.H, geoH);
@@ -560,11 +572,10 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       }
       lds_barrier();
       if (wave == 0) {   // the part's rows are whole code-word blocks of the image
-        uint8_t* img = reinterpret_cast<uint8_t*>(a.abuf) + slot * wimg_bytes(a.I, BITS);
+        uint8_t* img = reinterpret_cast<uint8_t*>(a.abuf) + islot * wimg_bytes(a.I, BITS);
         const bool live = lane < a.gu_rows;
         wimg_publish<BITS>(s_act[live ? lane : 0], live, img, a.I, part * a.gu_rows + lane);
       }
-      vm_drain();
     };
     // A quarter of router row e per wave (row E is the shared-expert gate).
     auto router_load = [&](float4 (&wv)[kQ], int e) {
@@ -573,84 +584,115 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
 #pragma unroll
       for (int q = 0; q < kQ; ++q) wv[q] = ld_nt(row + q0 + q * 64);
     };
+    // fp64 logit of the row in wv against x in LDS, stored by thread 0.
+    auto router_dot = [&](const float4 (&wv)[kQ], int e) {
+      const float4* xl = reinterpret_cast<const float4*>(lds_x) + wave * (a.H / 16) + lane;
+      double racc = 0.0;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const float4 xv = xl[q * 64];
+        racc = fma((double)wv[q].x, (double)xv.x, racc);
+        racc = fma((double)wv[q].y, (double)xv.y, racc);
+        racc = fma((double)wv[q].z, (double)xv.z, racc);
+        racc = fma((double)wv[q].w, (double)xv.w, racc);
+      }
+      racc = sum_lanes_f64(racc);
+      if (lane == kWave - 1) s_rp[wave] = racc;
+      lds_barrier();
+      if (tid == 0) st_agent(a.lg64 + e, ((s_rp[0] + s_rp[1]) + s_rp[2]) + s_rp[3]);
+    };
 
-    // Two passes over the item's gate/up parts (one copy of that code): pass 0
-    // the shared expert's part, which needs no routing, with the router rows
-    // and x staging between its loads and its compute; pass 1 the routed part
-    // after the routing, with the down tiles loaded alongside and held in
-    // registers until every SwiGLU output is in.
+    // Phases of an item, each a straight run of loads then their use (no
+    // join between a load and its use, where the compiler would wait):
+    //   1. x staged in LDS; router rows -> logits published, router arrival
+    //   2. the shared expert's gate/up part, in the time the routing takes
+    //   3. the routing (the shared expert's down tile is requested between
+    //      the logits and the selection); the routed gate/up part computed and
+    //      published
+    //   4. arrival; the selected experts' down tiles requested; the item flag;
+    //      the down part from the held tiles
     TileI tl[kFusedMaxSlots][kFusedUD];
     float acc[kFusedUD], rv[kFusedUD], gv[kFusedUD];
     const int wrow0 = (dpart >= 0 ? dpart : 0) * a.d_rows + wave * (kFusedUD * geoI.RPI);
 #pragma unroll
     for (int u = 0; u < kFusedUD; ++u) acc[u] = 0.f;
     if (!deferred) {
-      float4 wv[kQ];
-      if (routes) router_load(wv, item);
-#pragma unroll 1
-      for (int pass = 0; pass < 2; ++pass) {
-        const bool has = pass == 0 ? spart >= 0 : gslot >= 0;
-        const int slot = pass == 0 ? a.k : gslot, part = pass == 0 ? spart : gpart;
-        if (pass == 1 && (gslot >= 0 || dpart >= 0)) ensure_routing();
-        TileH tg[kUG], tu[kUG];
-        if (has) gu_load(tg, tu, slot, part);
-        if (pass == 0) {
-          // x staged in LDS (fp32 for the router rows, prepared for the
-          // gate/up rows) from registers, then the router rows (fp64)
-          if (!have_x) {
-            float4 xq[kQ];
+      // x is read only here, before this item's gate/up part, and every h_out
+      // write waits for the item flag, so h_out may alias x.
+      if (routes || !have_x) {
+        float4 wv[kQ];
+        if (routes) router_load(wv, item);
+        if (!have_x) {
+          float4 xq[kQ];
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) xq[q] = reinterpret_cast<const float4*>(a.x)[q * kThreads + tid];
+          for (int q = 0; q < kQ; ++q) xq[q] = reinterpret_cast<const float4*>(a.x)[q * kThreads + tid];
 #pragma unroll
-            for (int q = 0; q < kQ; ++q) {
-              reinterpret_cast<float4*>(lds_x)[q * kThreads + tid] = xq[q];
-              prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
-            }
-            have_x = true;
-            lds_barrier();
+          for (int q = 0; q < kQ; ++q) {
+            reinterpret_cast<float4*>(lds_x)[q * kThreads + tid] = xq[q];
+            prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
           }
-          if (routes) {
-            for (int e = item;;) {
-              const float4* xl = reinterpret_cast<const float4*>(lds_x) + wave * (a.H / 16) + lane;
-              double racc = 0.0;
-#pragma unroll
-              for (int q = 0; q < kQ; ++q) {
-                const float4 xv = xl[q * 64];
-                racc = fma((double)wv[q].x, (double)xv.x, racc);
-                racc = fma((double)wv[q].y, (double)xv.y, racc);
-                racc = fma((double)wv[q].z, (double)xv.z, racc);
-                racc = fma((double)wv[q].w, (double)xv.w, racc);
-              }
-              racc = sum_lanes_f64(racc);
-              if (lane == kWave - 1) s_rp[wave] = racc;
-              lds_barrier();
-              if (tid == 0) st_agent(a.lg64 + e, ((s_rp[0] + s_rp[1]) + s_rp[2]) + s_rp[3]);
-              e += a.nRr;
-              if (e > a.E) break;
-              router_load(wv, e);
-              lds_barrier();   // s_rp is reused
-            }
-            vm_drain();
-            lds_barrier();
-            if (tid == 0 && arrive(ctr, kRouterSubLine, item, a.nRr))
-              raise_flags(ctr, kRouterFlagLine);
-          }
-        } else if (dpart >= 0) {
-          QueueView qv{0, 0};
-          const bool check = wave == 0 && !drained;
-          if (check) qv = load_queue(ctr);   // consumed once the tile loads are out
-          down_load<BITS, G, SB>(tl, a, rc, wrow0, 0, min(kFusedMaxSlots, kp1), geoI);
-          down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
-          if (check) drained = queue_drained(qv, n_main);
+          have_x = true;
+          lds_barrier();
         }
-        if (has) gu_finish(tg, tu, slot, part);
+        if (routes) {
+          for (int e = item;;) {
+            router_dot(wv, e);
+            e += a.nRr;
+            if (e >= a.E) break;
+            router_load(wv, e);
+            lds_barrier();   // s_rp is reused
+          }
+          vm_drain();
+          lds_barrier();
+          if (tid == 0 && arrive(ctr, kRouterSubLine, item, a.nRr))
+            raise_flags(ctr, kRouterFlagLine);
+          if (item == a.E % a.nRr) {
+            // The shared-expert gate is first needed by the down parts, after
+            // the item flag, which this item's arrival (after this store) gates.
+            router_load(wv, a.E);
+            lds_barrier();   // s_rp is reused
+            router_dot(wv, a.E);
+          }
+        }
       }
-      // Every item arrives once, after its gate/up parts and its decision to
-      // wait for the item flag or to defer its down part.
+      if (spart >= 0) {
+        TileH tg[kUG], tu[kUG];
+        gu_load(tg, tu, a.E, spart);
+        gu_finish(tg, tu, 0, spart);
+      }
+      // The routing: logits first, then the shared expert's down tile, so
+      // that neither the selection nor the tile waits for the other.
+      double lg[VMAX / 4];
+      const bool route_now = !rc.ready;   // workgroup-uniform (shared, read after a barrier)
+      if (route_now) {
+        if (tid == 0) wait_flag(ctr, kRouterFlagLine);
+        lds_barrier();
+        topk_keys<VMAX / 4>(a, lg);
+      }
+      down_load<BITS, G, SB, 0, 1>(tl, a, rc, wrow0, 0, geoI);
+      if (route_now) {
+        topk_select<VMAX / 4>(a, lg, rc, s_tc);
+        if (tid == 0) rc.ready = 1;
+        lds_barrier();
+      }
+      {
+        // All of this phase's loads on every path (the part clamped for items
+        // without one; see down_load), so that the gate/up compute waits for
+        // its own tiles only.  The queue view rides along for the decision.
+        TileH tg[kUG], tu[kUG];
+        gu_load(tg, tu, rc.sel[gslot >= 0 ? gslot : 0], gslot >= 0 ? gpart : 0);
+        const QueueView qv = load_queue(ctr);
+        if (gslot >= 0) gu_finish(tg, tu, gslot + 1, gpart);
+        if (wave == 0 && !drained) drained = !queued || queue_drained(qv, n_main);
+      }
+      // Every item arrives once, after its gate/up parts (published: wave 0
+      // drains its stores) and its decision to wait for the item flag or to
+      // defer its down part.
+      if (wave == 0) vm_drain();
       lds_barrier();
       if (wave == 0) {
         bool defer = false;
-        if (dpart >= 0 && !drained) {
+        if (queued && dpart >= 0 && !drained) {
           drained = queue_drained(load_queue(ctr), n_main);
           defer = !drained;
         }
@@ -666,6 +708,9 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       }
       lds_barrier();
       if (dpart < 0 || s_defer) continue;
+      // The selected experts' down tiles load while the other parts finish.
+      down_load<BITS, G, SB, 1, kFusedMaxSlots>(tl, a, rc, wrow0, 0, geoI);
+      down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
       if (tid == 0) wait_flag(ctr, kItemFlagLine);
       lds_barrier();
       down_dot<BITS, G, SB>(tl, acc, a, rc, lds_ap, 0, min(kFusedMaxSlots, kp1), geoI);
@@ -676,8 +721,12 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
       down_batches<BITS, G, SB>(acc, a, rc, lds_ap, wrow0, 0, geoI);
     }
-    down_finish(a, rc, dpart, acc, rv, gv, wrow0, geoI.RPI, geoI.lane_row,
+    down_finish(a, dpart, acc, rv, gv, wrow0, geoI.RPI, geoI.lane_row,
                 geoI.lane_seg == geoI.LPR - 1, s_part, s_flag);
+    if (s_flag && tid < a.k) {   // the last down part also writes the routing outputs
+      if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
+      if (a.w_out) a.w_out[tid] = rc.coef[1 + tid];
+    }
   }
 
   // Leave; the last workgroup out resets queue heads, flags and the list.
@@ -686,12 +735,14 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     int* ctr = a.ctr;
     vm_drain();
     if (arrive(ctr, kExitSubLine, blockIdx.x, gridDim.x)) {
-      for (int s = 0; s < kSubs; ++s) {
-        st_agent(ctr_line(ctr, kQHeadLine + s), 0);
-        st_agent(ctr_line(ctr, kStartLine + s), 0);
+      if (a.nF > (int)gridDim.x) {
+        for (int s = 0; s < kSubs; ++s) {
+          st_agent(ctr_line(ctr, kQHeadLine + s), 0);
+          st_agent(ctr_line(ctr, kStartLine + s), 0);
+        }
+        st_agent(ctr_line(ctr, kDefHeadLine), 0);
+        st_agent(ctr_line(ctr, kDefTailLine), 0);
       }
-      st_agent(ctr_line(ctr, kDefHeadLine), 0);
-      st_agent(ctr_line(ctr, kDefTailLine), 0);
       for (int j = 0; j < 64; ++j) {
         st_agent(ctr_line(ctr, kRouterFlagLine + j), 0);
         st_agent(ctr_line(ctr, kItemFlagLine + j), 0);

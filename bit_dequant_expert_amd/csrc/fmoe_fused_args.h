@@ -20,6 +20,10 @@ constexpr size_t kFusedCtrBytes = (size_t)kFusedCtrLines * 256;
 constexpr int kFusedWaves = 4;
 constexpr int kFusedUD = 1;
 constexpr int kFusedMaxNormParts = 4 * 256;   // down parts the final norm sums
+// Every workspace layout keeps its data past this head, which holds only
+// counters that each call returns to zero: a call of any kind never leaves
+// data where another kind of call keeps its counters.
+constexpr size_t kWsReserved = kFusedCtrBytes;
 __host__ __device__ constexpr int fused_ug(int nsh) { return nsh == 1 ? 4 : 2; }
 inline int fused_gu_rows(int H, int bits) { return kFusedWaves * fused_ug(segs_per_lane(H, bits)); }
 inline int fused_d_rows(int I, int bits) { return kFusedWaves * kFusedUD * rows_per_iter(I, bits); }
@@ -39,7 +43,7 @@ struct FusedArgs {
   float eps;
   int H, I, E, k;
   double* lg64;      // [E+1]
-  float* abuf;       // [(k+1) * I]  SwiGLU outputs, slot-major
+  float* abuf;       // [(k+1) * I]  SwiGLU outputs, slot-major (slot 0 the shared expert)
   float* gh;         // [H]  gamma * h, read by the final norm
   float* partials;   // [nD]  sum of h^2 per down part
   int* dlist;        // [nD]  down parts deferred to the end of the queue
@@ -48,8 +52,9 @@ struct FusedArgs {
   int nD;            // down parts
   int nF;            // items: item f holds shared gate/up part f, routed gate/up
                      // part f (expert slot f / nGUs) and down part f
-  int nRr;           // items holding router rows (rows f, f + nRr, ...); set by
-                     // the launcher to min(grid, E + 1), so they are all first items
+  int nRr;           // items holding router rows (rows f, f + nRr, ... below E;
+                     // row E, the shared-expert gate, goes to item E mod nRr); set
+                     // by the launcher to min(grid, E), so they are all first items
   int gu_rows;       // gate/up rows per part
   int d_rows;        // down rows per part
 };
