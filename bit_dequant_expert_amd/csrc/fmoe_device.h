@@ -33,6 +33,13 @@ namespace fmoe {
 
 constexpr int kWave = 64;
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
+// kMagic in a VGPR: (codes & mask) | magic then takes one v_and_or_b32 (the
+// mask in an SGPR) instead of an and and an or with two literals.
+__device__ __forceinline__ uint32_t magic_v() {
+  uint32_t m = kMagic;
+  asm volatile("" : "+v"(m));
+  return m;
+}
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
@@ -424,21 +431,23 @@ __device__ __forceinline__ void seg_dot(const uint4& w, const uint32_t* xp, floa
 
 template <>
 __device__ __forceinline__ void seg_dot<4>(const uint4& w, const uint32_t* xp, float* d) {
+  const uint32_t mg = magic_v();
   const uint32_t v[4] = {w.x, w.y, w.z, w.w};
   float a = 0.f, b = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t v0 = v[i], v1 = v0 >> 8;
-    a = dot2((v0 & 0x000F000Fu) | kMagic, xp[4 * i + 0], a);
-    b = dot2((v0 & 0x00F000F0u) | kMagic, xp[4 * i + 1], b);
-    a = dot2((v1 & 0x000F000Fu) | kMagic, xp[4 * i + 2], a);
-    b = dot2((v1 & 0x00F000F0u) | kMagic, xp[4 * i + 3], b);
+    a = dot2((v0 & 0x000F000Fu) | mg, xp[4 * i + 0], a);
+    b = dot2((v0 & 0x00F000F0u) | mg, xp[4 * i + 1], b);
+    a = dot2((v1 & 0x000F000Fu) | mg, xp[4 * i + 2], a);
+    b = dot2((v1 & 0x00F000F0u) | mg, xp[4 * i + 3], b);
   }
   d[0] = a + b;
 }
 
 template <>
 __device__ __forceinline__ void seg_dot<2>(const uint4& w, const uint32_t* xp, float* d) {
+  const uint32_t mg = magic_v();
   const uint32_t v[4] = {w.x, w.y, w.z, w.w};
   float acc[2] = {0.f, 0.f};
 #pragma unroll
@@ -446,10 +455,10 @@ __device__ __forceinline__ void seg_dot<2>(const uint4& w, const uint32_t* xp, f
     const uint32_t v0 = v[i], v1 = v0 >> 10;
     float a = acc[i >> 1];
 #pragma unroll
-    for (int j = 0; j < 5; ++j) a = dot2((v0 & (0x00030003u << (2 * j))) | kMagic, xp[8 * i + j], a);
+    for (int j = 0; j < 5; ++j) a = dot2((v0 & (0x00030003u << (2 * j))) | mg, xp[8 * i + j], a);
 #pragma unroll
     for (int j = 0; j < 3; ++j)
-      a = dot2((v1 & (0x00030003u << (2 * j))) | kMagic, xp[8 * i + 5 + j], a);
+      a = dot2((v1 & (0x00030003u << (2 * j))) | mg, xp[8 * i + 5 + j], a);
     acc[i >> 1] = a;
   }
   d[0] = acc[0];
@@ -649,29 +658,31 @@ __device__ __forceinline__ void seg_dot_words(const uint4& w, const uint32_t* xp
 
 template <>
 __device__ __forceinline__ void seg_dot_words<4>(const uint4& w, const uint32_t* xp, float* d) {
+  const uint32_t mg = magic_v();
   const uint32_t v[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t v0 = v[i], v1 = v0 >> 8;
-    float a = dot2((v0 & 0x000F000Fu) | kMagic, xp[4 * i + 0], 0.f);
-    a = dot2((v0 & 0x00F000F0u) | kMagic, xp[4 * i + 1], a);
-    a = dot2((v1 & 0x000F000Fu) | kMagic, xp[4 * i + 2], a);
-    d[i] = dot2((v1 & 0x00F000F0u) | kMagic, xp[4 * i + 3], a);
+    float a = dot2((v0 & 0x000F000Fu) | mg, xp[4 * i + 0], 0.f);
+    a = dot2((v0 & 0x00F000F0u) | mg, xp[4 * i + 1], a);
+    a = dot2((v1 & 0x000F000Fu) | mg, xp[4 * i + 2], a);
+    d[i] = dot2((v1 & 0x00F000F0u) | mg, xp[4 * i + 3], a);
   }
 }
 
 template <>
 __device__ __forceinline__ void seg_dot_words<2>(const uint4& w, const uint32_t* xp, float* d) {
+  const uint32_t mg = magic_v();
   const uint32_t v[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t v0 = v[i], v1 = v0 >> 10;
     float a = 0.f;
 #pragma unroll
-    for (int j = 0; j < 5; ++j) a = dot2((v0 & (0x00030003u << (2 * j))) | kMagic, xp[8 * i + j], a);
+    for (int j = 0; j < 5; ++j) a = dot2((v0 & (0x00030003u << (2 * j))) | mg, xp[8 * i + j], a);
 #pragma unroll
     for (int j = 0; j < 3; ++j)
-      a = dot2((v1 & (0x00030003u << (2 * j))) | kMagic, xp[8 * i + 5 + j], a);
+      a = dot2((v1 & (0x00030003u << (2 * j))) | mg, xp[8 * i + 5 + j], a);
     d[i] = a;
   }
 }
@@ -721,6 +732,64 @@ __device__ __forceinline__ float tile_dot_w(const Tile<BITS, G, SB, 1>& t, const
     }
     acc = fmaf(sb_value<SB>(t.s[0][g]), u, acc);
     acc = fmaf(sb_value<SB>(t.b[0][g]), as, acc);
+  }
+  return acc;
+}
+
+// A one-segment 4-bit row tile whose codes are already fp16 pairs
+// (1024 + q, magic-number form): a later product with a word-blocked image
+// is dot2s only.  Made while the tile would otherwise sit idle in registers.
+template <int G, int SB>
+struct TileDq4 {
+  static constexpr int GPS = Tile<4, G, SB, 1>::GPS;
+  uint32_t h[16];
+  uint32_t s[GPS], b[GPS];
+  __device__ __forceinline__ void from(const Tile<4, G, SB, 1>& t) {
+    const uint32_t mg = magic_v();
+    const uint32_t v[4] = {t.q[0].x, t.q[0].y, t.q[0].z, t.q[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v0 = v[i], v1 = v0 >> 8;
+      h[4 * i + 0] = (v0 & 0x000F000Fu) | mg;
+      h[4 * i + 1] = (v0 & 0x00F000F0u) | mg;
+      h[4 * i + 2] = (v1 & 0x000F000Fu) | mg;
+      h[4 * i + 3] = (v1 & 0x00F000F0u) | mg;
+    }
+    // Pin the pairs here: the compiler would otherwise recompute them at their
+    // use, after the wait this conversion is meant to fill.
+#pragma unroll
+    for (int k = 0; k < 16; ++k) asm volatile("" : "+v"(h[k]));
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+      s[g] = t.s[0][g];
+      b[g] = t.b[0][g];
+    }
+  }
+};
+
+// tile_dot_w for a tile in fp16-pair form (same sums, same order).
+template <int G, int SB>
+__device__ __forceinline__ float tile_dot_w(const TileDq4<G, SB>& t, const XRegsW<4>& x) {
+  constexpr int GPS = TileDq4<G, SB>::GPS;
+  float d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = dot2(t.h[4 * i + 0], x.p[4 * i + 0], 0.f);
+    a = dot2(t.h[4 * i + 1], x.p[4 * i + 1], a);
+    a = dot2(t.h[4 * i + 2], x.p[4 * i + 2], a);
+    d[i] = dot2(t.h[4 * i + 3], x.p[4 * i + 3], a);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int g = 0; g < GPS; ++g) {
+    float u = 0.f, as = 0.f;
+#pragma unroll
+    for (int i = g * 4 / GPS; i < (g + 1) * 4 / GPS; ++i) {
+      u += fmaf(d[i], x.P[i], -x.C[i]);
+      as += x.A[i];
+    }
+    acc = fmaf(sb_value<SB>(t.s[g]), u, acc);
+    acc = fmaf(sb_value<SB>(t.b[g]), as, acc);
   }
   return acc;
 }

@@ -56,25 +56,32 @@ constexpr int kFusedMaxSlots = 5;   // active experts whose down tiles are held 
 constexpr int kFusedImgPer = 4;     // 8-byte words per thread of one SwiGLU image
 constexpr int kSpinLimit = 1 << 22;
 
-// Counter block layout, in 256-byte lines (64 ints) of the workspace.  Every
-// counter is split into kSubs sub-counters on lines of their own (a device-
+// Counter block layout, in 256-byte lines (64 ints) of the workspace.  A
+// phase's arrivals go to kSubs sub-counters on lines of their own (a device-
 // scope atomic on one address serialises at ~11 ns, and far worse while HBM
-// is saturated), then a top counter.
+// is saturated); the last arrival of a sub-counter resets it and stamps word
+// s of the phase's done line, written in kDoneCopies copies so that each
+// waiting workgroup polls one line shared with few others.  The stamp is the
+// call's epoch: one more than the down-phase stamp the previous call left
+// (which no workgroup of this call can change before every workgroup has read
+// it), so done lines are never reset.
 constexpr int kSubs = 64;
 constexpr int kLine = 64;
-constexpr int kQHeadLine = 0;                         // kSubs sub-queue heads
-constexpr int kStartLine = kQHeadLine + kSubs;        // kSubs started counters
-constexpr int kRouterSubLine = kStartLine + kSubs;    // kSubs subs + top
-constexpr int kItemSubLine = kRouterSubLine + kSubs + 1;
-constexpr int kDownSubLine = kItemSubLine + kSubs + 1;
-constexpr int kExitSubLine = kDownSubLine + kSubs + 1;
+constexpr int kDoneCopies = 8;
+constexpr int kQHeadLine = 0;                          // kSubs sub-queue heads
+constexpr int kStartLine = kQHeadLine + kSubs;         // kSubs started counters
+constexpr int kRouterSubLine = kStartLine + kSubs;     // kSubs each
+constexpr int kItemSubLine = kRouterSubLine + kSubs;
+constexpr int kDownSubLine = kItemSubLine + kSubs;
+constexpr int kExitSubLine = kDownSubLine + kSubs;     // kSubs subs + top
 constexpr int kTimeoutLine = kExitSubLine + kSubs + 1;
-constexpr int kDefHeadLine = kTimeoutLine + 1;      // deferred down parts: next one to take
-constexpr int kDefTailLine = kTimeoutLine + 2;      // deferred down parts: how many
-constexpr int kRouterFlagLine = kTimeoutLine + 4;   // 64 flags
-constexpr int kItemFlagLine = kRouterFlagLine + 64; // 64 flags
-static_assert(kItemFlagLine + 64 <= kFusedCtrLines, "counter block too small");
-constexpr int kNormPer = 16;   // gamma*h values per thread loaded at once by the norm
+constexpr int kDefHeadLine = kTimeoutLine + 1;         // deferred down parts: next one to take
+constexpr int kDefTailLine = kTimeoutLine + 2;         // deferred down parts: how many
+constexpr int kRouterDoneLine = kTimeoutLine + 3;      // kDoneCopies lines each
+constexpr int kItemDoneLine = kRouterDoneLine + kDoneCopies;
+constexpr int kDownDoneLine = kItemDoneLine + kDoneCopies;
+static_assert(kDownDoneLine + kDoneCopies <= kFusedCtrLines, "counter block too small");
+constexpr int kMaxDoneParts = kFusedMaxNormParts;      // down parts one workgroup may finish
 
 // LDS of one workgroup: [x fp32 | x prepared | down-stage activation images].
 inline size_t fused_lds_bytes(int H, int I, int bits) {
@@ -98,21 +105,47 @@ __device__ __forceinline__ bool arrive(int* ctr, int sub_line, int idx, int n) {
   return true;
 }
 
-__device__ __forceinline__ void raise_flags(int* ctr, int flag_line) {
-  for (int j = 0; j < 64; ++j) st_agent(ctr_line(ctr, flag_line + j), 1);
+// Arrival number idx of n at a phase: the last arrival of its sub-counter
+// resets it and stamps the phase's done line (all copies) with ep.
+__device__ __forceinline__ void arrive_done(int* ctr, int sub_line, int done_line, int idx, int n,
+                                            int ep) {
+  const int s = idx % kSubs;
+  const int sub_total = n / kSubs + ((s < n % kSubs) ? 1 : 0);
+  int* sub = ctr_line(ctr, sub_line + s);
+  if (add_agent(sub, 1) != sub_total - 1) return;
+  st_agent(sub, 0);
+  for (int c = 0; c < kDoneCopies; ++c) st_agent(ctr_line(ctr, done_line + c) + s, ep);
 }
 
-// Thread-level bounded wait on this workgroup's flag; a timeout is recorded
-// in the workspace instead of hanging.
-__device__ __forceinline__ void wait_flag(int* ctr, int flag_line) {
-  int* f = ctr_line(ctr, flag_line + (blockIdx.x & 63));
-  int spins = 0;
-  while (ld_agent(f) == 0) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++spins > kSpinLimit) {
+// One whole wave: bounded wait until every sub-counter of a phase with n
+// arrivals has stamped ep (lane s reads word s of this workgroup's copy).  A
+// timeout is recorded in the workspace instead of hanging.
+__device__ __forceinline__ void wait_done(int* ctr, int done_line, int n, int ep) {
+  const int lane = tid_x() & 63, nsub = n < kSubs ? n : kSubs;
+  const int* w = ctr_line(ctr, done_line + (int)(blockIdx.x % kDoneCopies)) + lane;
+  for (int spins = 0;; ++spins) {
+    if (__all(lane >= nsub || ld_agent(w) == ep)) break;
+    if (spins > kSpinLimit) {
       st_agent(ctr_line(ctr, kTimeoutLine), 1);
       break;
     }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+// The same by one thread (word after word).
+__device__ __forceinline__ void wait_done_thread(int* ctr, int done_line, int n, int ep) {
+  const int nsub = n < kSubs ? n : kSubs;
+  const int* w = ctr_line(ctr, done_line + (int)(blockIdx.x % kDoneCopies));
+  for (int s = 0, spins = 0; s < nsub; ++spins) {
+    if (ld_agent(w + s) == ep) {
+      ++s;
+      continue;
+    }
+    if (spins > kSpinLimit) {
+      st_agent(ctr_line(ctr, kTimeoutLine), 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
@@ -225,25 +258,29 @@ __device__ __forceinline__ void topk_select(const FusedArgs& a, const double (&l
       tc.idx[wave * a.k + r] = we;
     }
   }
+  // Candidates past 4k up to the next multiple of 16 lose every comparison
+  // (key 0, largest index), so the ranking needs no per-candidate guard.
+  {
+    const int nc = 4 * a.k;
+    if (wave == 0 && lane >= nc && lane < ((nc + 15) & ~15)) {
+      tc.key[lane] = 0ull;
+      tc.idx[lane] = 0x7FFFFFFF;
+    }
+  }
   lds_barrier();
   if (wave == 0) {
     const int nc = 4 * a.k;
     const bool c = lane < nc;
     const uint64_t ck = c ? tc.key[lane] : 0ull;
-    const int ce = c ? tc.idx[lane] : 0;
+    const int ce = c ? tc.idx[lane] : 0x7FFFFFFF;
     int rank = 0;
     for (int j0 = 0; j0 < nc; j0 += 16) {
-      uint64_t kk[16];
-      int ee[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const int j = min(j0 + t, nc - 1);
-        kk[t] = tc.key[j];
-        ee[t] = tc.idx[j];
+        const uint64_t kj = tc.key[j0 + t];
+        const int ej = tc.idx[j0 + t];
+        rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
       }
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (j0 + t < nc) rank += (kk[t] > ck || (kk[t] == ck && ee[t] < ce)) ? 1 : 0;
     }
     const bool sel = c && rank < a.k;
     const int L0 = __ffsll((unsigned long long)__ballot(c && rank == 0)) - 1;
@@ -287,8 +324,8 @@ __device__ __forceinline__ void down_load(Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSl
 // output).  The batch's word-blocked SwiGLU images (published by the gate/up
 // parts before the item flag) are copied to LDS first (all threads); the first
 // batch also takes the shared-expert gate from its logit.
-template <int BITS, int G, int SB>
-__device__ __forceinline__ void down_dot(const Tile<BITS, G, SB, 1> (&tl)[kFusedMaxSlots][kFusedUD],
+template <int BITS, class TileT>
+__device__ __forceinline__ void down_dot(const TileT (&tl)[kFusedMaxSlots][kFusedUD],
                                          float (&acc)[kFusedUD], const FusedArgs& a,
                                          RouteCache& rc, uint8_t* lds_ap, int s0, int ns,
                                          const RowGeo& geo) {
@@ -331,7 +368,7 @@ __device__ __forceinline__ void down_batches(float (&acc)[kFusedUD], const Fused
     const int ns = min(kFusedMaxSlots, kp1 - s0);
     Tile<BITS, G, SB, 1> tl[kFusedMaxSlots][kFusedUD];
     down_load<BITS, G, SB, 0, kFusedMaxSlots>(tl, a, rc, wrow0, s0, geo);
-    down_dot<BITS, G, SB>(tl, acc, a, rc, lds_ap, s0, ns, geo);
+    down_dot<BITS>(tl, acc, a, rc, lds_ap, s0, ns, geo);
   }
 }
 
@@ -346,23 +383,24 @@ __device__ __forceinline__ void down_vectors(const FusedArgs& a, int wrow0, int 
   }
 }
 
-// h = residual + combined expert output for the part's rows; gamma*h and the
-// part's sum of h^2 are published, and the last part to arrive finishes the
-// RMSNorm.  Called by the whole workgroup.
-__device__ __forceinline__ void down_finish(const FusedArgs& a, int d, const float (&acc)[kFusedUD],
-                                            const float (&rv)[kFusedUD],
-                                            const float (&gv)[kFusedUD], int wrow0, int rpi,
-                                            int lane_row, bool writer, float* s_part,
-                                            int& s_flag) {
+// h = residual + combined expert output for the part's rows (writer lanes),
+// kept as gamma*h in hy; the part's sum of h^2 is published and the part
+// arrives at the down phase.  Called by the whole workgroup.
+__device__ __forceinline__ void down_publish(const FusedArgs& a, int d,
+                                             const float (&acc)[kFusedUD],
+                                             const float (&rv)[kFusedUD],
+                                             const float (&gv)[kFusedUD], float (&hy)[kFusedUD],
+                                             int wrow0, int rpi, int lane_row, bool writer,
+                                             float* s_part, int ep) {
   const int tid = tid_x(), wave = tid >> 6, lane = tid & 63;
   float ss = 0.f;
 #pragma unroll
   for (int u = 0; u < kFusedUD; ++u) {
     const int m = wrow0 + u * rpi + lane_row;
+    const float h = rv[u] + acc[u];
+    hy[u] = gv[u] * h;
     if (writer) {
-      const float h = rv[u] + acc[u];
       a.h_out[m] = h;
-      st_agent(a.gh + m, gv[u] * h);
       if (a.moe_out) a.moe_out[m] = acc[u];
       ss = fmaf(h, h, ss);
     }
@@ -374,28 +412,25 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, int d, const flo
     float tot = 0.f;
     for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
     st_agent(a.partials + d, tot);
+    vm_drain();
+    arrive_done(a.ctr, kDownSubLine, kDownDoneLine, d, a.nD, ep);
   }
-  vm_drain();
-  lds_barrier();
-  if (tid == 0) s_flag = arrive(a.ctr, kDownSubLine, d, a.nD);
-  lds_barrier();
-  if (!s_flag) return;
-  // Last down part: y = (gamma*h) * rms^-1.  The first kNormPer*kThreads values
-  // of gamma*h are loaded together with the partial sums.
-  float hv[kNormPer], pv[kFusedMaxNormParts / kThreads];
+}
+
+// 1/rms of h from the nD partial sums (all published; the same order of
+// additions in every workgroup).  Called by the whole workgroup.
+__device__ __forceinline__ float norm_scale(const FusedArgs& a, float* s_part) {
+  constexpr int J = kFusedMaxNormParts / kThreads;
+  const int tid = tid_x(), wave = tid >> 6, lane = tid & 63;
+  float pv[J];
 #pragma unroll
-  for (int j = 0; j < kNormPer; ++j) {
-    const int m = j * kThreads + tid;
-    hv[j] = ld_agent(a.gh + (m < a.H ? m : a.H - 1));
-  }
-#pragma unroll
-  for (int j = 0; j < kFusedMaxNormParts / kThreads; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int r = j * kThreads + tid;
     pv[j] = ld_agent(a.partials + (r < a.nD ? r : a.nD - 1));
   }
   float part = 0.f;
 #pragma unroll
-  for (int j = 0; j < kFusedMaxNormParts / kThreads; ++j)
+  for (int j = 0; j < J; ++j)
     if (j * kThreads + tid < a.nD) part += pv[j];
   part = sum_lanes(part, kWave);
   lds_barrier();
@@ -403,24 +438,7 @@ __device__ __forceinline__ void down_finish(const FusedArgs& a, int d, const flo
   lds_barrier();
   float tot = 0.f;
   for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
-  const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
-#pragma unroll
-  for (int j = 0; j < kNormPer; ++j) {
-    const int m = j * kThreads + tid;
-    if (m < a.H) a.y_out[m] = hv[j] * inv;
-  }
-  for (int m0 = kNormPer * kThreads; m0 < a.H; m0 += kNormPer * kThreads) {
-#pragma unroll
-    for (int j = 0; j < kNormPer; ++j) {
-      const int m = m0 + j * kThreads + tid;
-      hv[j] = ld_agent(a.gh + (m < a.H ? m : a.H - 1));
-    }
-#pragma unroll
-    for (int j = 0; j < kNormPer; ++j) {
-      const int m = m0 + j * kThreads + tid;
-      if (m < a.H) a.y_out[m] = hv[j] * inv;
-    }
-  }
+  return 1.f / sqrtf(tot / (float)a.H + a.eps);
 }
 
 // The persistent loop's body is large and its address arithmetic depends on
@@ -459,8 +477,9 @@ template <int BITS, int G, int SB, int NSH, int VMAX>
 __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_item;
-  __shared__ int s_flag;
   __shared__ int s_defer;
+  __shared__ int s_ndone;                  // down parts finished before the last one
+  __shared__ int s_done[kMaxDoneParts];
   __shared__ float s_act[kWave];
   __shared__ float s_part[kThreads / kWave];
   __shared__ RouteCache rc;
@@ -478,7 +497,21 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
   bool first = true;                      // thread 0: first item not yet taken
   bool listing = false;                   // thread 0: now taking deferred down parts
   int ndef = 0;                           // thread 0: length of the deferred list
-  if (tid_x() == 0) rc.ready = 0;
+  // The call's epoch (stamp of the done lines), read at entry and first
+  // needed once the first loads are out.
+  const int ep_v = ld_agent(ctr_line(a_in.ctr, kDownDoneLine));
+  int ep = 0;
+  auto get_ep = [&]() {
+    if (ep == 0) ep = __builtin_amdgcn_readfirstlane(ep_v) + 1;
+    return ep;
+  };
+  // gamma*h of the last down part of this workgroup (writer lanes) and its index
+  float hy[kFusedUD];
+  int last_d = -1;
+  if (tid_x() == 0) {
+    rc.ready = 0;
+    s_ndone = 0;
+  }
 
   for (;;) {
     FusedArgs a = a_in;
@@ -513,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
         it = (int)gridDim.x + subq + kSubs * add_agent(ctr_line(ctr, kQHeadLine + subq), 1);
         if (it >= n_main) {
           listing = true;
-          wait_flag(ctr, kItemFlagLine);
+          wait_done_thread(ctr, kItemDoneLine, n_main, get_ep());
           ndef = ld_agent(ctr_line(ctr, kDefTailLine));
         }
       }
@@ -609,16 +642,16 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     //   3. the routing (the shared expert's down tile is requested between
     //      the logits and the selection); the routed gate/up part computed and
     //      published
-    //   4. arrival; the selected experts' down tiles requested; the item flag;
-    //      the down part from the held tiles
+    //   4. arrival; the selected experts' down tiles requested; once every
+    //      item has arrived, the down part from the held tiles
     TileI tl[kFusedMaxSlots][kFusedUD];
     float acc[kFusedUD], rv[kFusedUD], gv[kFusedUD];
     const int wrow0 = (dpart >= 0 ? dpart : 0) * a.d_rows + wave * (kFusedUD * geoI.RPI);
 #pragma unroll
     for (int u = 0; u < kFusedUD; ++u) acc[u] = 0.f;
     if (!deferred) {
-      // x is read only here, before this item's gate/up part, and every h_out
-      // write waits for the item flag, so h_out may alias x.
+      // x is read only here, before this item arrives, and every h_out write
+      // waits until every item has arrived, so h_out may alias x.
       if (routes || !have_x) {
         float4 wv[kQ];
         if (routes) router_load(wv, item);
@@ -631,6 +664,7 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
             reinterpret_cast<float4*>(lds_x)[q * kThreads + tid] = xq[q];
             prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
           }
+          get_ep();
           have_x = true;
           lds_barrier();
         }
@@ -642,10 +676,10 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
             router_load(wv, e);
             lds_barrier();   // s_rp is reused
           }
-          vm_drain();
-          lds_barrier();
-          if (tid == 0 && arrive(ctr, kRouterSubLine, item, a.nRr))
-            raise_flags(ctr, kRouterFlagLine);
+          if (tid == 0) {
+            vm_drain();
+            arrive_done(ctr, kRouterSubLine, kRouterDoneLine, item, a.nRr, get_ep());
+          }
           if (item == a.E % a.nRr) {
             // The shared-expert gate is first needed by the down parts, after
             // the item flag, which this item's arrival (after this store) gates.
@@ -665,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       double lg[VMAX / 4];
       const bool route_now = !rc.ready;   // workgroup-uniform (shared, read after a barrier)
       if (route_now) {
-        if (tid == 0) wait_flag(ctr, kRouterFlagLine);
+        if (wave == 0) wait_done(ctr, kRouterDoneLine, a.nRr, get_ep());
         lds_barrier();
         topk_keys<VMAX / 4>(a, lg);
       }
@@ -674,6 +708,10 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
         topk_select<VMAX / 4>(a, lg, rc, s_tc);
         if (tid == 0) rc.ready = 1;
         lds_barrier();
+        if (blockIdx.x == 0 && tid < a.k) {   // the routing outputs
+          if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
+          if (a.w_out) a.w_out[tid] = rc.coef[1 + tid];
+        }
       }
       {
         // All of this phase's loads on every path (the part clamped for items
@@ -703,7 +741,7 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
             st_agent(a.dlist + j, dpart);
             vm_drain();
           }
-          if (arrive(ctr, kItemSubLine, item, n_main)) raise_flags(ctr, kItemFlagLine);
+          arrive_done(ctr, kItemSubLine, kItemDoneLine, item, n_main, get_ep());
         }
       }
       lds_barrier();
@@ -711,9 +749,22 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       // The selected experts' down tiles load while the other parts finish.
       down_load<BITS, G, SB, 1, kFusedMaxSlots>(tl, a, rc, wrow0, 0, geoI);
       down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
-      if (tid == 0) wait_flag(ctr, kItemFlagLine);
-      lds_barrier();
-      down_dot<BITS, G, SB>(tl, acc, a, rc, lds_ap, 0, min(kFusedMaxSlots, kp1), geoI);
+      if constexpr (BITS == 4) {
+        // 4-bit tiles turn into fp16 pairs as soon as they arrive, before the
+        // wait, so that only the dot2s remain once the images are in.
+        TileDq4<G, SB> tq[kFusedMaxSlots][kFusedUD];
+#pragma unroll
+        for (int sl = 0; sl < kFusedMaxSlots; ++sl)
+#pragma unroll
+          for (int u = 0; u < kFusedUD; ++u) tq[sl][u].from(tl[sl][u]);
+        if (wave == 0) wait_done(ctr, kItemDoneLine, n_main, get_ep());
+        lds_barrier();
+        down_dot<BITS>(tq, acc, a, rc, lds_ap, 0, min(kFusedMaxSlots, kp1), geoI);
+      } else {
+        if (wave == 0) wait_done(ctr, kItemDoneLine, n_main, get_ep());
+        lds_barrier();
+        down_dot<BITS>(tl, acc, a, rc, lds_ap, 0, min(kFusedMaxSlots, kp1), geoI);
+      }
       if (kp1 > kFusedMaxSlots)
         down_batches<BITS, G, SB>(acc, a, rc, lds_ap, wrow0, kFusedMaxSlots, geoI);
     } else {
@@ -721,31 +772,55 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       down_vectors(a, wrow0, geoI.RPI, geoI.lane_row, rv, gv);
       down_batches<BITS, G, SB>(acc, a, rc, lds_ap, wrow0, 0, geoI);
     }
-    down_finish(a, dpart, acc, rv, gv, wrow0, geoI.RPI, geoI.lane_row,
-                geoI.lane_seg == geoI.LPR - 1, s_part, s_flag);
-    if (s_flag && tid < a.k) {   // the last down part also writes the routing outputs
-      if (a.idx_out) a.idx_out[tid] = rc.sel[tid];
-      if (a.w_out) a.w_out[tid] = rc.coef[1 + tid];
+    // A down part before this one keeps gamma*h in gh for the norm at exit.
+    if (last_d >= 0) {
+      const bool writer = geoI.lane_seg == geoI.LPR - 1;
+      const int w0 = last_d * a.d_rows + wave * (kFusedUD * geoI.RPI);
+#pragma unroll
+      for (int u = 0; u < kFusedUD; ++u)
+        if (writer) a.gh[w0 + u * geoI.RPI + geoI.lane_row] = hy[u];
+      if (tid == 0) s_done[s_ndone++] = last_d;
     }
+    down_publish(a, dpart, acc, rv, gv, hy, wrow0, geoI.RPI, geoI.lane_row,
+                 geoI.lane_seg == geoI.LPR - 1, s_part, get_ep());
+    last_d = dpart;
   }
 
-  // Leave; the last workgroup out resets queue heads, flags and the list.
-  if (tid_x() == 0) {
+  // RMSNorm of this workgroup's rows once every down part is in; then leave.
+  // With items past the grid, the last workgroup out resets the queue.
+  {
     FusedArgs a = a_in;
-    int* ctr = a.ctr;
-    vm_drain();
-    if (arrive(ctr, kExitSubLine, blockIdx.x, gridDim.x)) {
-      if (a.nF > (int)gridDim.x) {
+    opaque_args(a);
+    const int tid = tid_x(), wave = tid >> 6;
+    if (last_d >= 0) {   // workgroup-uniform
+      const RowGeo geoI(a.I, BITS);
+      const bool writer = geoI.lane_seg == geoI.LPR - 1;
+      if (wave == 0) wait_done(a.ctr, kDownDoneLine, a.nD, get_ep());
+      lds_barrier();
+      const float inv = norm_scale(a, s_part);
+      const int w0 = last_d * a.d_rows + wave * (kFusedUD * geoI.RPI);
+#pragma unroll
+      for (int u = 0; u < kFusedUD; ++u)
+        if (writer) a.y_out[w0 + u * geoI.RPI + geoI.lane_row] = hy[u] * inv;
+      for (int i = 0; i < s_ndone; ++i) {
+        const int w1 = s_done[i] * a.d_rows + wave * (kFusedUD * geoI.RPI);
+#pragma unroll
+        for (int u = 0; u < kFusedUD; ++u) {
+          const int m = w1 + u * geoI.RPI + geoI.lane_row;
+          if (writer) a.y_out[m] = a.gh[m] * inv;
+        }
+      }
+    }
+    if (tid == 0 && a.nF > (int)gridDim.x) {
+      int* ctr = a.ctr;
+      vm_drain();
+      if (arrive(ctr, kExitSubLine, blockIdx.x, gridDim.x)) {
         for (int s = 0; s < kSubs; ++s) {
           st_agent(ctr_line(ctr, kQHeadLine + s), 0);
           st_agent(ctr_line(ctr, kStartLine + s), 0);
         }
         st_agent(ctr_line(ctr, kDefHeadLine), 0);
         st_agent(ctr_line(ctr, kDefTailLine), 0);
-      }
-      for (int j = 0; j < 64; ++j) {
-        st_agent(ctr_line(ctr, kRouterFlagLine + j), 0);
-        st_agent(ctr_line(ctr, kItemFlagLine + j), 0);
       }
     }
   }
