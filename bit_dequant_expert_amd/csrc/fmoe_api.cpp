@@ -6,6 +6,7 @@
 // synchronises.
 #include <hip/hip_runtime.h>
 #include <limits.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -120,7 +121,8 @@ int64_t slab_layout(int H, int I, const QFmt& f, int64_t off[9]) {
 
 // ------------------------------------------------------------- workspace
 struct LayerWs {
-  size_t ctr, lg64, w, g, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist, total;
+  size_t ctr, lg64, w, g, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist;
+  size_t ximg, xsc, xsum, aimg, asc, asum, total;
   int maxA, nrb_gu, nrb_d;
 };
 
@@ -149,6 +151,15 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   const int nd_fused = (H + fmoe::fused_d_rows(I, bits) - 1) / fmoe::fused_d_rows(I, bits);
   w.part = pos; pos = align256(pos + (size_t)(nd_fused > w.nrb_d ? nd_fused : w.nrb_d) * 4);
   w.dlist = pos; pos = align256(pos + (T == 1 ? (size_t)nd_fused * 4 : 0));
+  // Matrix-core path (batches): activation images of the tokens and of the
+  // path's entries, with their scales and group sums (group 32: the larger).
+  const size_t mt = T > 1 ? (size_t)T : 0, me = T > 1 ? ent : 0;
+  w.ximg = pos; pos = align256(pos + mt * (size_t)H * 2);
+  w.xsc = pos; pos = align256(pos + mt * 4);
+  w.xsum = pos; pos = align256(pos + mt * (size_t)(H / 32) * 4);
+  w.aimg = pos; pos = align256(pos + me * (size_t)I * 2);
+  w.asc = pos; pos = align256(pos + me * 4);
+  w.asum = pos; pos = align256(pos + me * (size_t)(I / 32) * 4);
   w.total = pos;
   return w;
 }
@@ -174,6 +185,13 @@ size_t route_ws(int T, int E) { return fmoe::kWsReserved + align256((size_t)T * 
 
 // FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers (debug and
 // cross-checking only).
+// FMOE_NO_MFMA=1 keeps every expert of a batch on the multi-token GEMV path
+// (cross-checking only).
+bool mfma_disabled() {
+  const char* v = getenv("FMOE_NO_MFMA");
+  return v && v[0] == '1';
+}
+
 bool fused_disabled() {
   const char* v = getenv("FMOE_NO_FUSED");
   return v && v[0] == '1';
@@ -411,6 +429,10 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     if (fe != hipErrorNotSupported) return hip_fail(fe, "fused layer kernel");
   }
 
+  // Experts with many tokens of the batch take the matrix cores (4-bit).
+  const bool use_mfma = T > 1 && fmoe::mfma_supported(H, I, f.bits, f.group) && !mfma_disabled();
+  const int mfma_thr = use_mfma ? fmoe::kMfmaTokens : kMfmaThreshold;
+
   fmoe::RouteArgs ra{};
   ra.Wr = L->router_w; ra.wsg = L->shared_gate_w; ra.x = x;
   ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.rows = E + 1;
@@ -419,7 +441,7 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
   ra.idx_out = idx_out; ra.w_out = w_out;
   ra.w_ws = (float*)(wsb + W.w); ra.g_ws = (float*)(wsb + W.g);
   ra.counter = ctr + 0;
-  ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = kMfmaThreshold;
+  ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = mfma_thr;
   ra.xprep = wsb + W.xprep; ra.bits = f.bits;
   ra.n_prep_wgs = (int)(((int64_t)T * (H / 32) + 31) / 32);
   const size_t rlds = ((size_t)T * k + 3 * (size_t)E) * 4 + 64;
@@ -430,16 +452,36 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
   g.src = src; g.act = act; g.maxA = W.maxA; g.kp1 = kp1; g.H = H; g.I = I;
   g.xprep = wsb + W.xprep; g.abuf = (float*)(wsb + W.abuf); g.aprep = wsb + W.aprep;
   g.ccnt = (int*)(wsb + W.ccnt);
-  g.nrb = W.nrb_gu; g.U = fmoe::iters_per_wave(H, f.bits); g.mfma_thr = kMfmaThreshold;
+  g.nrb = W.nrb_gu; g.U = fmoe::iters_per_wave(H, f.bits); g.mfma_thr = mfma_thr;
   he = fmoe::launch_gateup(f, g, W.maxA * W.nrb_gu, s);
   if (he != hipSuccess) return hip_fail(he, "gate/up kernel");
+
+  if (use_mfma) {
+    fmoe::MfmaArgs m{};
+    m.src = src; m.act = act; m.maxA = W.maxA; m.kp1 = kp1; m.T = T; m.H = H; m.I = I;
+    m.x = x;
+    m.ximg = (uint4*)(wsb + W.ximg); m.xsc = (float*)(wsb + W.xsc); m.xsum = (float*)(wsb + W.xsum);
+    m.aimg = (uint4*)(wsb + W.aimg); m.asc = (float*)(wsb + W.asc); m.asum = (float*)(wsb + W.asum);
+    m.abuf = (float*)(wsb + W.abuf); m.yslot = (float*)(wsb + W.yslot);
+    // At most T*k/16 routed experts reach the threshold, plus the shared one.
+    const int nm_max = std::min(W.maxA, T * k / fmoe::kMfmaTokens + 1);
+    const int ent = T * kp1;
+    if ((he = fmoe::launch_mimg_prep(f, m, 0, T, s)) != hipSuccess)
+      return hip_fail(he, "activation image kernel");
+    if ((he = fmoe::launch_expert_mfma(f, m, 0, nm_max * (I / 16), s)) != hipSuccess)
+      return hip_fail(he, "gate/up matrix-core kernel");
+    if ((he = fmoe::launch_mimg_prep(f, m, 1, ent, s)) != hipSuccess)
+      return hip_fail(he, "activation image kernel");
+    if ((he = fmoe::launch_expert_mfma(f, m, 1, nm_max * (H / 16), s)) != hipSuccess)
+      return hip_fail(he, "down matrix-core kernel");
+  }
 
   fmoe::DArgs d{};
   d.src = src; d.act = act; d.maxA = W.maxA; d.kp1 = kp1; d.k = k; d.H = H; d.I = I;
   d.aprep = wsb + W.aprep; d.w_ws = (const float*)(wsb + W.w); d.g_ws = (const float*)(wsb + W.g);
   d.resid = residual; d.h_out = h_out; d.y_out = y_out; d.moe_out = moe_out;
   d.gamma = L->norm_w; d.eps = L->norm_eps;
-  d.nrb = W.nrb_d; d.U = fmoe::iters_per_wave(I, f.bits); d.mfma_thr = kMfmaThreshold;
+  d.nrb = W.nrb_d; d.U = fmoe::iters_per_wave(I, f.bits); d.mfma_thr = mfma_thr;
   if (T == 1) {
     d.partials = (float*)(wsb + W.part);
     d.ncnt = ctr + 1;

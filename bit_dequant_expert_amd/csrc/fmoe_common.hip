@@ -1,6 +1,6 @@
 // fmoe_common.hip -- launchers of the format-independent kernels and the
 // dispatch of format-templated launches to their translation units.
-#include "fmoe_fused.h"
+#include "fmoe_mfma.h"
 
 namespace fmoe {
 
@@ -74,6 +74,27 @@ hipError_t launch_down_combine(QFmt f, const DArgs& a, hipStream_t st) {
 hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
   VCall c = make_call(VCall::DOWN_SLOTS, f, segs_per_lane(a.I, f.bits), grid, st);
   c.d = &a;
+  return run_variant(c);
+}
+
+bool mfma_supported(int H, int I, int bits, int group) {
+  return bits == 4 && H % 64 == 0 && I % 64 == 0 && H / group <= kMfmaMaxGroups &&
+         I / group <= kMfmaMaxGroups && H / group >= 4 && I / group >= 4;
+}
+
+hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  VCall c = make_call(VCall::MIMG_PREP, f, 1, grid, st);
+  c.mf = &a;
+  c.mode = mode;
+  return run_variant(c);
+}
+
+hipError_t launch_expert_mfma(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  VCall c = make_call(VCall::EXPERT_MFMA, f, 1, grid, st);
+  c.mf = &a;
+  c.mode = mode;
   return run_variant(c);
 }
 

@@ -1,7 +1,7 @@
 // fmoe_inst.hip -- instantiates the format-templated kernels for one
 // (bits, group) pair, given by FMOE_BITS and FMOE_GROUP at compile time.  The
 // build compiles this file once per pair, in parallel.
-#include "fmoe_fused.h"
+#include "fmoe_mfma.h"
 
 #if !defined(FMOE_BITS) || !defined(FMOE_GROUP)
 #error "FMOE_BITS and FMOE_GROUP must be defined"
@@ -60,6 +60,19 @@ hipError_t run_one(const VCall& c) {
       else
         hipLaunchKernelGGL((k_down_slots<B, G, SB, NS, 1>), dim3(c.grid), dim3(kThreads),
                            xprep_bytes(c.d->I), c.st, *c.d);
+      break;
+    case VCall::MIMG_PREP:
+      hipLaunchKernelGGL((k_mimg_prep<G>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf, c.mode);
+      break;
+    case VCall::EXPERT_MFMA:
+      if constexpr (B != 4) {
+        return hipErrorNotSupported;
+      } else {
+        if (c.mode == 0)
+          hipLaunchKernelGGL((k_expert_mfma<G, SB, 0>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf);
+        else
+          hipLaunchKernelGGL((k_expert_mfma<G, SB, 1>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf);
+      }
       break;
     case VCall::FUSED1: {
       if constexpr (NS > 2) {

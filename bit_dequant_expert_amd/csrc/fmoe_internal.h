@@ -102,16 +102,24 @@ struct CombineArgs {
 
 struct FusedArgs;
 
+// Experts with many tokens on the matrix cores (4-bit): activation images
+// (fp16 words, one power-of-two scale per vector, scaled group sums) of the
+// tokens' x and of those experts' SwiGLU outputs, and where results go.
+constexpr int kMfmaTokens = 16;       // an expert with at least this many tokens takes the path
+constexpr int kMfmaMaxGroups = 128;   // K / G the path admits
 struct MfmaArgs {
   ExpertSrc src;
   const int32_t* act;
-  int maxA, kp1, H, I, T;
-  const uint8_t* xprep;    // gate/up input: per token
-  uint8_t* aprep;          // down input: per entry
-  float* abuf;
-  int* ccnt;
-  float* yslot;
-  int nrb;                 // row blocks per expert
+  int maxA, kp1, T, H, I;
+  const float* x;      // [T][H] layer input
+  uint4* ximg;         // [T][H/8]
+  float* xsc;          // [T]
+  float* xsum;         // [T][H/G]
+  uint4* aimg;         // [T*kp1][I/8]
+  float* asc;          // [T*kp1]
+  float* asum;         // [T*kp1][I/G]
+  float* abuf;         // [T*kp1][I] SwiGLU outputs
+  float* yslot;        // [T*kp1][H] down outputs
 };
 
 // Bytes of the prepared image of a K-vector: K/2 fp16 pairs + K/32 float4.
@@ -131,7 +139,7 @@ inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane re
 // One launch of a format-templated kernel; run_variant_<bits>_<group> (one
 // translation unit per pair, compiled in parallel) instantiates the kernels.
 struct VCall {
-  enum Kind { GEMV, GATEUP, DOWN_COMBINE, DOWN_SLOTS, GATEUP_MFMA, DOWN_MFMA, FUSED1 } kind;
+  enum Kind { GEMV, GATEUP, DOWN_COMBINE, DOWN_SLOTS, MIMG_PREP, EXPERT_MFMA, FUSED1 } kind;
   QFmt f;
   int ns;
   int grid;
@@ -143,6 +151,7 @@ struct VCall {
   const struct GUArgs* gu;
   const struct DArgs* d;
   const struct MfmaArgs* mf;
+  int mode;
   const struct FusedArgs* fu;
   size_t lds;
 };
@@ -164,8 +173,11 @@ hipError_t launch_gateup(QFmt f, const GUArgs& a, int grid, hipStream_t st);
 hipError_t launch_down_combine(QFmt f, const DArgs& a, hipStream_t st);
 hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st);
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
-hipError_t launch_gateup_mfma(QFmt f, const MfmaArgs& a, int grid, hipStream_t st);
-hipError_t launch_down_mfma(QFmt f, const MfmaArgs& a, int grid, hipStream_t st);
+// mode 0: gate/up (x images, then SwiGLU into abuf); mode 1: down (images of
+// the path's abuf entries, then yslot).  The prep is one launch per mode.
+bool mfma_supported(int H, int I, int bits, int group);
+hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st);
+hipError_t launch_expert_mfma(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st);
 // One-token layer in one persistent launch; returns hipErrorNotSupported when
 // the row geometry is outside what the fused kernel is instantiated for.
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st);

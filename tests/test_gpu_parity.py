@@ -390,6 +390,33 @@ def test_layer4_correlated_batch(layer4):
     check_layer(layer4, x, x, got, [0, 23])
 
 
+def test_layer4_mfma_matches_gemv_path(layer4, monkeypatch):
+    # Experts with >= 16 tokens run on the matrix cores; FMOE_NO_MFMA=1 keeps
+    # them on the multi-token GEMV.  Both fp16 activation forms must agree.
+    cfg = layer4.cfg
+    note("layer4 T=24 correlated, matrix cores vs GEMV")
+    base = synth.activations(cfg, 1, pool=4)
+    x = (base + 0.1 * synth.activations(cfg, 24, pool=5)).astype(np.float32)
+    a = layer4.forward(x, x)
+    monkeypatch.setenv("FMOE_NO_MFMA", "1")
+    b = layer4.forward(x, x)
+    monkeypatch.delenv("FMOE_NO_MFMA")
+    assert np.array_equal(a["idx"], b["idx"])
+    for name in ("moe", "h", "y"):
+        assert rel_l2(a[name], b[name]) <= 1e-3, name
+
+
+def test_tiny_batch_matrix_cores():
+    # The tiny config (group 32, fp32 scales): 20 tokens give the shared expert
+    # 20 >= 16 tokens, so it runs on the matrix cores with one MFMA step per group.
+    cfg = synth.CONFIGS["tiny"]
+    note("tiny T=20")
+    gl = GpuLayer(cfg, layer=5)
+    x = synth.activations(cfg, 20, pool=9)
+    got = gl.forward(x, x)
+    check_layer(gl, x, x, got, list(range(20)))
+
+
 def test_layer4_deterministic_and_inplace(layer4):
     cfg = layer4.cfg
     note("layer4 determinism / in-place")
