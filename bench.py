@@ -1,10 +1,12 @@
 """Benchmark: one decode step of the quantised MoE layer on one MI355X.
 
-A step is one MoE layer forward for one token (router GEMV -> softmax/top-4 of
-512 -> shared expert -> gathered dequant gate/up -> SwiGLU -> down -> weighted
-combine + sigmoid-gated shared expert + residual -> RMSNorm) at hidden 4096,
-512 routed experts + 1 shared, expert intermediate 1024, 4-bit codes in groups
-of 64 with bf16 scale/bias.  Inputs are seeded synthetic data resident in HBM.
+Default workload (layer4): a step is one MoE layer forward for one token
+(router GEMV -> softmax/top-4 of 512 -> shared expert -> gathered dequant
+gate/up -> SwiGLU -> down -> weighted combine + sigmoid-gated shared expert +
+residual -> RMSNorm) at hidden 4096, 512 routed experts + 1 shared, expert
+intermediate 1024, 4-bit codes in groups of 64 with bf16 scale/bias.  Inputs
+are seeded synthetic data resident in HBM.  layer2 is the same layer with
+2-bit codes.
 
 Cold-cache protocol: the steps rotate over R distinct layer replicas (default
 32, ~116 GB of expert slabs) and a pool of 64 activation vectors, so that the
@@ -12,9 +14,17 @@ per-layer router (8 MB) and shared expert (7 MB) do not stay in the 256 MB
 Infinity Cache.  Steps are captured in HIP graphs of 64 layers and replayed;
 HIP events on the capture/replay stream time exactly --steps steps.
 
-Prints one JSON line.  `value` is the achieved HBM throughput of the whole
-layer (algorithmic bytes / time); us_per_layer and MoE-layer tokens/s are
-reported beside it.  --gpus N with N > 1 is rejected (single-GPU build).
+Other workloads (not the default line):
+  expert   one expert's fused gate/up -> SwiGLU -> down (fmoe_expert_ffn) at
+           [1024 x 4096] / [4096 x 1024], rotating over 128 experts; the gate
+           GEMV and the down GEMV (fmoe_dequant_gemv) are timed alone beside it.
+  stack60  60 distinct 4-bit layers (217.8 GB of slabs) chained on the device
+           (x_{l+1} = y_l, r_{l+1} = h_l) for a batch of 32 independent tokens;
+           a step is the whole 60-layer pass, captured in one HIP graph.
+
+Prints one JSON line.  `value` is the achieved HBM throughput (algorithmic
+bytes / time); per-layer microseconds and tokens/s are reported beside it.
+--gpus N with N > 1 is rejected (single-GPU build).
 """
 import argparse
 import hashlib
@@ -31,14 +41,20 @@ METRIC = ("µs per MoE layer & achieved HBM GB/s (% of peak), 4-bit, hidden 4096
           "512 experts")
 GRAPH_LEN = 64
 XPOOL = 64
+DEFAULT_STEPS = {"layer4": (6400, 640), "layer2": (6400, 640), "expert": (4096, 640),
+                 "stack60": (40, 4)}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=6400)
-    p.add_argument("--warmup", type=int, default=640)
-    p.add_argument("--workload", default="layer4", choices=["layer4", "layer2"])
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 6400 layers; 64 expert passes x 64; 40 stacks)")
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="layer4",
+                   choices=["layer4", "layer2", "expert", "stack60"],
+                   help="layer4/layer2: one batch-1 layer per step; expert: one expert's "
+                        "gate/up/down per step; stack60: 60 chained layers x 32 tokens per step")
     p.add_argument("--replicas", type=int, default=32)
     p.add_argument("--cpu-sample", type=int, default=40, help="tokens timed on the oracle")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -123,10 +139,12 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
-    if args.steps % GRAPH_LEN or args.warmup % GRAPH_LEN:
+    dsteps, dwarm = DEFAULT_STEPS[args.workload]
+    args.steps = dsteps if args.steps is None else args.steps
+    args.warmup = dwarm if args.warmup is None else args.warmup
+    if args.workload != "stack60" and (args.steps % GRAPH_LEN or args.warmup % GRAPH_LEN):
         sys.exit(f"--steps and --warmup must be multiples of {GRAPH_LEN}")
 
-    import numpy as np
     import torch
 
     if args.copy_bytes:
@@ -142,6 +160,62 @@ def main():
         print(json.dumps({"copy_bytes": n, "dispatches": 3}))
         return
 
+    if args.workload == "expert":
+        out = bench_expert(args, torch)
+    elif args.workload == "stack60":
+        out = bench_stack(args, torch)
+    else:
+        out = bench_layer(args, torch)
+    if out is not None:
+        print(json.dumps(out), flush=True)
+
+
+def stream_probe(args, torch):
+    if args.no_stream_probe:
+        return None
+    try:
+        import probes
+        return round(probes.stream_read_gbps(torch), 1)
+    except Exception as exc:  # the probe is context only
+        print(f"[bench] stream probe skipped: {exc}", file=sys.stderr)
+        return None
+
+
+def time_replays(torch, graphs, reps, warmup_reps, stream):
+    """Replay graphs[i % len] warmup_reps times untimed, then reps times between
+    two HIP events on `stream`; then up to 20 single replays for the spread.
+    Returns (total ms, sorted per-replay ms)."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup_reps):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    per = []
+    with torch.cuda.stream(stream):
+        for i in range(min(reps, 20)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graphs[i % len(graphs)].replay()
+            b.record(stream)
+            per.append((a, b))
+    torch.cuda.synchronize()
+    return total_ms, sorted(a.elapsed_time(b) for a, b in per)
+
+
+def spread(vals):
+    return [round(vals[0], 3), round(vals[len(vals) // 2], 3), round(vals[int(len(vals) * 0.9)], 3)]
+
+
+def bench_layer(args, torch):
+    import numpy as np
     import bit_dequant_expert_amd as fm
     import synth
 
@@ -209,32 +283,9 @@ def main():
         graphs.append(g)
     torch.cuda.synchronize()
 
-    with torch.cuda.stream(s):
-        for i in range(args.warmup // GRAPH_LEN):
-            graphs[i % n_graphs].replay()
-    torch.cuda.synchronize()
-
-    reps = args.steps // GRAPH_LEN
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    per_replay = []
-    with torch.cuda.stream(s):
-        torch.cuda.synchronize()
-        ev0.record(s)
-        for i in range(reps):
-            graphs[i % n_graphs].replay()
-        ev1.record(s)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    # per-replay spread (separate pass, same protocol)
-    with torch.cuda.stream(s):
-        for i in range(min(reps, 20)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(s)
-            graphs[i % n_graphs].replay()
-            b.record(s)
-            per_replay.append((a, b))
-    torch.cuda.synchronize()
-    rep_us = sorted(a.elapsed_time(b) * 1000.0 / GRAPH_LEN for a, b in per_replay)
+    total_ms, rep_ms = time_replays(torch, graphs, args.steps // GRAPH_LEN,
+                                    args.warmup // GRAPH_LEN, s)
+    rep_us = [v * 1000.0 / GRAPH_LEN for v in rep_ms]
 
     ms_per_step = total_ms / args.steps
     us = ms_per_step * 1000.0
@@ -242,13 +293,7 @@ def main():
     gbps = nbytes / (us * 1e-6) / 1e9
     khash = source_hash()
     traffic = traffic_from_profiles(khash, args.workload)
-    stream = None
-    if not args.no_stream_probe:
-        try:
-            import probes
-            stream = round(probes.stream_read_gbps(torch), 1)
-        except Exception as exc:  # the probe is context only
-            print(f"[bench] stream probe skipped: {exc}", file=sys.stderr)
+    stream = stream_probe(args, torch)
     out = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -268,8 +313,7 @@ def main():
                    "bits": sp.bits, "group": sp.group, "scale_dtype": "bf16",
                    "batch": 1, "replicas": R, "graph_len": GRAPH_LEN},
         "us_per_layer": round(us, 3),
-        "us_per_layer_min_median_p90": [round(rep_us[0], 3), round(rep_us[len(rep_us) // 2], 3),
-                                        round(rep_us[int(len(rep_us) * 0.9)], 3)],
+        "us_per_layer_min_median_p90": spread(rep_us),
         "moe_layer_tokens_per_s": round(1e6 / us, 1),
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "algorithmic_bytes_per_layer": nbytes,
@@ -291,7 +335,283 @@ def main():
                                          f"(route over 512 + 5 experts), {cus:.0f} us/token, "
                                          f"1 thread of {multiprocessing.cpu_count()} host "
                                          f"logical cores"}
-    print(json.dumps(out), flush=True)
+    return out
+
+
+
+def _fmt_and_layers(torch, fm, synth, cfg, layer_ids, dev):
+    sp = cfg.spec
+    off, stride = sp.layout()
+    fmt = fm.qformat(sp.bits, sp.group, sp.sbytes == 2)
+    layers = []
+    for l in layer_ids:
+        slabs = torch.empty(stride * (cfg.E + 1), dtype=torch.uint8, device=dev)
+        synth.fill_device_slabs(slabs.data_ptr(), sp, cfg.seed, l, 0, cfg.E + 1, stride)
+        Wr = torch.from_numpy(synth.router(cfg, l)).to(dev)
+        wsg = torch.from_numpy(synth.shared_gate(cfg, l)).to(dev)
+        gam = torch.from_numpy(synth.gamma(cfg, l)).to(dev)
+        layers.append(fm.fmoe_layer_desc(cfg.H, cfg.I, cfg.E, cfg.k, fmt, Wr, slabs, stride,
+                                         wsg, gam, cfg.eps))
+    return fmt, layers
+
+
+def bench_expert(args, torch):
+    """One expert at hidden 4096 / inter 1024, 4-bit G64 bf16: the fused FFN
+    (fmoe_expert_ffn) per step, and the gate and down GEMVs (fmoe_dequant_gemv)
+    alone.  Steps rotate over 128 experts (906 MB of slabs, more than the
+    Infinity Cache) and 64 input vectors."""
+    import ctypes as C
+    import bit_dequant_expert_amd as fm
+    import synth
+
+    cfg = synth.CONFIGS["layer4"]
+    sp = cfg.spec
+    H, I = cfg.H, cfg.I
+    dev = torch.device("cuda:0")
+    off, stride = sp.layout()
+    NE = 128
+    slabs = torch.empty(stride * NE, dtype=torch.uint8, device=dev)
+    synth.fill_device_slabs(slabs.data_ptr(), sp, cfg.seed, 0, 0, NE, stride)
+    fmt = fm.qformat(sp.bits, sp.group, sp.sbytes == 2)
+    base = slabs.data_ptr()
+    exps = []
+    for e in range(NE):
+        b = base + e * stride
+        exps.append(fm.fmoe_expert(fm.qmat(b + off[0], b + off[1], b + off[2], I, H),
+                                   fm.qmat(b + off[3], b + off[4], b + off[5], I, H),
+                                   fm.qmat(b + off[6], b + off[7], b + off[8], H, I)))
+    xpool = torch.from_numpy(synth.activations(cfg, XPOOL, pool=1)).to(dev)
+    hpool = torch.from_numpy(synth.normal(cfg.seed, 20_000, 9, (XPOOL, I))).to(dev)
+    y = torch.empty(XPOOL, H, device=dev)
+    yi = torch.empty(XPOOL, I, device=dev)
+    ws_bytes = fm.fmoe_expert_ffn_workspace_size(exps[0], fmt)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    L = fm.lib()
+    xb, hb, yb, yib = xpool.data_ptr(), hpool.data_ptr(), y.data_ptr(), yi.data_ptr()
+
+    def call(kind, i, stream):
+        e, j = exps[i % NE], i % XPOOL
+        if kind == "ffn":
+            rc = L.fmoe_expert_ffn(C.byref(e), C.byref(fmt), xb + j * H * 4, yb + j * H * 4,
+                                   ws.data_ptr(), ws_bytes, stream)
+        elif kind == "gate":
+            rc = L.fmoe_dequant_gemv(C.byref(e.gate), C.byref(fmt), xb + j * H * 4,
+                                     yib + j * I * 4, stream)
+        else:
+            rc = L.fmoe_dequant_gemv(C.byref(e.down), C.byref(fmt), hb + j * I * 4,
+                                     yb + j * H * 4, stream)
+        if rc != 0:
+            raise fm.FmoeError(rc, fm.fmoe_last_error())
+
+    s = torch.cuda.Stream()
+    if args.kernel_steps:
+        with torch.cuda.stream(s):
+            for kind in ("ffn", "gate", "down"):
+                for i in range(args.kernel_steps):
+                    call(kind, i, s.cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
+        return None
+
+    qb = I * H * sp.bits // 8
+    sb = 2 * I * (H // sp.group) * sp.sbytes
+    nbytes = {"ffn": stride + 2 * H * 4, "gate": qb + sb + H * 4 + I * 4,
+              "down": qb + sb + I * 4 + H * 4}
+    res = {}
+    for kind in ("ffn", "gate", "down"):
+        with torch.cuda.stream(s):
+            for i in range(8):
+                call(kind, i, s.cuda_stream)
+        torch.cuda.synchronize()
+        graphs = []
+        for gi in range(NE // GRAPH_LEN):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(GRAPH_LEN):
+                    call(kind, gi * GRAPH_LEN + i, cs)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        total_ms, rep_ms = time_replays(torch, graphs, args.steps // GRAPH_LEN,
+                                        args.warmup // GRAPH_LEN, s)
+        us = total_ms * 1000.0 / args.steps
+        res[kind] = {"us": round(us, 3), "gbps": round(nbytes[kind] / (us * 1e-6) / 1e9, 1),
+                     "bytes": nbytes[kind],
+                     "us_min_median_p90": spread([v * 1000.0 / GRAPH_LEN for v in rep_ms])}
+    us = res["ffn"]["us"]
+    gbps = res["ffn"]["gbps"]
+    out = {
+        "metric": METRIC,
+        "value": gbps,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes x f16 activations, f32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": f"expert_ffn_h{H}_i{I}_4bit_g{sp.group}_bf16_batch1",
+                   "hidden": H, "inter": I, "bits": sp.bits, "group": sp.group,
+                   "scale_dtype": "bf16", "batch": 1, "experts_rotated": NE,
+                   "graph_len": GRAPH_LEN},
+        "us_per_expert": us,
+        "parts": res,
+        "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "fmoe_expert_ffn (all launches of one call)",
+                     "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "kernel_source_hash": source_hash(),
+        "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
+    }
+    if not args.no_cpu_baseline:
+        import multiprocessing
+        import oracle
+        n = max(1, args.cpu_sample // 2)
+        x = synth.activations(cfg, n, pool=1)
+        total = 0.0
+        for t in range(n):
+            slab = synth.slab(sp, cfg.seed, 0, t)
+            t0 = time.perf_counter()
+            oracle.expert_ffn(slab, H, I, sp.bits, sp.group, sp.sbytes, x[t])
+            total += time.perf_counter() - t0
+        cus = total / n * 1e6
+        out["cpu_baseline"] = {"value": round(nbytes["ffn"] / (cus * 1e-6) / 1e9, 4),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} experts' gate/up/down on the host, "
+                                         f"{cus:.0f} us/expert, 1 thread of "
+                                         f"{multiprocessing.cpu_count()} host logical cores"}
+    return out
+
+
+def bench_stack(args, torch):
+    """60 distinct 4-bit layers chained on the device for 32 independent tokens
+    (each layer's y and h are the next layer's x and residual); a step is the
+    whole 60-layer pass, captured in one HIP graph.  The algorithmic bytes of a
+    step count each distinct expert a layer touches once (its slab is read once
+    for all the tokens routed to it), plus the shared expert, the router and the
+    vectors; the distinct counts are read back from the run's own routing."""
+    import ctypes as C
+    import numpy as np
+    import bit_dequant_expert_amd as fm
+    import synth
+
+    cfg = synth.CONFIGS["layer4"]
+    sp = cfg.spec
+    NL, T = 60, 32
+    MODES = ("independent", "chained")
+    dev = torch.device("cuda:0")
+    off, stride = sp.layout()
+    print(f"[bench] generating {NL} layers ({NL * stride * (cfg.E + 1) / 1e9:.1f} GB)",
+          file=sys.stderr, flush=True)
+    fmt, layers = _fmt_and_layers(torch, fm, synth, cfg, range(NL), dev)
+    xs = torch.from_numpy(synth.activations(cfg, NL * T, pool=4)).to(dev).view(NL, T, cfg.H)
+    hbuf = [torch.empty(T, cfg.H, device=dev) for _ in range(2)]
+    ybuf = [torch.empty(T, cfg.H, device=dev) for _ in range(2)]
+    idx = {m: torch.empty(NL, T, cfg.k, dtype=torch.int32, device=dev) for m in MODES}
+    wts = torch.empty(NL, T, cfg.k, device=dev)
+    ws_bytes = fm.fmoe_workspace_size(layers[0], T)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print("[bench] layers ready", file=sys.stderr, flush=True)
+    Lp = [C.addressof(L) for L in layers]
+
+    def step(mode, stream):
+        x = r = xs[0].data_ptr()
+        for l in range(NL):
+            if mode == "independent":
+                x = r = xs[l].data_ptr()
+            h, y = hbuf[l % 2].data_ptr(), ybuf[l % 2].data_ptr()
+            rc = fm.fmoe_moe_layer_forward_raw(Lp[l], T, x, r, h, y, idx[mode][l].data_ptr(),
+                                               wts[l].data_ptr(), None, ws.data_ptr(),
+                                               ws_bytes, stream)
+            if rc != 0:
+                raise fm.FmoeError(rc, fm.fmoe_last_error())
+            x, r = y, h
+
+    s = torch.cuda.Stream()
+    if args.kernel_steps:
+        with torch.cuda.stream(s):
+            for i in range(args.kernel_steps):
+                step("independent", s.cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
+        return None
+
+    res = {}
+    for mode in MODES:
+        with torch.cuda.stream(s):
+            step(mode, s.cuda_stream)                 # eager warm-up before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step(mode, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        total_ms, rep_ms = time_replays(torch, [g], args.steps, args.warmup, s)
+        ms = total_ms / args.steps
+        sel = idx[mode].cpu().numpy()
+        distinct = [int(np.unique(sel[l]).size) for l in range(NL)]
+        counts = [np.bincount(sel[l].ravel(), minlength=cfg.E) for l in range(NL)]
+        nbytes = (sum(distinct) + NL) * stride + NL * cfg.E * cfg.H * 4 \
+            + NL * (4 * T + 2) * cfg.H * 4
+        res[mode] = {"ms_per_step": round(ms, 6), "ms_min_median_p90": spread(rep_ms),
+                     "tokens_per_s": round(T / (ms * 1e-3), 1),
+                     "us_per_layer": round(ms * 1000.0 / NL, 3),
+                     "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "algorithmic_bytes_per_step": nbytes,
+                     "distinct_routed_experts_per_layer": {
+                         "mean": round(float(np.mean(distinct)), 2), "min": min(distinct),
+                         "max": max(distinct)},
+                     "routed_experts_on_matrix_cores_per_layer": round(
+                         float(np.mean([int((c >= 16).sum()) for c in counts])), 3)}
+        del g
+    main_res = res["independent"]
+    ms, gbps = main_res["ms_per_step"], main_res["gbps"]
+    out = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes x f16 activations, f32 accumulation (router f64)",
+        "data": "synthetic",
+        "config": {"workload": f"moe_stack60_h{cfg.H}_e{cfg.E}_i{cfg.I}_top{cfg.k}+1_batch{T}",
+                   "layers": NL, "batch": T, "hidden": cfg.H, "experts": cfg.E,
+                   "inter": cfg.I, "top_k": cfg.k, "bits": sp.bits, "group": sp.group,
+                   "scale_dtype": "bf16", "resident_slab_gb": round(
+                       NL * stride * (cfg.E + 1) / 1e9, 1)},
+        "tokens_per_s": main_res["tokens_per_s"],
+        "us_per_layer": main_res["us_per_layer"],
+        "routing": "independent: every layer takes a fresh N(0,1) batch (x = r), so routing "
+                   "is independent across tokens and layers; chained: y and h of each layer "
+                   "are the next layer's x and residual",
+        "modes": res,
+        "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "all launches of the 60 layers (one graph)",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "kernel_source_hash": source_hash(),
+        "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
+    }
+    if not args.no_cpu_baseline:
+        import multiprocessing
+        n = max(1, args.cpu_sample // 2)
+        cus, _ = cpu_baseline(cfg, n)
+        out["cpu_baseline"] = {"value": round(1e6 / (NL * cus), 4), "unit": "tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n} layer-tokens of a 4-bit layer (route over 512 + "
+                                         f"5 experts), {cus:.0f} us per layer-token, scaled to "
+                                         f"60 layers; 1 thread of "
+                                         f"{multiprocessing.cpu_count()} host logical cores"}
+    return out
 
 
 if __name__ == "__main__":

@@ -121,8 +121,8 @@ int64_t slab_layout(int H, int I, const QFmt& f, int64_t off[9]) {
 
 // ------------------------------------------------------------- workspace
 struct LayerWs {
-  size_t ctr, lg64, w, g, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist;
-  size_t ximg, xsc, xsum, aimg, asc, asum, total;
+  size_t ctr, lg64, sel, w, g, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist;
+  size_t ximg, xsc, xsum, total;
   int maxA, nrb_gu, nrb_d;
 };
 
@@ -138,7 +138,10 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   const size_t ent = (size_t)T * kp1;
   size_t pos = 0;
   w.ctr = pos; pos += fmoe::kWsReserved;   // counters (the one-launch path's block)
-  w.lg64 = pos; pos = align256(pos + (size_t)T * (E + 1) * 8);
+  // Router logits: [T, E+1] for the one-launch path, partial sums per slice
+  // [ksplit, T, E+1] for the multi-launch path (ksplit >= 1).
+  w.lg64 = pos; pos = align256(pos + (size_t)fmoe::route_ksplit(T, E + 1) * T * (E + 1) * 8);
+  w.sel = pos; pos = align256(pos + (size_t)T * k * 4);
   w.w = pos; pos = align256(pos + (size_t)T * k * 4);
   w.g = pos; pos = align256(pos + (size_t)T * 4);
   w.act = pos; pos = align256(pos + act_ints(w.maxA, T, kp1) * 4);
@@ -151,15 +154,12 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   const int nd_fused = (H + fmoe::fused_d_rows(I, bits) - 1) / fmoe::fused_d_rows(I, bits);
   w.part = pos; pos = align256(pos + (size_t)(nd_fused > w.nrb_d ? nd_fused : w.nrb_d) * 4);
   w.dlist = pos; pos = align256(pos + (T == 1 ? (size_t)nd_fused * 4 : 0));
-  // Matrix-core path (batches): activation images of the tokens and of the
-  // path's entries, with their scales and group sums (group 32: the larger).
-  const size_t mt = T > 1 ? (size_t)T : 0, me = T > 1 ? ent : 0;
+  // Matrix-core path (batches): activation images of the tokens, with their
+  // scales and group sums (group 32: the larger).
+  const size_t mt = T > 1 ? (size_t)T : 0;
   w.ximg = pos; pos = align256(pos + mt * (size_t)H * 2);
   w.xsc = pos; pos = align256(pos + mt * 4);
   w.xsum = pos; pos = align256(pos + mt * (size_t)(H / 32) * 4);
-  w.aimg = pos; pos = align256(pos + me * (size_t)I * 2);
-  w.asc = pos; pos = align256(pos + me * 4);
-  w.asum = pos; pos = align256(pos + me * (size_t)(I / 32) * 4);
   w.total = pos;
   return w;
 }
@@ -181,15 +181,25 @@ FfnWs ffn_ws(int H, int I) {
   return w;
 }
 
-size_t route_ws(int T, int E) { return fmoe::kWsReserved + align256((size_t)T * E * 8); }
+size_t route_ws(int T, int E) {
+  return fmoe::kWsReserved + align256((size_t)fmoe::route_ksplit(T, E) * T * E * 8);
+}
 
 // FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers (debug and
 // cross-checking only).
 // FMOE_NO_MFMA=1 keeps every expert of a batch on the multi-token GEMV path
-// (cross-checking only).
+// (cross-checking only).  FMOE_MFMA_MIN_TOKENS=n sends only experts with at
+// least n tokens of the batch to the matrix cores and the rest to the GEMV
+// kernels (cross-checking only; the default sends every expert).
 bool mfma_disabled() {
   const char* v = getenv("FMOE_NO_MFMA");
   return v && v[0] == '1';
+}
+
+int mfma_min_tokens() {
+  const char* v = getenv("FMOE_MFMA_MIN_TOKENS");
+  const int n = v ? atoi(v) : 0;
+  return n >= 1 ? n : fmoe::kMfmaTokens;
 }
 
 bool fused_disabled() {
@@ -254,8 +264,9 @@ fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, in
   a.wsg = nullptr;
   a.x = x;
   a.T = T; a.H = H; a.E = E; a.k = k; a.rows = E;
-  a.n_router_wgs = (E + 3) / 4;
-  a.lg64 = (double*)(wsb + fmoe::kWsReserved);
+  a.ksplit = fmoe::route_ksplit(T, E);
+  a.part = (double*)(wsb + fmoe::kWsReserved);
+  a.sel_ws = nullptr;
   a.logits_out = logits_out;
   a.idx_out = idx;
   a.w_out = w;
@@ -263,8 +274,7 @@ fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, in
   a.kp1 = k + 1;
   a.mfma_thr = kMfmaThreshold;
   a.n_prep_wgs = 0;
-  const size_t lds = (size_t)T * k * 4 + 64;
-  hipError_t e = fmoe::launch_route(a, lds, (hipStream_t)stream);
+  hipError_t e = fmoe::launch_route(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "route kernel");
   return FMOE_OK;
 }
@@ -429,51 +439,48 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     if (fe != hipErrorNotSupported) return hip_fail(fe, "fused layer kernel");
   }
 
-  // Experts with many tokens of the batch take the matrix cores (4-bit).
+  // Experts of a batch take the matrix cores (4-bit); experts with fewer than
+  // mfma_thr tokens (none at the default threshold) take the GEMV kernels.
   const bool use_mfma = T > 1 && fmoe::mfma_supported(H, I, f.bits, f.group) && !mfma_disabled();
-  const int mfma_thr = use_mfma ? fmoe::kMfmaTokens : kMfmaThreshold;
+  const int mfma_thr = use_mfma ? mfma_min_tokens() : kMfmaThreshold;
+  const bool use_gemv = !use_mfma || mfma_thr > 1;
 
   fmoe::RouteArgs ra{};
   ra.Wr = L->router_w; ra.wsg = L->shared_gate_w; ra.x = x;
   ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.rows = E + 1;
-  ra.n_router_wgs = (E + 1 + 3) / 4;
-  ra.lg64 = (double*)(wsb + W.lg64);
+  ra.ksplit = fmoe::route_ksplit(T, E + 1);
+  ra.part = (double*)(wsb + W.lg64);
+  ra.sel_ws = (int32_t*)(wsb + W.sel);
   ra.idx_out = idx_out; ra.w_out = w_out;
   ra.w_ws = (float*)(wsb + W.w); ra.g_ws = (float*)(wsb + W.g);
   ra.counter = ctr + 0;
   ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = mfma_thr;
-  ra.xprep = wsb + W.xprep; ra.bits = f.bits;
-  ra.n_prep_wgs = (int)(((int64_t)T * (H / 32) + 31) / 32);
-  const size_t rlds = ((size_t)T * k + 3 * (size_t)E) * 4 + 64;
-  hipError_t he = fmoe::launch_route(ra, rlds, s);
+  ra.xprep = use_gemv ? wsb + W.xprep : nullptr; ra.bits = f.bits;
+  ra.n_prep_wgs = use_gemv ? (int)(((int64_t)T * (H / 32) + 31) / 32) : 0;
+  hipError_t he = fmoe::launch_route(ra, s);
   if (he != hipSuccess) return hip_fail(he, "route kernel");
 
-  fmoe::GUArgs g{};
-  g.src = src; g.act = act; g.maxA = W.maxA; g.kp1 = kp1; g.H = H; g.I = I;
-  g.xprep = wsb + W.xprep; g.abuf = (float*)(wsb + W.abuf); g.aprep = wsb + W.aprep;
-  g.ccnt = (int*)(wsb + W.ccnt);
-  g.nrb = W.nrb_gu; g.U = fmoe::iters_per_wave(H, f.bits); g.mfma_thr = mfma_thr;
-  he = fmoe::launch_gateup(f, g, W.maxA * W.nrb_gu, s);
-  if (he != hipSuccess) return hip_fail(he, "gate/up kernel");
+  if (use_gemv) {
+    fmoe::GUArgs g{};
+    g.src = src; g.act = act; g.maxA = W.maxA; g.kp1 = kp1; g.H = H; g.I = I;
+    g.xprep = wsb + W.xprep; g.abuf = (float*)(wsb + W.abuf); g.aprep = wsb + W.aprep;
+    g.ccnt = (int*)(wsb + W.ccnt);
+    g.nrb = W.nrb_gu; g.U = fmoe::iters_per_wave(H, f.bits); g.mfma_thr = mfma_thr;
+    he = fmoe::launch_gateup(f, g, W.maxA * W.nrb_gu, s);
+    if (he != hipSuccess) return hip_fail(he, "gate/up kernel");
+  }
 
+  fmoe::MfmaArgs m{};
   if (use_mfma) {
-    fmoe::MfmaArgs m{};
     m.src = src; m.act = act; m.maxA = W.maxA; m.kp1 = kp1; m.T = T; m.H = H; m.I = I;
+    m.mfma_thr = mfma_thr;
     m.x = x;
     m.ximg = (uint4*)(wsb + W.ximg); m.xsc = (float*)(wsb + W.xsc); m.xsum = (float*)(wsb + W.xsum);
-    m.aimg = (uint4*)(wsb + W.aimg); m.asc = (float*)(wsb + W.asc); m.asum = (float*)(wsb + W.asum);
     m.abuf = (float*)(wsb + W.abuf); m.yslot = (float*)(wsb + W.yslot);
-    // At most T*k/16 routed experts reach the threshold, plus the shared one.
-    const int nm_max = std::min(W.maxA, T * k / fmoe::kMfmaTokens + 1);
-    const int ent = T * kp1;
-    if ((he = fmoe::launch_mimg_prep(f, m, 0, T, s)) != hipSuccess)
+    if ((he = fmoe::launch_mimg_prep(f, m, s)) != hipSuccess)
       return hip_fail(he, "activation image kernel");
-    if ((he = fmoe::launch_expert_mfma(f, m, 0, nm_max * (I / 16), s)) != hipSuccess)
+    if ((he = fmoe::launch_moe_mfma(f, m, 0, s)) != hipSuccess)
       return hip_fail(he, "gate/up matrix-core kernel");
-    if ((he = fmoe::launch_mimg_prep(f, m, 1, ent, s)) != hipSuccess)
-      return hip_fail(he, "activation image kernel");
-    if ((he = fmoe::launch_expert_mfma(f, m, 1, nm_max * (H / 16), s)) != hipSuccess)
-      return hip_fail(he, "down matrix-core kernel");
   }
 
   fmoe::DArgs d{};
@@ -494,8 +501,14 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     if (he != hipSuccess) return hip_fail(he, "down/combine kernel");
   } else {
     d.yslot = (float*)(wsb + W.yslot);
-    he = fmoe::launch_down_slots(f, d, W.maxA * W.nrb_d, s);
-    if (he != hipSuccess) return hip_fail(he, "down kernel");
+    if (use_gemv) {
+      he = fmoe::launch_down_slots(f, d, W.maxA * W.nrb_d, s);
+      if (he != hipSuccess) return hip_fail(he, "down kernel");
+    }
+    if (use_mfma) {
+      if ((he = fmoe::launch_moe_mfma(f, m, 1, s)) != hipSuccess)
+        return hip_fail(he, "down matrix-core kernel");
+    }
     fmoe::CombineArgs c{};
     c.T = T; c.H = H; c.k = k; c.kp1 = kp1;
     c.yslot = d.yslot; c.w_ws = d.w_ws; c.g_ws = d.g_ws; c.resid = residual;

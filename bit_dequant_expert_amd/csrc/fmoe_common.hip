@@ -1,24 +1,74 @@
 // fmoe_common.hip -- launchers of the format-independent kernels and the
 // dispatch of format-templated launches to their translation units.
 #include "fmoe_mfma.h"
+#include "fmoe_route.h"
 
 namespace fmoe {
 
 // ================================================= combine + norm (tokens)
+// One workgroup per token.  [WAS] section 3, "MoE-Kombination + Residual +
+// Sigmoid-Gating", and the two-phase RMSNorm: h = r + sum_i w_i y_i + g y_s
+// (routed slots in selection order, then the shared one), y = gamma h / rms(h).
+// Each thread keeps its float4s of h in registers between the two phases; the
+// slot loads are issued four slots at a time ahead of their use.
 __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
+  constexpr int MAXJ = 8;   // H <= 8 * 4 * kThreads
   __shared__ float s_part[kThreads / kWave];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nf = a.H / 4;
   const int64_t row = (int64_t)t * a.H;
+  const float4* ys = reinterpret_cast<const float4*>(a.yslot + (int64_t)t * a.kp1 * a.H);
+  float4 acc[MAXJ], rv[MAXJ], gm[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int f = j * kThreads + tid;
+    const int fc = f < nf ? f : 0;
+    acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rv[j] = reinterpret_cast<const float4*>(a.resid + row)[fc];
+    gm[j] = reinterpret_cast<const float4*>(a.gamma)[fc];
+  }
+  for (int i0 = 0; i0 < a.kp1; i0 += 4) {
+    float4 v[4][MAXJ];
+    float c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q < a.kp1 ? i0 + q : a.k;
+      c[q] = i < a.k ? a.w_ws[(int64_t)t * a.k + i] : a.g_ws[t];
+      if (i0 + q >= a.kp1) c[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) {
+        const int f = j * kThreads + tid;
+        v[q][j] = ys[(int64_t)i * nf + (f < nf ? f : 0)];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (i0 + q < a.kp1) {
+#pragma unroll
+        for (int j = 0; j < MAXJ; ++j) {
+          acc[j].x = fmaf(c[q], v[q][j].x, acc[j].x);
+          acc[j].y = fmaf(c[q], v[q][j].y, acc[j].y);
+          acc[j].z = fmaf(c[q], v[q][j].z, acc[j].z);
+          acc[j].w = fmaf(c[q], v[q][j].w, acc[j].w);
+        }
+      }
+    }
+  }
   float ss = 0.f;
-  for (int m = tid; m < a.H; m += kThreads) {
-    float moe = 0.f;
-    for (int i = 0; i < a.k; ++i)
-      moe = fmaf(a.w_ws[(int64_t)t * a.k + i], a.yslot[((int64_t)t * a.kp1 + i) * a.H + m], moe);
-    moe = fmaf(a.g_ws[t], a.yslot[((int64_t)t * a.kp1 + a.k) * a.H + m], moe);
-    const float h = a.resid[row + m] + moe;
-    a.h_out[row + m] = h;
-    if (a.moe_out) a.moe_out[row + m] = moe;
-    ss = fmaf(h, h, ss);
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int f = j * kThreads + tid;
+    if (f < nf) {
+      const float4 h = make_float4(rv[j].x + acc[j].x, rv[j].y + acc[j].y, rv[j].z + acc[j].z,
+                                   rv[j].w + acc[j].w);
+      rv[j] = h;
+      reinterpret_cast<float4*>(a.h_out + row)[f] = h;
+      if (a.moe_out) reinterpret_cast<float4*>(a.moe_out + row)[f] = acc[j];
+      ss = fmaf(h.x, h.x, ss);
+      ss = fmaf(h.y, h.y, ss);
+      ss = fmaf(h.z, h.z, ss);
+      ss = fmaf(h.w, h.w, ss);
+    }
   }
   ss = sum_lanes(ss, kWave);
   if (lane == kWave - 1) s_part[wave] = ss;
@@ -26,7 +76,14 @@ __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
   float tot = 0.f;
   for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
   const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
-  for (int m = tid; m < a.H; m += kThreads) a.y_out[row + m] = a.gamma[m] * a.h_out[row + m] * inv;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int f = j * kThreads + tid;
+    if (f < nf)
+      reinterpret_cast<float4*>(a.y_out + row)[f] =
+          make_float4(gm[j].x * rv[j].x * inv, gm[j].y * rv[j].y * inv, gm[j].z * rv[j].z * inv,
+                      gm[j].w * rv[j].w * inv);
+  }
 }
 
 
@@ -78,19 +135,22 @@ hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
 }
 
 bool mfma_supported(int H, int I, int bits, int group) {
-  return bits == 4 && H % 64 == 0 && I % 64 == 0 && H / group <= kMfmaMaxGroups &&
-         I / group <= kMfmaMaxGroups && H / group >= 4 && I / group >= 4;
+  return bits == 4 && H % 128 == 0 && I % 128 == 0 && I <= kMfmaMaxI &&
+         H / group <= kMfmaMaxGroups && I / group <= kMfmaMaxGroups && H / group >= 4 &&
+         I / group >= 4;
 }
 
-hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st) {
+hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, hipStream_t st) {
+  const int grid = (a.T + kThreads / kWave - 1) / (kThreads / kWave);
   if (grid <= 0) return hipSuccess;
   VCall c = make_call(VCall::MIMG_PREP, f, 1, grid, st);
   c.mf = &a;
-  c.mode = mode;
   return run_variant(c);
 }
 
-hipError_t launch_expert_mfma(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st) {
+hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st) {
+  const int N = mode == 0 ? a.I : a.H;
+  const int grid = a.maxA * (N / 64);
   if (grid <= 0) return hipSuccess;
   VCall c = make_call(VCall::EXPERT_MFMA, f, 1, grid, st);
   c.mf = &a;
@@ -139,18 +199,22 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
   return run_variant(c);
 }
 
-hipError_t launch_route(const RouteArgs& a, size_t lds_bytes, hipStream_t st) {
-  const int nj_need = (a.H + 255) / 256, v_need = (a.E + 63) / 64;
-  const int grid = a.n_router_wgs + a.n_prep_wgs;
-#define FMOE_RT(NJ, V)                                                                  \
-  if (nj_need <= NJ && v_need <= V) {                                                  \
-    hipLaunchKernelGGL((k_route<NJ, V>), dim3(grid), dim3(kThreads), lds_bytes, st, a); \
-    return hipGetLastError();                                                          \
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+  const int nlog = ((a.rows + 15) / 16) * ((a.T + 31) / 32) * a.ksplit;
+  hipLaunchKernelGGL(k_route_logits, dim3(nlog + a.n_prep_wgs), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lg = (size_t)a.rows * 8;
+  const size_t gr = a.act ? ((size_t)a.T * a.k + 3 * (size_t)a.E) * 4 : 0;
+  const size_t lds = lg > gr ? lg : gr;
+  const int v_need = (a.E + 63) / 64;
+#define FMOE_RS(V)                                                                   \
+  if (v_need <= V) {                                                                 \
+    hipLaunchKernelGGL((k_route_select<V>), dim3(a.T), dim3(kThreads), lds, st, a);  \
+    return hipGetLastError();                                                        \
   }
-#define FMOE_RV(NJ) FMOE_RT(NJ, 1) FMOE_RT(NJ, 2) FMOE_RT(NJ, 4) FMOE_RT(NJ, 8) FMOE_RT(NJ, 16) FMOE_RT(NJ, 32)
-  FMOE_RV(1) FMOE_RV(2) FMOE_RV(4) FMOE_RV(8) FMOE_RV(16) FMOE_RV(32)
-#undef FMOE_RV
-#undef FMOE_RT
+  FMOE_RS(1) FMOE_RS(2) FMOE_RS(4) FMOE_RS(8) FMOE_RS(16) FMOE_RS(32)
+#undef FMOE_RS
   return hipErrorInvalidValue;
 }
 

@@ -62,16 +62,22 @@ hipError_t run_one(const VCall& c) {
                            xprep_bytes(c.d->I), c.st, *c.d);
       break;
     case VCall::MIMG_PREP:
-      hipLaunchKernelGGL((k_mimg_prep<G>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf, c.mode);
+      hipLaunchKernelGGL((k_mimg_prep<G>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf);
       break;
     case VCall::EXPERT_MFMA:
       if constexpr (B != 4) {
         return hipErrorNotSupported;
       } else {
+        // More than 64 KB of dynamic LDS must be allowed per kernel first.
+        const size_t lds = moe_mfma_lds(c.mode, c.mf->H, c.mf->I, G, SB);
+        const void* fn = c.mode == 0 ? reinterpret_cast<const void*>(&k_moe_mfma<G, SB, 0>)
+                                     : reinterpret_cast<const void*>(&k_moe_mfma<G, SB, 1>);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
         if (c.mode == 0)
-          hipLaunchKernelGGL((k_expert_mfma<G, SB, 0>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf);
+          hipLaunchKernelGGL((k_moe_mfma<G, SB, 0>), dim3(c.grid), dim3(kThreads), lds, c.st, *c.mf);
         else
-          hipLaunchKernelGGL((k_expert_mfma<G, SB, 1>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf);
+          hipLaunchKernelGGL((k_moe_mfma<G, SB, 1>), dim3(c.grid), dim3(kThreads), lds, c.st, *c.mf);
       }
       break;
     case VCall::FUSED1: {

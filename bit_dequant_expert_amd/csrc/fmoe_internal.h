@@ -41,8 +41,9 @@ struct RouteArgs {
   const float* wsg;        // shared-gate row (router row E) or null
   const float* x;          // [T, H]
   int T, H, E, k, rows;    // rows = E (+1 with wsg)
-  int n_router_wgs;
-  double* lg64;            // [T, rows]
+  int ksplit;              // slices of the hidden dim (route_ksplit)
+  double* part;            // [ksplit, T, rows] partial logits
+  int32_t* sel_ws;         // [T, k] selections handed to the grouping, or null
   float* logits_out;       // [T, E] or null
   int32_t* idx_out;        // [T, k] or null
   float* w_out;            // [T, k] or null
@@ -55,6 +56,14 @@ struct RouteArgs {
   int bits;
   int n_prep_wgs;
 };
+
+// Slices of the hidden dim for the router's matrix product: enough
+// workgroups (16 rows x 32 tokens x slice) to cover the chip, at most 8.
+inline int route_ksplit(int T, int rows) {
+  const int tiles = ((rows + 15) / 16) * ((T + 31) / 32);
+  int ks = (256 + tiles - 1) / tiles;
+  return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+}
 
 struct GUArgs {
   ExpertSrc src;
@@ -105,19 +114,18 @@ struct FusedArgs;
 // Experts with many tokens on the matrix cores (4-bit): activation images
 // (fp16 words, one power-of-two scale per vector, scaled group sums) of the
 // tokens' x and of those experts' SwiGLU outputs, and where results go.
-constexpr int kMfmaTokens = 16;       // an expert with at least this many tokens takes the path
+constexpr int kMfmaTokens = 1;        // an expert with at least this many tokens takes the path
 constexpr int kMfmaMaxGroups = 128;   // K / G the path admits
+constexpr int kMfmaMaxI = 2048;       // down input images of a 16-token pass held in LDS
 struct MfmaArgs {
   ExpertSrc src;
   const int32_t* act;
   int maxA, kp1, T, H, I;
+  int mfma_thr;        // experts with fewer tokens are left to the GEMV kernels
   const float* x;      // [T][H] layer input
   uint4* ximg;         // [T][H/8]
   float* xsc;          // [T]
   float* xsum;         // [T][H/G]
-  uint4* aimg;         // [T*kp1][I/8]
-  float* asc;          // [T*kp1]
-  float* asum;         // [T*kp1][I/G]
   float* abuf;         // [T*kp1][I] SwiGLU outputs
   float* yslot;        // [T*kp1][H] down outputs
 };
@@ -166,7 +174,7 @@ int fused_occupancy_2_64(int sb, int ns, int E, size_t lds);
 
 hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t* b, int N,
                        int K, const float* x, float* y, hipStream_t st);
-hipError_t launch_route(const RouteArgs& a, size_t lds_bytes, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_ffn_prep(int bits, const float* x, int H, uint8_t* xprep, int32_t* act,
                            int maxA, hipStream_t st);
 hipError_t launch_gateup(QFmt f, const GUArgs& a, int grid, hipStream_t st);
@@ -176,8 +184,8 @@ hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
 // mode 0: gate/up (x images, then SwiGLU into abuf); mode 1: down (images of
 // the path's abuf entries, then yslot).  The prep is one launch per mode.
 bool mfma_supported(int H, int I, int bits, int group);
-hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st);
-hipError_t launch_expert_mfma(QFmt f, const MfmaArgs& a, int mode, int grid, hipStream_t st);
+hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, hipStream_t st);
+hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st);
 // One-token layer in one persistent launch; returns hipErrorNotSupported when
 // the row geometry is outside what the fused kernel is instantiated for.
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st);

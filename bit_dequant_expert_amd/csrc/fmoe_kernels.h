@@ -7,9 +7,9 @@
 //          Notebook ausfuehren" (news.hada.io)
 //
 // Kernels, in the order a layer runs them:
-//   k_route        router GEMV (fp64 accumulation) + shared gate + activation
-//                  prep; the last workgroup picks top-k, softmax weights and
-//                  builds the active-expert list (indices stay on the device)
+//   k_route_logits, k_route_select (fmoe_route.h)   router product (fp64),
+//                  top-k, softmax weights, shared gate, activation prep and
+//                  the active-expert list (indices stay on the device)
 //   k_gateup       gathered gate/up dequant-GEMV over the active slabs, SwiGLU
 //                  epilogue; the last writer of each 32-row block prepares it
 //                  as the down projection's input
@@ -103,197 +103,6 @@ __device__ __forceinline__ int block_exscan(int v, int* scratch, int& total) {
   }
   __syncthreads();
   return before + inc - v;
-}
-
-// [WAS] "Verstaendnis von Mixture-of-Experts (MoE) ...": the router picks k
-// routed experts (plus the shared one) per token.  Logits accumulate in fp64
-// (exact fp32 products) so the selection does not depend on summation order;
-// ties go to the lower index; weights are the softmax over the selected
-// logits (= full softmax renormalised over the selection).
-template <int NJ, int VMAX>
-__global__ __launch_bounds__(kThreads) void k_route(RouteArgs a) {
-  extern __shared__ __align__(16) int lds_i[];
-  __shared__ int s_last;
-  __shared__ int s_scan[8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  if ((int)blockIdx.x >= a.n_router_wgs) {
-    // ---- activation prep for the gate/up products (independent of routing)
-    if (!a.xprep) return;
-    const int pb = blockIdx.x - a.n_router_wgs;
-    const int per_tok = a.H / 32;
-    const int gb = pb * (kThreads / 8) + (tid >> 3);
-    const bool ok = gb < a.T * per_tok;
-    const int t = ok ? gb / per_tok : 0, blk = ok ? gb % per_tok : -1;
-    const float* src = a.x + (int64_t)t * a.H;
-    uint8_t* dst = a.xprep + (int64_t)t * xprep_bytes(a.H);
-    if (a.bits == 4) prep_blocks<4, false>(src, dst, a.H, blk);
-    else prep_blocks<2, false>(src, dst, a.H, blk);
-    return;
-  }
-
-  // ---- router rows (row E is the shared-expert gate vector)
-  {
-    const int e = blockIdx.x * 4 + wave;
-    if (e < a.rows) {
-      const float* wrow = (e < a.E) ? a.Wr + (int64_t)e * a.H : a.wsg;
-      const int nf4 = a.H / 4;
-      float4 wv[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int f = j * kWave + lane;
-        wv[j] = f < nf4 ? ld_nt(reinterpret_cast<const float4*>(wrow) + f) : make_float4(0, 0, 0, 0);
-      }
-      for (int t = 0; t < a.T; ++t) {
-        const float4* xt = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
-        double acc = 0.0;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int f = j * kWave + lane;
-          if (f < nf4) {
-            const float4 xv = xt[f];
-            acc = fma((double)wv[j].x, (double)xv.x, acc);
-            acc = fma((double)wv[j].y, (double)xv.y, acc);
-            acc = fma((double)wv[j].z, (double)xv.z, acc);
-            acc = fma((double)wv[j].w, (double)xv.w, acc);
-          }
-        }
-        acc = sum_lanes_f64(acc);
-        if (lane == kWave - 1) {
-          st_agent(a.lg64 + (int64_t)t * a.rows + e, acc);
-          if (a.logits_out && e < a.E) a.logits_out[(int64_t)t * a.E + e] = (float)acc;
-        }
-      }
-    }
-  }
-  vm_drain();
-  __syncthreads();
-  if (tid == 0) s_last = (add_agent(a.counter, 1) == a.n_router_wgs - 1);
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---- last workgroup: top-k, weights, shared gate, active list
-  int* s_sel = lds_i;  // [T*k]
-  for (int t = wave; t < a.T; t += kThreads / kWave) {
-    const double* lg = a.lg64 + (int64_t)t * a.rows;
-    uint64_t key[VMAX];
-    double lv[VMAX];
-#pragma unroll
-    for (int v = 0; v < VMAX; ++v) {   // all loads first (clamped addresses)
-      const int e = lane * VMAX + v;
-      lv[v] = ld_agent(lg + (e < a.E ? e : 0));
-    }
-#pragma unroll
-    for (int v = 0; v < VMAX; ++v) key[v] = (lane * VMAX + v) < a.E ? order_key(lv[v]) : 0ull;
-    int sel_e = 0;
-    for (int r = 0; r < a.k; ++r) {
-      uint64_t best = 0;
-      int bv = -1;
-#pragma unroll
-      for (int v = 0; v < VMAX; ++v) {
-        if (key[v] > best) { best = key[v]; bv = v; }
-      }
-      const uint64_t m = max_lanes_u64(best);
-      const uint64_t ball = __ballot(bv >= 0 && best == m);
-      const int L = ball ? __ffsll((unsigned long long)ball) - 1 : 0;
-      const int win = __shfl(lane * VMAX + (bv < 0 ? 0 : bv), L);
-#pragma unroll
-      for (int v = 0; v < VMAX; ++v)
-        if (lane == L && v == bv) key[v] = 0ull;
-      if (lane == r) sel_e = win;
-    }
-    double l = 0.0;
-    if (lane < a.k) l = ld_agent(lg + sel_e);
-    const double l0 = __shfl(l, 0);
-    const double ex = lane < a.k ? exp(l - l0) : 0.0;
-    const double z = sum_lanes64(ex);
-    if (lane < a.k) {
-      const float w = (float)(ex / z);
-      const int64_t o = (int64_t)t * a.k + lane;
-      if (a.idx_out) a.idx_out[o] = sel_e;
-      if (a.w_out) a.w_out[o] = w;
-      if (a.w_ws) a.w_ws[o] = w;
-      s_sel[o] = sel_e;
-    }
-    if (lane == 0 && a.g_ws && a.rows > a.E) {
-      const double gl = ld_agent(lg + a.E);
-      a.g_ws[t] = (float)(1.0 / (1.0 + exp(-gl)));
-    }
-  }
-  __syncthreads();
-
-  if (a.act) {
-    int32_t* act = a.act;
-    int32_t* act_e = act + 2;
-    int32_t* act_off = act_e + a.maxA;
-    int32_t* act_cnt = act_off + a.maxA;
-    int32_t* act_mf = act_cnt + a.maxA;
-    int32_t* entries = act_mf + a.maxA;
-    const int nsel = a.T * a.k;
-    if (a.T == 1) {
-      // One token: the k routed experts in selection order, then the shared one.
-      if (tid <= a.k) {
-        act_e[tid] = tid < a.k ? s_sel[tid] : a.E;
-        act_off[tid] = tid;
-        act_cnt[tid] = 1;
-        entries[tid] = tid;
-      }
-      if (tid == 0) {
-        int nm = 0;
-        for (int i = 0; i <= a.k; ++i)
-          if (1 >= a.mfma_thr) act_mf[nm++] = i;
-        act[0] = a.k + 1;
-        act[1] = nm;
-      }
-    } else {
-      // Group token slots by expert: histogram, exclusive scans, stable scatter.
-      int* s_cnt = s_sel + nsel;   // [E]
-      int* s_pos = s_cnt + a.E;    // [E] rank among active experts
-      int* s_off = s_pos + a.E;    // [E] first entry
-      for (int e = tid; e < a.E; e += kThreads) s_cnt[e] = 0;
-      __syncthreads();
-      for (int j = tid; j < nsel; j += kThreads) atomicAdd(&s_cnt[s_sel[j]], 1);
-      __syncthreads();
-      const int per = (a.E + kThreads - 1) / kThreads;
-      const int e0 = tid * per, e1 = min(a.E, e0 + per);
-      int nf = 0, nc = 0;
-      for (int e = e0; e < e1; ++e) { nf += s_cnt[e] > 0; nc += s_cnt[e]; }
-      int tf, tc;
-      int bf = block_exscan(nf, s_scan, tf);
-      int bc = block_exscan(nc, s_scan, tc);
-      for (int e = e0; e < e1; ++e) {
-        s_pos[e] = bf;
-        s_off[e] = bc;
-        if (s_cnt[e] > 0) {
-          act_e[bf] = e;
-          act_off[bf] = bc;
-          act_cnt[bf] = s_cnt[e];
-          ++bf;
-        }
-        bc += s_cnt[e];
-      }
-      __syncthreads();
-      for (int j = tid; j < nsel; j += kThreads) {
-        const int e = s_sel[j];
-        int rank = 0;
-        for (int jj = 0; jj < j; ++jj) rank += (s_sel[jj] == e);
-        entries[s_off[e] + rank] = (j / a.k) * a.kp1 + (j % a.k);
-      }
-      for (int t = tid; t < a.T; t += kThreads) entries[nsel + t] = t * a.kp1 + a.k;
-      if (tid == 0) {
-        act_e[tf] = a.E;
-        act_off[tf] = nsel;
-        act_cnt[tf] = a.T;
-        int nm = 0;
-        for (int e = 0; e < a.E; ++e)
-          if (s_cnt[e] >= a.mfma_thr) act_mf[nm++] = s_pos[e];
-        if (a.T >= a.mfma_thr) act_mf[nm++] = tf;
-        act[0] = tf + 1;
-        act[1] = nm;
-      }
-    }
-  }
-  if (tid == 0) st_agent(a.counter, 0);
 }
 
 // ============================================================= FFN setup

@@ -1,0 +1,273 @@
+// fmoe_route.h -- router of the multi-launch path (any number of tokens).
+//
+// [WAS] "Verstaendnis von Mixture-of-Experts (MoE) ...": the router scores
+// every expert for every token and keeps the k best, plus the shared expert.
+// Two kernels:
+//   k_route_logits  logits = Wr . x for all tokens as one fp64 matrix product
+//                   on the matrix cores (v_mfma_f64_16x16x4_f64).  Every
+//                   product of two fp32 values is exact in fp64, so the sums
+//                   do not depend on their order beyond fp64 rounding.  A
+//                   workgroup takes 16 router rows x 32 tokens over one slice
+//                   of the hidden dim (its 4 waves split the slice again and
+//                   add in a fixed order through LDS); partial sums per slice
+//                   go to the workspace.  Extra workgroups prepare the
+//                   activations of the gate/up products.
+//   k_route_select  one workgroup per token: adds the slices in a fixed
+//                   order, picks the top k (larger logit first, lower index on
+//                   ties), the softmax weights over the selection and the
+//                   shared expert's sigmoid gate; the last workgroup groups
+//                   the token slots by expert (histogram, scans, stable
+//                   scatter) for the expert kernels.
+#pragma once
+
+#include "fmoe_kernels.h"
+
+namespace fmoe {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
+  __shared__ f64x4 s_red[3][2][kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrt = (a.rows + 15) / 16, ntp = (a.T + 31) / 32;
+  const int nlog = nrt * ntp * a.ksplit;
+
+  if ((int)blockIdx.x >= nlog) {
+    // ---- activation prep for the gate/up products (independent of routing)
+    if (!a.xprep) return;
+    const int pb = blockIdx.x - nlog;
+    const int per_tok = a.H / 32;
+    const int gb = pb * (kThreads / 8) + (tid >> 3);
+    const bool ok = gb < a.T * per_tok;
+    const int t = ok ? gb / per_tok : 0, blk = ok ? gb % per_tok : -1;
+    const float* src = a.x + (int64_t)t * a.H;
+    uint8_t* dst = a.xprep + (int64_t)t * xprep_bytes(a.H);
+    if (a.bits == 4) prep_blocks<4, false>(src, dst, a.H, blk);
+    else prep_blocks<2, false>(src, dst, a.H, blk);
+    return;
+  }
+
+  const int ks = blockIdx.x % a.ksplit;
+  const int rest = blockIdx.x / a.ksplit;
+  const int rt = rest % nrt, tp = rest / nrt;
+  // Operand lanes: lane = m + 16 g supplies row m of the A tile (router rows)
+  // and column m of the B tile (tokens) at the k index of group g.
+  const int m = lane & 15, g = lane >> 4;
+  const int row = rt * 16 + m;
+  const float* wrow = row < a.E ? a.Wr + (int64_t)row * a.H : (row < a.rows ? a.wsg : a.Wr);
+  const bool wok = row < a.rows;
+  const int t0 = tp * 32 + m, t1 = t0 + 16;
+  const bool ok0 = t0 < a.T, ok1 = t1 < a.T;
+  const float* x0 = a.x + (int64_t)(ok0 ? t0 : 0) * a.H;
+  const float* x1 = a.x + (int64_t)(ok1 ? t1 : 0) * a.H;
+
+  // Hidden dim in blocks of 64; slice s of NS gets blocks [b0, b1).
+  const int nblk = (a.H + 63) / 64, NS = a.ksplit * 4, s = ks * 4 + wave;
+  const int b0 = (int)((int64_t)s * nblk / NS), b1 = (int)((int64_t)(s + 1) * nblk / NS);
+
+  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  for (int b = b0; b < b1; ++b) {
+    // Lane group g covers elements kb .. kb+15 of its row and of its tokens.
+    const int kb = b * 64 + 16 * g;
+    float4 wv[4], xa[4], xb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = kb + 4 * j;
+      const bool in = kk < a.H;   // H % 4 == 0: a float4 is wholly in or out
+      const int kc = in ? kk : 0;
+      wv[j] = ld_nt(reinterpret_cast<const float4*>(wrow + kc));
+      xa[j] = *reinterpret_cast<const float4*>(x0 + kc);
+      xb[j] = *reinterpret_cast<const float4*>(x1 + kc);
+      if (!(in && wok)) wv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (!(in && ok0)) xa[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (!(in && ok1)) xb[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w4[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+      const float a4[4] = {xa[j].x, xa[j].y, xa[j].z, xa[j].w};
+      const float c4[4] = {xb[j].x, xb[j].y, xb[j].z, xb[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double wd = (double)w4[c];
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(wd, (double)a4[c], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(wd, (double)c4[c], acc1, 0, 0, 0);
+      }
+    }
+  }
+
+  // Waves 1..3 hand their tiles to wave 0, which adds them in wave order.
+  if (wave > 0) {
+    s_red[wave - 1][0][lane] = acc0;
+    s_red[wave - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    acc0 += s_red[w][0][lane];
+    acc1 += s_red[w][1][lane];
+  }
+  // Result lane layout of the fp64 16x16 product: element r of lane
+  // (m + 16 g) is row g + 4 r of the tile, token column m (unlike the fp32
+  // products, whose element r is row 4 g + r).
+  double* part = a.part + (int64_t)ks * a.T * a.rows;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = rt * 16 + g + 4 * r;
+    if (rr < a.rows) {
+      if (ok0) part[(int64_t)t0 * a.rows + rr] = acc0[r];
+      if (ok1) part[(int64_t)t1 * a.rows + rr] = acc1[r];
+    }
+  }
+}
+
+// One workgroup per token; the last one to finish groups the slots by expert.
+template <int VMAX>
+__global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
+  extern __shared__ __align__(16) double lds_d[];
+  __shared__ int s_last;
+  __shared__ int s_scan[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+
+  // Logits of this token: the slices added in slice order.
+  double* s_lg = lds_d;   // [rows]
+  for (int e0 = 0; e0 < a.rows; e0 += 4 * kThreads) {
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int ks = 0; ks < a.ksplit; ++ks) {
+      const double* p = a.part + ((int64_t)ks * a.T + t) * a.rows;
+      double pv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + j * kThreads + tid;
+        pv[j] = p[e < a.rows ? e : 0];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += pv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + j * kThreads + tid;
+      if (e < a.rows) {
+        s_lg[e] = v[j];
+        if (a.logits_out && e < a.E) a.logits_out[(int64_t)t * a.E + e] = (float)v[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    uint64_t key[VMAX];
+#pragma unroll
+    for (int v = 0; v < VMAX; ++v) {
+      const int e = lane * VMAX + v;
+      key[v] = e < a.E ? order_key(s_lg[e]) : 0ull;
+    }
+    int sel_e = 0;
+    for (int r = 0; r < a.k; ++r) {
+      uint64_t best = 0;
+      int bv = -1;
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v) {
+        if (key[v] > best) { best = key[v]; bv = v; }
+      }
+      const uint64_t mx = max_lanes_u64(best);
+      // Equal keys: the lowest lane holds the lowest index (indices ascend
+      // with lane, then with v, and the first maximum in v order is kept).
+      const uint64_t ball = __ballot(bv >= 0 && best == mx);
+      const int L = ball ? __ffsll((unsigned long long)ball) - 1 : 0;
+      const int win = __shfl(lane * VMAX + (bv < 0 ? 0 : bv), L);
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v)
+        if (lane == L && v == bv) key[v] = 0ull;
+      if (lane == r) sel_e = win;
+    }
+    const double l = lane < a.k ? s_lg[sel_e] : 0.0;
+    const double l0 = __shfl(l, 0);
+    const double ex = lane < a.k ? exp(l - l0) : 0.0;
+    const double z = sum_lanes64(ex);
+    if (lane < a.k) {
+      const float w = (float)(ex / z);
+      const int64_t o = (int64_t)t * a.k + lane;
+      if (a.idx_out) a.idx_out[o] = sel_e;
+      if (a.w_out) a.w_out[o] = w;
+      if (a.w_ws) a.w_ws[o] = w;
+      if (a.sel_ws) st_agent(a.sel_ws + o, sel_e);
+    }
+    if (lane == 0 && a.g_ws && a.rows > a.E)
+      a.g_ws[t] = (float)(1.0 / (1.0 + exp(-s_lg[a.E])));
+  }
+  if (!a.act) return;
+
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) s_last = (add_agent(a.counter, 1) == a.T - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last workgroup: group token slots by expert.
+  int32_t* act = a.act;
+  int32_t* act_e = act + 2;
+  int32_t* act_off = act_e + a.maxA;
+  int32_t* act_cnt = act_off + a.maxA;
+  int32_t* act_mf = act_cnt + a.maxA;
+  int32_t* entries = act_mf + a.maxA;
+  const int nsel = a.T * a.k;
+  int* s_sel = reinterpret_cast<int*>(lds_d);   // [T*k], then [E] x 3
+  for (int j = tid; j < nsel; j += kThreads) s_sel[j] = ld_agent(a.sel_ws + j);
+  int* s_cnt = s_sel + nsel;   // [E]
+  int* s_pos = s_cnt + a.E;    // [E] rank among active experts
+  int* s_off = s_pos + a.E;    // [E] first entry
+  for (int e = tid; e < a.E; e += kThreads) s_cnt[e] = 0;
+  __syncthreads();
+  for (int j = tid; j < nsel; j += kThreads) atomicAdd(&s_cnt[s_sel[j]], 1);
+  __syncthreads();
+  const int per = (a.E + kThreads - 1) / kThreads;
+  const int e0 = tid * per, e1 = min(a.E, e0 + per);
+  int nf = 0, nc = 0;
+  for (int e = e0; e < e1; ++e) { nf += s_cnt[e] > 0; nc += s_cnt[e]; }
+  int tf, tc;
+  int bf = block_exscan(nf, s_scan, tf);
+  int bc = block_exscan(nc, s_scan, tc);
+  for (int e = e0; e < e1; ++e) {
+    s_pos[e] = bf;
+    s_off[e] = bc;
+    if (s_cnt[e] > 0) {
+      act_e[bf] = e;
+      act_off[bf] = bc;
+      act_cnt[bf] = s_cnt[e];
+      ++bf;
+    }
+    bc += s_cnt[e];
+  }
+  __syncthreads();
+  // Stable scatter: a slot's rank among the slots of its expert is the number
+  // of earlier slots (token order, then selection order) with that expert.
+  for (int j = tid; j < nsel; j += kThreads) {
+    const int e = s_sel[j];
+    int rank = 0;
+    for (int jj = 0; jj < j; ++jj) rank += (s_sel[jj] == e);
+    entries[s_off[e] + rank] = (j / a.k) * a.kp1 + (j % a.k);
+  }
+  for (int tt = tid; tt < a.T; tt += kThreads) entries[nsel + tt] = tt * a.kp1 + a.k;
+  // Matrix-core list: experts at or above the threshold in expert order, then
+  // the shared expert.
+  int nm = 0;
+  for (int e = e0; e < e1; ++e) nm += s_cnt[e] >= a.mfma_thr;
+  int tm;
+  int bm = block_exscan(nm, s_scan, tm);
+  for (int e = e0; e < e1; ++e)
+    if (s_cnt[e] >= a.mfma_thr) act_mf[bm++] = s_pos[e];
+  if (tid == 0) {
+    act_e[tf] = a.E;
+    act_off[tf] = nsel;
+    act_cnt[tf] = a.T;
+    if (a.T >= a.mfma_thr) act_mf[tm++] = tf;
+    act[0] = tf + 1;
+    act[1] = tm;
+    st_agent(a.counter, 0);
+  }
+}
+
+}  // namespace fmoe

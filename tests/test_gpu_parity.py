@@ -391,7 +391,7 @@ def test_layer4_correlated_batch(layer4):
 
 
 def test_layer4_mfma_matches_gemv_path(layer4, monkeypatch):
-    # Experts with >= 16 tokens run on the matrix cores; FMOE_NO_MFMA=1 keeps
+    # The experts of a batch run on the matrix cores; FMOE_NO_MFMA=1 keeps
     # them on the multi-token GEMV.  Both fp16 activation forms must agree.
     cfg = layer4.cfg
     note("layer4 T=24 correlated, matrix cores vs GEMV")
@@ -406,9 +406,28 @@ def test_layer4_mfma_matches_gemv_path(layer4, monkeypatch):
         assert rel_l2(a[name], b[name]) <= 1e-3, name
 
 
+def test_layer4_mixed_threshold(layer4, monkeypatch):
+    # FMOE_MFMA_MIN_TOKENS=16: experts with >= 16 tokens on the matrix cores,
+    # the others on the multi-token GEMV kernels, in the same layer.
+    cfg = layer4.cfg
+    note("layer4 T=24 correlated, matrix cores from 16 tokens")
+    base = synth.activations(cfg, 1, pool=4)
+    x = (base + 0.1 * synth.activations(cfg, 24, pool=5)).astype(np.float32)
+    a = layer4.forward(x, x)
+    monkeypatch.setenv("FMOE_MFMA_MIN_TOKENS", "16")
+    b = layer4.forward(x, x)
+    monkeypatch.delenv("FMOE_MFMA_MIN_TOKENS")
+    counts = np.bincount(b["idx"].ravel(), minlength=cfg.E)
+    assert counts.max() >= 16 and (counts[counts > 0] < 16).any()
+    assert np.array_equal(a["idx"], b["idx"])
+    for name in ("moe", "h", "y"):
+        assert rel_l2(a[name], b[name]) <= 1e-3, name
+    check_layer(layer4, x, x, b, [0, 11, 23])
+
+
 def test_tiny_batch_matrix_cores():
-    # The tiny config (group 32, fp32 scales): 20 tokens give the shared expert
-    # 20 >= 16 tokens, so it runs on the matrix cores with one MFMA step per group.
+    # The tiny config (group 32, fp32 scales, one MFMA step per group): 20
+    # tokens give the shared expert two passes (16 + 4 tokens).
     cfg = synth.CONFIGS["tiny"]
     note("tiny T=20")
     gl = GpuLayer(cfg, layer=5)
