@@ -135,7 +135,7 @@ hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
 }
 
 bool mfma_supported(int H, int I, int bits, int group) {
-  return bits == 4 && H % 128 == 0 && I % 128 == 0 && I <= kMfmaMaxI &&
+  return bits == 4 && H % 128 == 0 && I % 128 == 0 && I <= kMfmaMaxI && H <= kMfmaMaxH &&
          H / group <= kMfmaMaxGroups && I / group <= kMfmaMaxGroups && H / group >= 4 &&
          I / group >= 4;
 }

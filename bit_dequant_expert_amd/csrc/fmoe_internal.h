@@ -117,6 +117,8 @@ struct FusedArgs;
 constexpr int kMfmaTokens = 1;        // an expert with at least this many tokens takes the path
 constexpr int kMfmaMaxGroups = 128;   // K / G the path admits
 constexpr int kMfmaMaxI = 2048;       // down input images of a 16-token pass held in LDS
+constexpr int kMfmaMaxH = 8192;       // gate/up input images built in one pass of registers
+constexpr int kMoeLdsTokens = 2;      // gate/up passes with at most this many tokens read A from LDS
 struct MfmaArgs {
   ExpertSrc src;
   const int32_t* act;

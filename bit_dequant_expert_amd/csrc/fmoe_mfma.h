@@ -19,9 +19,12 @@
 // K runs in blocks of 128: lane group l / 16 takes 32 consecutive codes (16
 // bytes) of its row, one 16-byte load, and feeds them to 4 MFMA steps; the
 // activation words follow the same k order.  Codes (and the gate/up
-// activation words) stream through a register ring of blocks; the scales of the
-// workgroup's 64 rows sit in LDS, and so do the down projection's inputs.
+// activation words of passes with many tokens) stream through a register
+// ring of blocks; the scales of the workgroup's 64 rows and the other
+// activation images sit in LDS.
 #pragma once
+
+#include <type_traits>
 
 #include "fmoe_fused.h"
 
@@ -38,18 +41,27 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // [2^13, 2^14).  Per group of G elements: the sum of the fp16 x' values
 // (written when sums is not null).  One wave converts src[0..K) into
 // dst[0..K/8) and sums[0..K/G) and returns sc (dst and sums may be global or
-// LDS).
-template <int G>
+// LDS); K <= 512 MAXW.
+template <int G, int MAXW>
 __device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, float* sums) {
+  // One load of the vector (MAXW words per lane, K <= 512 MAXW), the max,
+  // then the conversion from registers.
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int WPG = G / 8;   // words per group
   const int NW = K / 8;
   const float4* s4 = reinterpret_cast<const float4*>(src);
+  float4 lo[MAXW], hi[MAXW];
+#pragma unroll
+  for (int j = 0; j < MAXW; ++j) {
+    const int w = min(j * kWave + lane, NW - 1);
+    lo[j] = s4[2 * w];
+    hi[j] = s4[2 * w + 1];
+  }
   uint32_t m = 0;   // max |x| as bits (non-negative floats order like their bits)
-  for (int w = lane; w < NW; w += kWave) {
-    const float4 lo = s4[2 * w], hi = s4[2 * w + 1];
-    const float v = fmaxf(fmaxf(fmaxf(fabsf(lo.x), fabsf(lo.y)), fmaxf(fabsf(lo.z), fabsf(lo.w))),
-                          fmaxf(fmaxf(fabsf(hi.x), fabsf(hi.y)), fmaxf(fabsf(hi.z), fabsf(hi.w))));
+#pragma unroll
+  for (int j = 0; j < MAXW; ++j) {
+    const float v = fmaxf(fmaxf(fmaxf(fabsf(lo[j].x), fabsf(lo[j].y)), fmaxf(fabsf(lo[j].z), fabsf(lo[j].w))),
+                          fmaxf(fmaxf(fabsf(hi[j].x), fabsf(hi[j].y)), fmaxf(fabsf(hi[j].z), fabsf(hi[j].w))));
     m = max(m, __float_as_uint(v));
   }
   m = wave_max_u32(m);
@@ -60,13 +72,13 @@ __device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, 
     frexpf(mx, &ex);        // mx = f * 2^ex, f in [0.5, 1)
     sh = ex - 14;           // max|x'| in [2^13, 2^14)
   }
-  for (int w0 = 0; w0 < NW; w0 += kWave) {
-    const int w = w0 + lane;
-    float s2 = 0.f;
-    if (w < NW) {
-      const float4 lo = s4[2 * w], hi = s4[2 * w + 1];
-      const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int j = 0; j < MAXW; ++j) {
+    const int w = j * kWave + lane;
+    if (j * kWave < NW) {   // uniform
+      const float xv[8] = {lo[j].x, lo[j].y, lo[j].z, lo[j].w, hi[j].x, hi[j].y, hi[j].z, hi[j].w};
       _Float16 h[8];
+      float s2 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         h[e] = (_Float16)ldexpf(xv[e], -sh);
@@ -77,12 +89,12 @@ __device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, 
       for (int i = 0; i < 4; ++i)
         p[i] = (uint32_t)__builtin_bit_cast(uint16_t, h[i]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, h[4 + i]) << 16);
-      dst[w] = make_uint4(p[0], p[1], p[2], p[3]);
-    }
-    // The words of a group sit in WPG consecutive lanes (WPG divides 64).
-    if (sums) {
-      s2 = sum_lanes(s2, WPG);
-      if (w < NW && lane % WPG == WPG - 1) sums[w / WPG] = s2;
+      if (w < NW) dst[w] = make_uint4(p[0], p[1], p[2], p[3]);
+      // The words of a group sit in WPG consecutive lanes (WPG divides 64).
+      if (sums) {
+        s2 = sum_lanes(s2, WPG);
+        if (w < NW && lane % WPG == WPG - 1) sums[w / WPG] = s2;
+      }
     }
   }
   return ldexpf(1.f, sh);
@@ -93,8 +105,8 @@ template <int G>
 __global__ __launch_bounds__(kThreads) void k_mimg_prep(MfmaArgs a) {
   const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  const float sc = image_row<G>(a.x + (int64_t)t * a.H, a.H, a.ximg + (int64_t)t * (a.H / 8),
-                                nullptr);
+  const float sc = image_row<G, kMfmaMaxH / 512>(a.x + (int64_t)t * a.H, a.H,
+                                                 a.ximg + (int64_t)t * (a.H / 8), nullptr);
   if ((threadIdx.x & (kWave - 1)) == 0) a.xsc[t] = sc;
 }
 
@@ -113,32 +125,40 @@ __device__ __forceinline__ f16x8 weights_f16x8(uint32_t w, f16x2 s2, f16x2 b2) {
 }
 
 // LDS of k_moe_mfma: scales and biases of the workgroup's 64 rows
-// ([NM][2][64] rows of NG*SB bytes, padded by 4), then (down) the images of
-// the pass's 16 inputs ([16][K/8 + 1] words).
+// ([NM][2][64] rows of NG*SB bytes, padded by 4), then the images of the
+// pass's inputs that are read from LDS ([kMoeLdsTokens or 16][K/8 + 1] words).
 __host__ __device__ inline int moe_scl_row(int K, int G, int SB) { return (K / G) * SB + 4; }
 __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, int SB) {
   const int nm = mode == 0 ? 2 : 1, K = mode == 0 ? H : I;
   const size_t scl = ((size_t)nm * 2 * 64 * moe_scl_row(K, G, SB) + 15) / 16 * 16;
-  return scl + (mode == 0 ? 0 : (size_t)16 * (K / 8 + 1) * 16);
+  return scl + (size_t)(mode == 0 ? kMoeLdsTokens : 16) * (K / 8 + 1) * 16;
 }
 
-// Blocks of 128 k a wave keeps in flight: gate/up ring slots hold the two
-// matrices' code words and the activation words (24 VGPRs), down slots the
-// code words only.
-template <int MODE> struct MoePB { static constexpr int value = MODE == 0 ? 4 : 8; };
+// Blocks of 128 k a wave keeps in flight.  A ring slot holds the lane's 16
+// bytes of codes per matrix and, when the activation words come from global
+// memory (gate/up passes of many tokens), those too (16 VGPRs).
+#ifndef FMOE_MOE_PB_GU
+#define FMOE_MOE_PB_GU 4    // gate/up, activation words from LDS
+#endif
+#ifndef FMOE_MOE_PB_REG
+#define FMOE_MOE_PB_REG 4   // gate/up, activation words in the ring
+#endif
+#ifndef FMOE_MOE_PB_DN
+#define FMOE_MOE_PB_DN 6    // down
+#endif
 
 // Workgroup (ai, rb): active expert ai (every expert with at least
 // a.mfma_thr tokens), rows 64 rb .. 64 rb + 63 (N % 64 == 0), wave w the tile
-// of 16 rows 64 rb + 16 w.  MODE 0: gate and up (K = H) with SwiGLU into abuf,
-// the activation words loaded from the token images in global memory; MODE 1: down (K = I) into yslot, the images of
-// the pass's SwiGLU rows built in LDS first.  Lane l: B column (weight row)
-// l % 16, A row (token) l % 16, k sub-block l / 16; D element i is token
-// 4 (l / 16) + i, weight row l % 16.  Needs K % 128 == 0.
+// of 16 rows 64 rb + 16 w.  MODE 0: gate and up (K = H) with SwiGLU into abuf;
+// the activation words come from the token images in LDS when the pass has
+// at most kMoeLdsTokens tokens, else from global memory through the register
+// ring.  MODE 1: down (K = I) into yslot, the images of the pass's SwiGLU
+// rows built in LDS first.  Lane l: B column (weight row) l % 16, A row
+// (token) l % 16, k sub-block l / 16; D element i is token 4 (l / 16) + i,
+// weight row l % 16.  Needs K % 128 == 0.
 template <int G, int SB, int MODE>
 __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   constexpr int NM = MODE == 0 ? 2 : 1;   // matrices: gate and up, or down
-  constexpr int PB = MoePB<MODE>::value;
-  constexpr int NXW = MODE == 0 ? 4 : 1;  // activation words per lane in a ring slot
   extern __shared__ __align__(16) uint4 lds4[];
   __shared__ float s_sc[16];
   __shared__ int s_ent[16];
@@ -154,18 +174,18 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   const uint8_t* base = a.src.base + e * a.src.stride;
   const int tid = tid_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nl = wave * 16 + (lane & 15);       // row within the workgroup's 64
-  const int n = rb * 64 + nl;
+  const int n = rb * 64 + wave * 16 + (lane & 15);
   const int jg = lane >> 4, am = lane & 15;
   const int NG = K / G, NW = K / 8, NBK = K / 128;
   const int SROW = moe_scl_row(K, G, SB);
+  const int nl = wave * 16 + (lane & 15);       // row within the workgroup's 64
   const int om = MODE == 0 ? 0 : 6;
   uint8_t* s_scl = reinterpret_cast<uint8_t*>(lds4);
   uint4* s_img = reinterpret_cast<uint4*>(s_scl + ((size_t)NM * 2 * 64 * SROW + 15) / 16 * 16);
 
   // Scales and biases of rows rb*64 .. +63: contiguous in the slab, copied
   // into padded LDS rows (16-byte loads where the rows allow, else 4-byte).
-  {
+  auto stage_scales = [&]() {
     const int rowb = NG * SB;
 #pragma unroll
     for (int arr = 0; arr < 2 * NM; ++arr) {
@@ -187,11 +207,14 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         }
       }
     }
-  }
+  };
+  // Addresses: the wave's first row as a wave-uniform base (SGPRs) and one
+  // 32-bit offset per lane, so that a ring slot costs no address registers.
+  const int64_t row0 = (int64_t)rb * 64 + wave * 16;
   const uint8_t* qm[NM];
 #pragma unroll
-  for (int mi = 0; mi < NM; ++mi)
-    qm[mi] = base + a.src.off[om + 3 * mi] + (int64_t)n * (K / 2) + jg * 16;
+  for (int mi = 0; mi < NM; ++mi) qm[mi] = uniform_gptr(base + a.src.off[om + 3 * mi] + row0 * (K / 2));
+  const uint32_t lq = (uint32_t)(lane & 15) * (uint32_t)(K / 2) + (uint32_t)jg * 16u;
 
   for (int c0 = 0; c0 < cnt; c0 += 16) {
     const int pc = min(16, cnt - c0);     // tokens in this pass
@@ -202,73 +225,85 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
       if (MODE == 0) s_sc[tid] = a.xsc[p / a.kp1];
     }
     __syncthreads();
-    if (MODE == 1) {
-      for (int r = wave; r < pc; r += kThreads / kWave) {
-        const float sc = image_row<G>(a.abuf + (int64_t)s_ent[r] * a.I, a.I,
-                                      s_img + r * (NW + 1), nullptr);
-        if (lane == 0) s_sc[r] = sc;
-      }
-      __syncthreads();
-    }
-
     // A row of this lane: token am of the pass, or (idle rows, am >= pc) the
     // pass's last token again.  An output row of the product depends on its
     // own A row only, and idle rows are never stored, so they need no zeros.
     const int ar = min(am, pc - 1);
-    const uint4* xrow = a.ximg;
-    if (MODE == 0) xrow += (int64_t)(s_ent[ar] / a.kp1) * NW;
-    xrow += jg * 4;
-    const uint4* lrow = s_img + ar * (NW + 1) + jg * 4;
 
     f32x4 acc[NM];
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 rq[PB][NM], rx[PB][NXW];
-    auto issue = [&](int u, int b) {
+    auto run = [&](auto al_c) {
+      constexpr bool AL = decltype(al_c)::value;          // activation words from LDS
+      constexpr int PB = MODE == 1 ? FMOE_MOE_PB_DN : (AL ? FMOE_MOE_PB_GU : FMOE_MOE_PB_REG);
+      constexpr int NXW = AL ? 1 : 4;
+      const uint4* xrow = a.ximg + (int64_t)(MODE == 0 ? s_ent[ar] / a.kp1 : 0) * NW + jg * 4;
+      const uint4* lrow = s_img + ar * (NW + 1) + jg * 4;
+      uint4 rq[PB][NM], rx[PB][NXW];
+      auto issue = [&](int u, int b) {
 #pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-        rq[u][mi] = *reinterpret_cast<const uint4*>(qm[mi] + (int64_t)b * 64);
-      if (MODE == 0) {
+        for (int mi = 0; mi < NM; ++mi)
+          rq[u][mi] = *reinterpret_cast<const uint4*>(uniform_gptr(qm[mi] + b * 64) + lq);
+        if (!AL) {
 #pragma unroll
-        for (int s = 0; s < NXW; ++s) rx[u][s] = xrow[b * 16 + s];
+          for (int s = 0; s < NXW; ++s) rx[u][s] = xrow[b * 16 + s];
+        }
+      };
+      auto compute = [&](int u, int b) {
+        uint4 xw[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xw[s] = AL ? lrow[b * 16 + s] : rx[u][s % NXW];
+        const int gi = (b * 128 + jg * 32) / G;
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          const uint8_t* sr = s_scl + ((size_t)(2 * mi) * 64 + nl) * SROW + gi * SB;
+          const uint8_t* br = s_scl + ((size_t)(2 * mi + 1) * 64 + nl) * SROW + gi * SB;
+          const float sv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(sr))
+                                   : *reinterpret_cast<const float*>(sr);
+          const float bv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(br))
+                                   : *reinterpret_cast<const float*>(br);
+          const f16x2 s2 = {(_Float16)sv, (_Float16)sv}, b2 = {(_Float16)bv, (_Float16)bv};
+          const uint32_t cw[4] = {rq[u][mi].x, rq[u][mi].y, rq[u][mi].z, rq[u][mi].w};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, xw[s]), weights_f16x8(cw[s], s2, b2), acc[mi], 0, 0, 0);
+        }
+      };
+      // The first ring of loads goes out before the LDS set-up (the input
+      // images), so their latencies overlap.
+#pragma unroll
+      for (int u = 0; u < PB; ++u) issue(u, min(u, NBK - 1));
+      if (c0 == 0) stage_scales();
+      if (MODE == 1) {
+        for (int r = wave; r < pc; r += kThreads / kWave) {
+          const float sc = image_row<G, kMfmaMaxI / 512>(a.abuf + (int64_t)s_ent[r] * a.I, a.I,
+                                                         s_img + r * (NW + 1), nullptr);
+          if (lane == 0) s_sc[r] = sc;
+        }
+      } else if (AL) {
+        for (int i = tid; i < pc * NW; i += kThreads) {
+          const int m = i / NW, w = i - m * NW;
+          s_img[m * (NW + 1) + w] = a.ximg[(int64_t)(s_ent[m] / a.kp1) * NW + w];
+        }
       }
+      __syncthreads();
+      // Whole rings without branches (the load waits stay exact), then the rest.
+      int bb = 0;
+      for (; bb + PB <= NBK; bb += PB) {
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          compute(u, bb + u);
+          issue(u, min(bb + u + PB, NBK - 1));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (bb + u < NBK) compute(u, bb + u);
     };
-    auto compute = [&](int u, int b) {
-      const int gi = (b * 128 + jg * 32) / G;
-      uint4 xw[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xw[s] = MODE == 0 ? rx[u][s] : lrow[b * 16 + s];
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi) {
-        const uint8_t* sr = s_scl + ((size_t)(2 * mi) * 64 + nl) * SROW + gi * SB;
-        const uint8_t* br = s_scl + ((size_t)(2 * mi + 1) * 64 + nl) * SROW + gi * SB;
-        const float sv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(sr))
-                                 : *reinterpret_cast<const float*>(sr);
-        const float bv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(br))
-                                 : *reinterpret_cast<const float*>(br);
-        const f16x2 s2 = {(_Float16)sv, (_Float16)sv}, b2 = {(_Float16)bv, (_Float16)bv};
-        const uint32_t cw[4] = {rq[u][mi].x, rq[u][mi].y, rq[u][mi].z, rq[u][mi].w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, xw[s]), weights_f16x8(cw[s], s2, b2), acc[mi], 0, 0, 0);
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < PB; ++u) issue(u, min(u, NBK - 1));
-    // Whole rings without branches (the load waits stay exact), then the rest.
-    int bb = 0;
-    for (; bb + PB <= NBK; bb += PB) {
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        compute(u, bb + u);
-        issue(u, min(bb + u + PB, NBK - 1));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PB; ++u)
-      if (bb + u < NBK) compute(u, bb + u);
+    if (MODE == 1 || pc <= kMoeLdsTokens) run(std::true_type{});
+    else run(std::false_type{});
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
