@@ -59,10 +59,11 @@ struct RouteArgs {
 
 // Slices of the hidden dim for the router's matrix product: enough
 // workgroups (16 rows x 32 tokens x slice) to cover the chip, at most 8.
+constexpr int kRouteMaxSplit = 8;
 inline int route_ksplit(int T, int rows) {
   const int tiles = ((rows + 15) / 16) * ((T + 31) / 32);
   int ks = (256 + tiles - 1) / tiles;
-  return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+  return ks < 1 ? 1 : (ks > kRouteMaxSplit ? kRouteMaxSplit : ks);
 }
 
 struct GUArgs {

@@ -20,7 +20,7 @@
 //                   scatter) for the expert kernels.
 #pragma once
 
-#include "fmoe_kernels.h"
+#include "fmoe_fused.h"   // wave_max_u32 (and the common kernels)
 
 namespace fmoe {
 
@@ -66,13 +66,11 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   const int b0 = (int)((int64_t)s * nblk / NS), b1 = (int)((int64_t)(s + 1) * nblk / NS);
 
   f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-  for (int b = b0; b < b1; ++b) {
-    // Lane group g covers elements kb .. kb+15 of its row and of its tokens.
-    const int kb = b * 64 + 16 * g;
-    float4 wv[4], xa[4], xb[4];
+  // Lane group g covers elements kb .. kb+15 of its row and of its tokens.
+  auto load_block = [&](int b, float4 (&wv)[4], float4 (&xa)[4], float4 (&xb)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int kk = kb + 4 * j;
+      const int kk = b * 64 + 16 * g + 4 * j;
       const bool in = kk < a.H;   // H % 4 == 0: a float4 is wholly in or out
       const int kc = in ? kk : 0;
       wv[j] = ld_nt(reinterpret_cast<const float4*>(wrow + kc));
@@ -82,6 +80,8 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
       if (!(in && ok0)) xa[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (!(in && ok1)) xb[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  auto mul_block = [&](const float4 (&wv)[4], const float4 (&xa)[4], const float4 (&xb)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float w4[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
@@ -94,6 +94,14 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
         acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(wd, (double)c4[c], acc1, 0, 0, 0);
       }
     }
+  };
+  // Two blocks in flight: the loads of block b+1 go out before block b's products.
+  for (int b = b0; b < b1; b += 2) {
+    float4 wv0[4], xa0[4], xb0[4], wv1[4], xa1[4], xb1[4];
+    load_block(b, wv0, xa0, xb0);
+    load_block(min(b + 1, b1 - 1), wv1, xa1, xb1);
+    mul_block(wv0, xa0, xb0);
+    if (b + 1 < b1) mul_block(wv1, xa1, xb1);
   }
 
   // Waves 1..3 hand their tiles to wave 0, which adds them in wave order.
@@ -110,15 +118,22 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   }
   // Result lane layout of the fp64 16x16 product: element r of lane
   // (m + 16 g) is row g + 4 r of the tile, token column m (unlike the fp32
-  // products, whose element r is row 4 g + r).
-  double* part = a.part + (int64_t)ks * a.T * a.rows;
+  // products, whose element r is row 4 g + r).  Through LDS into
+  // [token][row] order, then each token's 16 rows go out as one 128-byte run.
+  double* s_t = reinterpret_cast<double*>(&s_red[0][0][0]);   // [32][16], reuses s_red
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int rr = rt * 16 + g + 4 * r;
-    if (rr < a.rows) {
-      if (ok0) part[(int64_t)t0 * a.rows + rr] = acc0[r];
-      if (ok1) part[(int64_t)t1 * a.rows + rr] = acc1[r];
-    }
+    s_t[m * 16 + g + 4 * r] = acc0[r];
+    s_t[(m + 16) * 16 + g + 4 * r] = acc1[r];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  double* part = a.part + (int64_t)ks * a.T * a.rows;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = q * 64 + lane, tt = i >> 4, rr = rt * 16 + (i & 15), t = tp * 32 + tt;
+    if (t < a.T && rr < a.rows) part[(int64_t)t * a.rows + rr] = s_t[i];
   }
 }
 
@@ -134,18 +149,23 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
   // Logits of this token: the slices added in slice order.
   double* s_lg = lds_d;   // [rows]
   for (int e0 = 0; e0 < a.rows; e0 += 4 * kThreads) {
-    double v[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int ks = 0; ks < a.ksplit; ++ks) {
-      const double* p = a.part + ((int64_t)ks * a.T + t) * a.rows;
-      double pv[4];
+    // Every slice's loads first (clamped; slices past ksplit are not added),
+    // then the sums in slice order.
+    double pv[kRouteMaxSplit][4];
+#pragma unroll
+    for (int ks = 0; ks < kRouteMaxSplit; ++ks) {
+      const double* p = a.part + ((int64_t)min(ks, a.ksplit - 1) * a.T + t) * a.rows;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + j * kThreads + tid;
-        pv[j] = p[e < a.rows ? e : 0];
+        pv[ks][j] = p[e < a.rows ? e : 0];
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += pv[j];
     }
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < kRouteMaxSplit; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = ks < a.ksplit ? v[j] + pv[ks][j] : v[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + j * kThreads + tid;
@@ -172,12 +192,17 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
       for (int v = 0; v < VMAX; ++v) {
         if (key[v] > best) { best = key[v]; bv = v; }
       }
-      const uint64_t mx = max_lanes_u64(best);
+      // Wave maximum on DPP row operations: the high halves first, the low
+      // halves only among lanes that tie on them.
+      const uint32_t hi = (uint32_t)(best >> 32);
+      const uint32_t mh = wave_max_u32(hi);
+      const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)best : 0u);
+      const uint64_t mx = ((uint64_t)mh << 32) | ml;
       // Equal keys: the lowest lane holds the lowest index (indices ascend
       // with lane, then with v, and the first maximum in v order is kept).
       const uint64_t ball = __ballot(bv >= 0 && best == mx);
       const int L = ball ? __ffsll((unsigned long long)ball) - 1 : 0;
-      const int win = __shfl(lane * VMAX + (bv < 0 ? 0 : bv), L);
+      const int win = __builtin_amdgcn_readlane(lane * VMAX + (bv < 0 ? 0 : bv), L);
 #pragma unroll
       for (int v = 0; v < VMAX; ++v)
         if (lane == L && v == bv) key[v] = 0ull;
@@ -244,10 +269,16 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
   __syncthreads();
   // Stable scatter: a slot's rank among the slots of its expert is the number
   // of earlier slots (token order, then selection order) with that expert.
+  const int4* s_sel4 = reinterpret_cast<const int4*>(s_sel);
   for (int j = tid; j < nsel; j += kThreads) {
     const int e = s_sel[j];
-    int rank = 0;
-    for (int jj = 0; jj < j; ++jj) rank += (s_sel[jj] == e);
+    int rank = 0, jj = 0;
+#pragma unroll 4
+    for (; jj + 4 <= j; jj += 4) {   // four slots per LDS read
+      const int4 v = s_sel4[jj >> 2];
+      rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    }
+    for (; jj < j; ++jj) rank += (s_sel[jj] == e);
     entries[s_off[e] + rank] = (j / a.k) * a.kp1 + (j % a.k);
   }
   for (int tt = tid; tt < a.T; tt += kThreads) entries[nsel + tt] = tt * a.kp1 + a.k;
