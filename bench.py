@@ -108,6 +108,28 @@ def traffic_from_profiles(kernel_hash, workload):
         return None
 
 
+def stack_traffic_from_profiles(kernel_hash, n_layers):
+    """HBM bytes of one 60-layer step: the per-dispatch bytes of every layer kernel in
+    profiles/k_moe_mfma_stack60_batch32_traffic.txt (rocprofv3 counters, copy-calibrated)
+    times the layer count, when the profile was taken on this exact source, else None."""
+    path = os.path.join(ROOT, "profiles", "k_moe_mfma_stack60_batch32_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    total, hsh = 0.0, None
+    for line in open(path):
+        if line.startswith("source_hash:"):
+            hsh = line.split(":", 1)[1].strip()
+        elif line.startswith("| ") and "fmoe::" in line:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            try:
+                total += float(cells[-1])
+            except ValueError:
+                pass
+    if hsh != kernel_hash or total <= 0:
+        return None
+    return int(total * n_layers)
+
+
 def cpu_baseline(cfg, n_tokens):
     """The CPU oracle (single-threaded C, fp64) on a bounded sample of tokens of
     the same workload: routing over all 512 experts plus the 5 active experts'
@@ -597,7 +619,8 @@ def bench_stack(args, torch):
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "roofline": {"bound": "hbm", "kernel": "all launches of the 60 layers (one graph)",
                      "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": stack_traffic_from_profiles(source_hash(), NL)},
         "kernel_source_hash": source_hash(),
         "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
     }
