@@ -478,6 +478,33 @@ def test_stack_chained_tiny():
         x, r = y, h
 
 
+def test_layer4_stack_chained_batch32():
+    # The 60-layer benchmark's configuration at full size, three layers deep:
+    # 32 independent tokens, each layer's y and h fed to the next on the device
+    # through one shared workspace (as the benchmark runs it), sampled tokens of
+    # every layer checked against the oracle fed the GPU's own layer inputs.
+    cfg = synth.CONFIGS["layer4"]
+    layers = [GpuLayer(cfg, layer=10 + l, random_gamma=False) for l in range(3)]
+    T = 32
+    x = dev(synth.activations(cfg, T, pool=4))
+    r = x.clone()
+    ws = torch.zeros(fm.fmoe_workspace_size(layers[0].L, T), dtype=torch.uint8, device="cuda")
+    for l, gl in enumerate(layers):
+        note(f"layer4 stack T=32, layer {l}")
+        h = torch.empty_like(x)
+        y = torch.empty_like(x)
+        idx = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, cfg.k, device="cuda")
+        moe = torch.empty_like(x)
+        fm.fmoe_moe_layer_forward(gl.L, T, x, r, h, y, idx, w, moe, ws)
+        torch.cuda.synchronize()
+        got = dict(h=h.cpu().numpy(), y=y.cpu().numpy(), moe=moe.cpu().numpy(),
+                   idx=idx.cpu().numpy(), w=w.cpu().numpy())
+        excl = check_layer(gl, x.cpu().numpy(), r.cpu().numpy(), got, [0, 17, 31])
+        assert excl <= 1
+        x, r = y, h
+
+
 # ------------------------------------------------ one-launch layer kernel
 def test_fused_matches_multilaunch(layer4, monkeypatch):
     # The one-token layer runs as one persistent launch; FMOE_NO_FUSED=1 forces
