@@ -141,7 +141,7 @@ __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, in
 #define FMOE_MOE_PB_GU 4    // gate/up, activation words from LDS
 #endif
 #ifndef FMOE_MOE_PB_REG
-#define FMOE_MOE_PB_REG 4   // gate/up, activation words in the ring
+#define FMOE_MOE_PB_REG 2   // gate/up, activation words in the ring
 #endif
 #ifndef FMOE_MOE_PB_DN
 #define FMOE_MOE_PB_DN 6    // down

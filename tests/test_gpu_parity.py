@@ -366,6 +366,19 @@ def test_layer2_single_token(layer2):
         check_layer(layer2, x[t:t + 1], x[t:t + 1], got, [0])
 
 
+def test_layer2_batch_gemv(layer2):
+    # 2-bit batches run on the multi-token GEMV kernels (no matrix-core form);
+    # correlated tokens give experts several tokens each.
+    cfg = layer2.cfg
+    note("layer2 T=12 correlated")
+    base = synth.activations(cfg, 1, pool=11)
+    x = (base + 0.3 * synth.activations(cfg, 12, pool=12)).astype(np.float32)
+    got = layer2.forward(x, x)
+    counts = np.bincount(got["idx"].ravel(), minlength=cfg.E)
+    assert counts.max() >= 2
+    check_layer(layer2, x, x, got, [0, 5, 11])
+
+
 def test_layer4_batch32_subset(layer4):
     cfg = layer4.cfg
     note("layer4 T=32")
