@@ -319,36 +319,15 @@ fmoe_status fmoe_expert_ffn(const fmoe_expert* e, const fmoe_qformat* fmt, const
   uint8_t* wsb = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
 
-  fmoe::ExpertSrc src{};
-  src.base = nullptr;
-  src.stride = 0;
-  const fmoe_qmat* m[3] = {&e->gate, &e->up, &e->down};
-  for (int i = 0; i < 3; ++i) {
-    src.off[3 * i] = (int64_t)(uintptr_t)m[i]->q;
-    src.off[3 * i + 1] = (int64_t)(uintptr_t)m[i]->scale;
-    src.off[3 * i + 2] = (int64_t)(uintptr_t)m[i]->bias;
-  }
-  int32_t* act = (int32_t*)(wsb + L.act);
-  hipError_t he = fmoe::launch_ffn_prep(f.bits, x, H, wsb + L.xprep, act, 1, s);
-  if (he != hipSuccess) return hip_fail(he, "ffn prep kernel");
-
-  fmoe::GUArgs g{};
-  g.src = src; g.act = act; g.maxA = 1; g.kp1 = 1; g.H = H; g.I = I;
-  g.xprep = wsb + L.xprep; g.abuf = (float*)(wsb + L.abuf); g.aprep = wsb + L.aprep;
-  g.ccnt = (int*)(wsb + L.ccnt);
-  g.nrb = (I + fmoe::rows_per_wg(H, f.bits) - 1) / fmoe::rows_per_wg(H, f.bits);
-  g.U = fmoe::iters_per_wave(H, f.bits);
-  g.mfma_thr = INT_MAX;
-  he = fmoe::launch_gateup(f, g, g.nrb, s);
+  // Two launches: gate and up with SwiGLU into the workspace, then down.
+  float* abuf = (float*)(wsb + L.abuf);
+  hipError_t he = fmoe::launch_gemv_swiglu(
+      f, (const uint8_t*)e->gate.q, (const uint8_t*)e->gate.scale, (const uint8_t*)e->gate.bias,
+      (const uint8_t*)e->up.q, (const uint8_t*)e->up.scale, (const uint8_t*)e->up.bias, I, H, x,
+      abuf, s);
   if (he != hipSuccess) return hip_fail(he, "gate/up kernel");
-
-  fmoe::DArgs d{};
-  d.src = src; d.act = act; d.maxA = 1; d.kp1 = 1; d.k = 0; d.H = H; d.I = I;
-  d.aprep = wsb + L.aprep; d.yslot = y;
-  d.nrb = (H + fmoe::rows_per_wg(I, f.bits) - 1) / fmoe::rows_per_wg(I, f.bits);
-  d.U = fmoe::iters_per_wave(I, f.bits);
-  d.mfma_thr = INT_MAX;
-  he = fmoe::launch_down_slots(f, d, d.nrb, s);
+  he = fmoe::launch_gemv(f, (const uint8_t*)e->down.q, (const uint8_t*)e->down.scale,
+                         (const uint8_t*)e->down.bias, H, I, abuf, y, s);
   if (he != hipSuccess) return hip_fail(he, "down kernel");
   return FMOE_OK;
 }

@@ -116,6 +116,15 @@ hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t
   return run_variant(c);
 }
 
+hipError_t launch_gemv_swiglu(QFmt f, const uint8_t* gq, const uint8_t* gs, const uint8_t* gb,
+                              const uint8_t* uq, const uint8_t* us, const uint8_t* ub, int N,
+                              int K, const float* x, float* a, hipStream_t st) {
+  VCall c = make_call(VCall::GEMV_SWIGLU, f, segs_per_lane(K, f.bits), 0, st);
+  c.q = gq; c.s = gs; c.b = gb; c.q2 = uq; c.s2 = us; c.b2 = ub;
+  c.N = N; c.K = K; c.x = x; c.y = a;
+  return run_variant(c);
+}
+
 hipError_t launch_gateup(QFmt f, const GUArgs& a, int grid, hipStream_t st) {
   VCall c = make_call(VCall::GATEUP, f, segs_per_lane(a.H, f.bits), grid, st);
   c.gu = &a;

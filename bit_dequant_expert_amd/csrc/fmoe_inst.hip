@@ -29,6 +29,17 @@ hipError_t run_one(const VCall& c) {
                          c.st, c.q, c.s, c.b, c.N, c.K, c.x, c.y, U);
       break;
     }
+    case VCall::GEMV_SWIGLU: {
+      const int rpi = rows_per_iter(c.K, B);
+      int U = c.N / (4 * rpi * 256);
+      U = U < 1 ? 1 : (U > kUMax ? kUMax : U);
+      const int rwg = 4 * rpi * U;
+      const int grid = (c.N + rwg - 1) / rwg;
+      hipLaunchKernelGGL((k_gemv_swiglu<B, G, SB, NS>), dim3(grid), dim3(kThreads),
+                         xprep_bytes(c.K), c.st, c.q, c.s, c.b, c.q2, c.s2, c.b2, c.N, c.K, c.x,
+                         c.y, U);
+      break;
+    }
     case VCall::GATEUP:
       if (c.gu->U == 2)
         hipLaunchKernelGGL((k_gateup<B, G, SB, NS, 2>), dim3(c.grid), dim3(kThreads),

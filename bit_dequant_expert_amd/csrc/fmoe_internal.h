@@ -150,12 +150,13 @@ inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane re
 // One launch of a format-templated kernel; run_variant_<bits>_<group> (one
 // translation unit per pair, compiled in parallel) instantiates the kernels.
 struct VCall {
-  enum Kind { GEMV, GATEUP, DOWN_COMBINE, DOWN_SLOTS, MIMG_PREP, EXPERT_MFMA, FUSED1 } kind;
+  enum Kind { GEMV, GEMV_SWIGLU, GATEUP, DOWN_COMBINE, DOWN_SLOTS, MIMG_PREP, EXPERT_MFMA, FUSED1 } kind;
   QFmt f;
   int ns;
   int grid;
   hipStream_t st;
   const uint8_t *q, *s, *b;
+  const uint8_t *q2, *s2, *b2;   // GEMV_SWIGLU: the up matrix (q, s, b: gate)
   int N, K;
   const float* x;
   float* y;
@@ -177,6 +178,10 @@ int fused_occupancy_2_64(int sb, int ns, int E, size_t lds);
 
 hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t* b, int N,
                        int K, const float* x, float* y, hipStream_t st);
+// a[n] = silu(gate . x)[n] * (up . x)[n] for one expert's [N x K] gate and up.
+hipError_t launch_gemv_swiglu(QFmt f, const uint8_t* gq, const uint8_t* gs, const uint8_t* gb,
+                              const uint8_t* uq, const uint8_t* us, const uint8_t* ub, int N,
+                              int K, const float* x, float* a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_ffn_prep(int bits, const float* x, int H, uint8_t* xprep, int32_t* act,
                            int maxA, hipStream_t st);

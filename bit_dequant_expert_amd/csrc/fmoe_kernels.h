@@ -70,6 +70,46 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ q
   }
 }
 
+// Gate and up of one expert against one vector, SwiGLU applied: the same
+// structure as k_gemv with a pair of tiles per row ([WAS] "3. Handoptimierte
+// Metal Compute-Shader": dequant matrix-vector products with the SwiGLU
+// activation fused).
+template <int BITS, int G, int SB, int NS>
+__global__ __launch_bounds__(kThreads) void k_gemv_swiglu(
+    const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gs, const uint8_t* __restrict__ gb,
+    const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us, const uint8_t* __restrict__ ub,
+    int N, int K, const float* __restrict__ x, float* __restrict__ y, int U) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  using TileT = Tile<BITS, G, SB, NS>;
+  const RowGeo geo(K, BITS);
+  const int wave = threadIdx.x >> 6;
+  const int rpw = U * geo.RPI;
+  int64_t n = ((int64_t)blockIdx.x * 4 + wave) * rpw + geo.lane_row;
+
+  TileT cg, cu;
+  if (n < N) { cg.load(gq, gs, gb, K, n, geo); cu.load(uq, us, ub, K, n, geo); }
+  else { cg.zero(); cu.zero(); }
+
+  prep_vector<BITS, kThreads>(x, lds, K);
+  __syncthreads();
+  XRegs<BITS, NS> xr;
+  xr.load(lds, K, geo);
+
+  for (int it = 0; it < U; ++it) {
+    TileT ng, nu;
+    const bool more = it + 1 < U;
+    const int64_t nn = n + geo.RPI;
+    if (more) {
+      if (nn < N) { ng.load(gq, gs, gb, K, nn, geo); nu.load(uq, us, ub, K, nn, geo); }
+      else { ng.zero(); nu.zero(); }
+    }
+    const float g = sum_lanes(tile_dot(cg, xr), geo.LPR);
+    const float u = sum_lanes(tile_dot(cu, xr), geo.LPR);
+    if (n < N && geo.lane_seg == geo.LPR - 1) y[n] = silu(g) * u;
+    if (more) { cg = ng; cu = nu; n = nn; }
+  }
+}
+
 // ================================================================== route
 __device__ __forceinline__ uint64_t order_key(double v) {
   // Monotone map of fp64 to uint64 (larger value -> larger key).
