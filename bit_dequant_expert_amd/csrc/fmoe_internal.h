@@ -26,6 +26,8 @@ struct ExpertSrc {
 //   act[0] = number of active experts, act[1] = number of them on the MFMA path,
 //   then act_e[maxA], act_off[maxA], act_cnt[maxA], mfma[maxA], entries[T*(k+1)].
 // Entry p = t*(k+1) + slot names token t's slot (slot k = the shared expert).
+// Batches list the shared expert first (index 0, entries T*k ..), then the
+// routed experts in expert order with their entries in token order.
 struct ActView {
   const int32_t* base;
   int maxA;

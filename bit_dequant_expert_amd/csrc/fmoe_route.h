@@ -255,13 +255,16 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
   int tf, tc;
   int bf = block_exscan(nf, s_scan, tf);
   int bc = block_exscan(nc, s_scan, tc);
+  // The shared expert (all T tokens: the most work) takes active index 0 so
+  // that the expert kernels start its workgroups first; routed experts follow
+  // in expert order at 1 .. tf.
   for (int e = e0; e < e1; ++e) {
-    s_pos[e] = bf;
+    s_pos[e] = bf + 1;
     s_off[e] = bc;
     if (s_cnt[e] > 0) {
-      act_e[bf] = e;
-      act_off[bf] = bc;
-      act_cnt[bf] = s_cnt[e];
+      act_e[bf + 1] = e;
+      act_off[bf + 1] = bc;
+      act_cnt[bf + 1] = s_cnt[e];
       ++bf;
     }
     bc += s_cnt[e];
@@ -282,21 +285,22 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
     entries[s_off[e] + rank] = (j / a.k) * a.kp1 + (j % a.k);
   }
   for (int tt = tid; tt < a.T; tt += kThreads) entries[nsel + tt] = tt * a.kp1 + a.k;
-  // Matrix-core list: experts at or above the threshold in expert order, then
-  // the shared expert.
+  // Matrix-core list: the shared expert, then the routed experts at or above
+  // the threshold in expert order.
   int nm = 0;
   for (int e = e0; e < e1; ++e) nm += s_cnt[e] >= a.mfma_thr;
   int tm;
-  int bm = block_exscan(nm, s_scan, tm);
+  const int sh = a.T >= a.mfma_thr ? 1 : 0;
+  int bm = block_exscan(nm, s_scan, tm) + sh;
   for (int e = e0; e < e1; ++e)
     if (s_cnt[e] >= a.mfma_thr) act_mf[bm++] = s_pos[e];
   if (tid == 0) {
-    act_e[tf] = a.E;
-    act_off[tf] = nsel;
-    act_cnt[tf] = a.T;
-    if (a.T >= a.mfma_thr) act_mf[tm++] = tf;
+    act_e[0] = a.E;
+    act_off[0] = nsel;
+    act_cnt[0] = a.T;
+    if (sh) act_mf[0] = 0;
     act[0] = tf + 1;
-    act[1] = tm;
+    act[1] = tm + sh;
     st_agent(a.counter, 0);
   }
 }
