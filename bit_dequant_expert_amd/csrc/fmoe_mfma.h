@@ -42,21 +42,29 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // (written when sums is not null).  One wave converts src[0..K) into
 // dst[0..K/8) and sums[0..K/G) and returns sc (dst and sums may be global or
 // LDS); K <= 512 MAXW.
-template <int G, int MAXW>
-__device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, float* sums) {
-  // One load of the vector (MAXW words per lane, K <= 512 MAXW), the max,
-  // then the conversion from registers.
+// The loads of image_row: MAXW words per lane (K <= 512 MAXW), clamped.
+template <int MAXW>
+__device__ __forceinline__ void image_load(const float* src, int K, float4 (&lo)[MAXW],
+                                           float4 (&hi)[MAXW]) {
   const int lane = threadIdx.x & (kWave - 1);
-  constexpr int WPG = G / 8;   // words per group
   const int NW = K / 8;
   const float4* s4 = reinterpret_cast<const float4*>(src);
-  float4 lo[MAXW], hi[MAXW];
 #pragma unroll
   for (int j = 0; j < MAXW; ++j) {
     const int w = min(j * kWave + lane, NW - 1);
     lo[j] = s4[2 * w];
     hi[j] = s4[2 * w + 1];
   }
+}
+
+// The rest of image_row, from the loaded words: the max, the scale, the
+// conversion and the stores; returns sc.
+template <int G, int MAXW>
+__device__ __forceinline__ float image_finish(const float4 (&lo)[MAXW], const float4 (&hi)[MAXW],
+                                              int K, uint4* dst, float* sums) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int WPG = G / 8;   // words per group
+  const int NW = K / 8;
   uint32_t m = 0;   // max |x| as bits (non-negative floats order like their bits)
 #pragma unroll
   for (int j = 0; j < MAXW; ++j) {
@@ -98,6 +106,13 @@ __device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, 
     }
   }
   return ldexpf(1.f, sh);
+}
+
+template <int G, int MAXW>
+__device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, float* sums) {
+  float4 lo[MAXW], hi[MAXW];
+  image_load<MAXW>(src, K, lo, hi);
+  return image_finish<G, MAXW>(lo, hi, K, dst, sums);
 }
 
 // Images of the batch's token vectors (the gate/up input): one wave per token.
@@ -184,9 +199,39 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   uint4* s_img = reinterpret_cast<uint4*>(s_scl + ((size_t)NM * 2 * 64 * SROW + 15) / 16 * 16);
 
   // Scales and biases of rows rb*64 .. +63: contiguous in the slab, copied
-  // into padded LDS rows (16-byte loads where the rows allow, else 4-byte).
+  // into padded LDS rows.  When they fit in kSR 16-byte words per thread they
+  // are loaded into registers first and stored later (scales_load,
+  // scales_store), else copied in one loop (stage_scales).
+  constexpr int kSR = 1;
+  const int rowb = NG * SB;
+  const int sper = 64 * rowb / 16, stot = 2 * NM * sper;
+  // (Down only: gate/up has no registers to spare for it.)
+  const bool sfast = MODE == 1 && rowb % 16 == 0 && stot <= kSR * kThreads;   // uniform
+  uint4 sreg[kSR];
+  auto scl_src = [&](int arr) {
+    return base + a.src.off[om + 3 * (arr >> 1) + 1 + (arr & 1)] + (int64_t)rb * 64 * rowb;
+  };
+  auto scales_load = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSR; ++j) {
+      const int i = min(j * kThreads + tid, stot - 1);
+      const int arr = i / sper, k = i - arr * sper;
+      sreg[j] = reinterpret_cast<const uint4*>(scl_src(arr))[k];
+    }
+  };
+  auto scales_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSR; ++j) {
+      const int i = j * kThreads + tid;
+      if (i < stot) {
+        const int arr = i / sper, k = i - arr * sper;
+        const int r = (k * 16) / rowb, c = k * 16 - r * rowb;
+        uint32_t* d = reinterpret_cast<uint32_t*>(s_scl + (size_t)arr * 64 * SROW + r * SROW + c);
+        d[0] = sreg[j].x; d[1] = sreg[j].y; d[2] = sreg[j].z; d[3] = sreg[j].w;
+      }
+    }
+  };
   auto stage_scales = [&]() {
-    const int rowb = NG * SB;
 #pragma unroll
     for (int arr = 0; arr < 2 * NM; ++arr) {
       const uint8_t* src = base + a.src.off[om + 3 * (arr >> 1) + 1 + (arr & 1)] +
@@ -271,16 +316,45 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
                 __builtin_bit_cast(f16x8, xw[s]), weights_f16x8(cw[s], s2, b2), acc[mi], 0, 0, 0);
         }
       };
-      // The first ring of loads goes out before the LDS set-up (the input
-      // images), so their latencies overlap.
+      // LDS set-up: the staging loads go out first (scales on the first pass,
+      // the inputs), then the first ring of code loads, then the LDS stores,
+      // each of which waits for its own loads only (one in-order counter);
+      // the code latency overlaps the set-up.
+      constexpr int IMW = kMfmaMaxI / 512;   // down: words per lane of an input row
+      constexpr int kXS = 4;                 // gate/up: image words per thread
+      const bool stage_s = c0 == 0;
+      if (stage_s && sfast) scales_load();
+      float4 ilo[IMW], ihi[IMW];
+      uint4 xs[kXS];
+      const bool xfast = false;   // gate/up: no registers to spare (copied after the ring)
+      if (MODE == 1) {
+        image_load<IMW>(a.abuf + (int64_t)s_ent[min(wave, pc - 1)] * a.I, a.I, ilo, ihi);
+      } else if (xfast) {
+#pragma unroll
+        for (int j = 0; j < kXS; ++j) {
+          const int i = min(j * kThreads + tid, pc * NW - 1), m = i / NW, w = i - m * NW;
+          xs[j] = a.ximg[(int64_t)(s_ent[m] / a.kp1) * NW + w];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < PB; ++u) issue(u, min(u, NBK - 1));
-      if (c0 == 0) stage_scales();
+      if (stage_s && sfast) scales_store();
+      else if (stage_s) stage_scales();
       if (MODE == 1) {
-        for (int r = wave; r < pc; r += kThreads / kWave) {
-          const float sc = image_row<G, kMfmaMaxI / 512>(a.abuf + (int64_t)s_ent[r] * a.I, a.I,
-                                                         s_img + r * (NW + 1), nullptr);
+        if (wave < pc) {
+          const float sc = image_finish<G, IMW>(ilo, ihi, a.I, s_img + wave * (NW + 1), nullptr);
+          if (lane == 0) s_sc[wave] = sc;
+        }
+        for (int r = wave + kThreads / kWave; r < pc; r += kThreads / kWave) {
+          const float sc = image_row<G, IMW>(a.abuf + (int64_t)s_ent[r] * a.I, a.I,
+                                             s_img + r * (NW + 1), nullptr);
           if (lane == 0) s_sc[r] = sc;
+        }
+      } else if (xfast) {
+#pragma unroll
+        for (int j = 0; j < kXS; ++j) {
+          const int i = j * kThreads + tid, m = i / NW, w = i - m * NW;
+          if (i < pc * NW) s_img[m * (NW + 1) + w] = xs[j];
         }
       } else if (AL) {
         for (int i = tid; i < pc * NW; i += kThreads) {
