@@ -436,6 +436,10 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
   ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = mfma_thr;
   ra.xprep = use_gemv ? wsb + W.xprep : nullptr; ra.bits = f.bits;
   ra.n_prep_wgs = use_gemv ? (int)(((int64_t)T * (H / 32) + 31) / 32) : 0;
+  if (use_mfma) {   // the tokens' matrix-core images, in the same launch
+    ra.ximg = (uint4*)(wsb + W.ximg);
+    ra.xsc = (float*)(wsb + W.xsc);
+  }
   hipError_t he = fmoe::launch_route(ra, s);
   if (he != hipSuccess) return hip_fail(he, "route kernel");
 
@@ -456,8 +460,6 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     m.x = x;
     m.ximg = (uint4*)(wsb + W.ximg); m.xsc = (float*)(wsb + W.xsc); m.xsum = (float*)(wsb + W.xsum);
     m.abuf = (float*)(wsb + W.abuf); m.yslot = (float*)(wsb + W.yslot);
-    if ((he = fmoe::launch_mimg_prep(f, m, s)) != hipSuccess)
-      return hip_fail(he, "activation image kernel");
     if ((he = fmoe::launch_moe_mfma(f, m, 0, s)) != hipSuccess)
       return hip_fail(he, "gate/up matrix-core kernel");
   }

@@ -149,14 +149,6 @@ bool mfma_supported(int H, int I, int bits, int group) {
          I / group >= 4;
 }
 
-hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, hipStream_t st) {
-  const int grid = (a.T + kThreads / kWave - 1) / (kThreads / kWave);
-  if (grid <= 0) return hipSuccess;
-  VCall c = make_call(VCall::MIMG_PREP, f, 1, grid, st);
-  c.mf = &a;
-  return run_variant(c);
-}
-
 hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st) {
   const int N = mode == 0 ? a.I : a.H;
   const int grid = a.maxA * (N / 64);
@@ -210,7 +202,8 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nlog = ((a.rows + 15) / 16) * ((a.T + 31) / 32) * a.ksplit;
-  hipLaunchKernelGGL(k_route_logits, dim3(nlog + a.n_prep_wgs), dim3(kThreads), 0, st, a);
+  const int nimg = a.ximg ? (a.T + kThreads / kWave - 1) / (kThreads / kWave) : 0;
+  hipLaunchKernelGGL(k_route_logits, dim3(nlog + a.n_prep_wgs + nimg), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lg = (size_t)a.rows * 8;

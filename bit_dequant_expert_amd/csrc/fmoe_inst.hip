@@ -72,9 +72,6 @@ hipError_t run_one(const VCall& c) {
         hipLaunchKernelGGL((k_down_slots<B, G, SB, NS, 1>), dim3(c.grid), dim3(kThreads),
                            xprep_bytes(c.d->I), c.st, *c.d);
       break;
-    case VCall::MIMG_PREP:
-      hipLaunchKernelGGL((k_mimg_prep<G>), dim3(c.grid), dim3(kThreads), 0, c.st, *c.mf);
-      break;
     case VCall::EXPERT_MFMA:
       if constexpr (B != 4) {
         return hipErrorNotSupported;

@@ -57,6 +57,8 @@ struct RouteArgs {
   uint8_t* xprep;          // per-token prepared activations or null
   int bits;
   int n_prep_wgs;
+  uint4* ximg;             // per-token matrix-core images [T][H/8] or null
+  float* xsc;              // their scales [T]
 };
 
 // Slices of the hidden dim for the router's matrix product: enough
@@ -152,7 +154,7 @@ inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane re
 // One launch of a format-templated kernel; run_variant_<bits>_<group> (one
 // translation unit per pair, compiled in parallel) instantiates the kernels.
 struct VCall {
-  enum Kind { GEMV, GEMV_SWIGLU, GATEUP, DOWN_COMBINE, DOWN_SLOTS, MIMG_PREP, EXPERT_MFMA, FUSED1 } kind;
+  enum Kind { GEMV, GEMV_SWIGLU, GATEUP, DOWN_COMBINE, DOWN_SLOTS, EXPERT_MFMA, FUSED1 } kind;
   QFmt f;
   int ns;
   int grid;
@@ -194,7 +196,6 @@ hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
 // mode 0: gate/up (x images, then SwiGLU into abuf); mode 1: down (images of
 // the path's abuf entries, then yslot).  The prep is one launch per mode.
 bool mfma_supported(int H, int I, int bits, int group);
-hipError_t launch_mimg_prep(QFmt f, const MfmaArgs& a, hipStream_t st);
 hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st);
 // One-token layer in one persistent launch; returns hipErrorNotSupported when
 // the row geometry is outside what the fused kernel is instantiated for.

@@ -115,16 +115,6 @@ __device__ __forceinline__ float image_row(const float* src, int K, uint4* dst, 
   return image_finish<G, MAXW>(lo, hi, K, dst, sums);
 }
 
-// Images of the batch's token vectors (the gate/up input): one wave per token.
-template <int G>
-__global__ __launch_bounds__(kThreads) void k_mimg_prep(MfmaArgs a) {
-  const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const float sc = image_row<G, kMfmaMaxH / 512>(a.x + (int64_t)t * a.H, a.H,
-                                                 a.ximg + (int64_t)t * (a.H / 8), nullptr);
-  if ((threadIdx.x & (kWave - 1)) == 0) a.xsc[t] = sc;
-}
-
 // Weights of one 32-bit code word (8 codes, in the nibble-mask order) as the
 // B operand's 8 halves: q exactly (1024 + q minus 1024), then q s + b.
 __device__ __forceinline__ f16x8 weights_f16x8(uint32_t w, f16x2 s2, f16x2 b2) {

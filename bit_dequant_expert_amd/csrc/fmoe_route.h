@@ -11,7 +11,8 @@
 //                   of the hidden dim (its 4 waves split the slice again and
 //                   add in a fixed order through LDS); partial sums per slice
 //                   go to the workspace.  Extra workgroups prepare the
-//                   activations of the gate/up products.
+//                   activations of the gate/up products (GEMV form, or the
+//                   matrix-core images: one wave per token).
 //   k_route_select  one workgroup per token: adds the slices in a fixed
 //                   order, picks the top k (larger logit first, lower index on
 //                   ties), the softmax weights over the selection and the
@@ -20,7 +21,7 @@
 //                   scatter) for the expert kernels.
 #pragma once
 
-#include "fmoe_fused.h"   // wave_max_u32 (and the common kernels)
+#include "fmoe_mfma.h"    // image_row, wave_max_u32 (and the common kernels)
 
 namespace fmoe {
 
@@ -32,6 +33,15 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   const int nrt = (a.rows + 15) / 16, ntp = (a.T + 31) / 32;
   const int nlog = nrt * ntp * a.ksplit;
 
+  if ((int)blockIdx.x >= nlog + a.n_prep_wgs) {
+    // ---- matrix-core images of the tokens (one wave per token)
+    const int t = ((int)blockIdx.x - nlog - a.n_prep_wgs) * (kThreads / kWave) + wave;
+    if (!a.ximg || t >= a.T) return;
+    const float sc = image_row<64, kMfmaMaxH / 512>(a.x + (int64_t)t * a.H, a.H,
+                                                    a.ximg + (int64_t)t * (a.H / 8), nullptr);
+    if (lane == 0) a.xsc[t] = sc;
+    return;
+  }
   if ((int)blockIdx.x >= nlog) {
     // ---- activation prep for the gate/up products (independent of routing)
     if (!a.xprep) return;
