@@ -171,11 +171,12 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   const int nrb = N / 64;
   const int ai = blockIdx.x / nrb, rb = blockIdx.x - ai * nrb;
   const ActView av{a.act, a.maxA};
-  if (ai >= av.base[0]) return;
-  const int cnt = av.cnt()[ai];
-  if (cnt < a.mfma_thr) return;
+  // The list header and this workgroup's entry in one round trip (ai < maxA:
+  // the entry is inside the list even when it is not in use).
+  const int nact = av.base[0], cnt = av.cnt()[ai];
   const int64_t e = av.e()[ai];
   const int eoff = av.off()[ai];
+  if (ai >= nact || cnt < a.mfma_thr) return;
   const uint8_t* base = a.src.base + e * a.src.stride;
   const int tid = tid_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
