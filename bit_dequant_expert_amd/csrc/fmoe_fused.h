@@ -273,14 +273,21 @@ __device__ __forceinline__ void topk_select(const FusedArgs& a, const double (&l
     const bool c = lane < nc;
     const uint64_t ck = c ? tc.key[lane] : 0ull;
     const int ce = c ? tc.idx[lane] : 0x7FFFFFFF;
+    // All 16 candidates of a block are read before any comparison, and the
+    // comparison has no short circuit: a branch per candidate would make
+    // each LDS read a round trip of its own.
     int rank = 0;
     for (int j0 = 0; j0 < nc; j0 += 16) {
+      uint64_t kj[16];
+      int ej[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const uint64_t kj = tc.key[j0 + t];
-        const int ej = tc.idx[j0 + t];
-        rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
+        kj[t] = tc.key[j0 + t];
+        ej[t] = tc.idx[j0 + t];
       }
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        rank += (int)((kj[t] > ck) | ((kj[t] == ck) & (ej[t] < ce)));
     }
     const bool sel = c && rank < a.k;
     const int L0 = __ffsll((unsigned long long)__ballot(c && rank == 0)) - 1;
@@ -497,14 +504,12 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
   bool first = true;                      // thread 0: first item not yet taken
   bool listing = false;                   // thread 0: now taking deferred down parts
   int ndef = 0;                           // thread 0: length of the deferred list
-  // The call's epoch (stamp of the done lines), read at entry and first
-  // needed once the first loads are out.
-  const int ep_v = ld_agent(ctr_line(a_in.ctr, kDownDoneLine));
+  // The call's epoch (stamp of the done lines).  It is loaded together with
+  // x on the first item (every workgroup stages x before its first arrival,
+  // so before any done line of this call is stamped): a load of its own at
+  // entry would be a round trip ahead of the first weight loads.
   int ep = 0;
-  auto get_ep = [&]() {
-    if (ep == 0) ep = __builtin_amdgcn_readfirstlane(ep_v) + 1;
-    return ep;
-  };
+  auto get_ep = [&]() { return ep; };
   // gamma*h of the last down part of this workgroup (writer lanes) and its index
   float hy[kFusedUD];
   int last_d = -1;
@@ -653,18 +658,24 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
       // x is read only here, before this item arrives, and every h_out write
       // waits until every item has arrived, so h_out may alias x.
       if (routes || !have_x) {
+        // x (and the epoch) first: x is staged and prepared while the
+        // router rows are still streaming in.
         float4 wv[kQ];
-        if (routes) router_load(wv, item);
+        float4 xq[kQ];
+        int ep_v = 0;
         if (!have_x) {
-          float4 xq[kQ];
 #pragma unroll
           for (int q = 0; q < kQ; ++q) xq[q] = reinterpret_cast<const float4*>(a.x)[q * kThreads + tid];
+          ep_v = ld_agent(ctr_line(ctr, kDownDoneLine));
+        }
+        if (routes) router_load(wv, item);
+        if (!have_x) {
 #pragma unroll
           for (int q = 0; q < kQ; ++q) {
             reinterpret_cast<float4*>(lds_x)[q * kThreads + tid] = xq[q];
             prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
           }
-          get_ep();
+          ep = __builtin_amdgcn_readfirstlane(ep_v) + 1;
           have_x = true;
           lds_barrier();
         }
@@ -784,6 +795,9 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     down_publish(a, dpart, acc, rv, gv, hy, wrow0, geoI.RPI, geoI.lane_row,
                  geoI.lane_seg == geoI.LPR - 1, s_part, get_ep());
     last_d = dpart;
+    // Without a queue a workgroup holds one item: straight to the norm, with
+    // no drain of this part's stores and no barrier ahead of the wait.
+    if (!queued) break;
   }
 
   // RMSNorm of this workgroup's rows once every down part is in; then leave.
