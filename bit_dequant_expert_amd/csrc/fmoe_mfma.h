@@ -149,7 +149,7 @@ __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, in
 #define FMOE_MOE_PB_REG 2   // gate/up, activation words in the ring
 #endif
 #ifndef FMOE_MOE_PB_DN
-#define FMOE_MOE_PB_DN 6    // down
+#define FMOE_MOE_PB_DN 4    // down (K / 128 = 8 blocks: two whole rings)
 #endif
 
 // Workgroup (ai, rb): active expert ai (every expert with at least
@@ -354,18 +354,27 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         }
       }
       __syncthreads();
-      // Whole rings without branches (the load waits stay exact), then the rest.
+      // Whole rings without branches while a whole next ring follows (the
+      // load waits stay exact); then the ring in flight is computed while the
+      // r blocks after it, if any, are requested, and those last.  No block
+      // is requested twice.
       int bb = 0;
-      for (; bb + PB <= NBK; bb += PB) {
+      for (; bb + 2 * PB <= NBK; bb += PB) {
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
           compute(u, bb + u);
-          issue(u, min(bb + u + PB, NBK - 1));
+          issue(u, bb + u + PB);
         }
+      }
+      const int r = NBK - bb - PB;   // < 0 when the whole K is one short ring
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        if (bb + u < NBK) compute(u, bb + u);
+        if (u < r) issue(u, bb + PB + u);
       }
 #pragma unroll
       for (int u = 0; u < PB; ++u)
-        if (bb + u < NBK) compute(u, bb + u);
+        if (u < r) compute(u, bb + PB + u);
     };
     if (MODE == 1 || pc <= kMoeLdsTokens) run(std::true_type{});
     else run(std::false_type{});
