@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
   const int subq = blockIdx.x % kSubs;
   bool have_x = false;                    // LDS already holds x (fp32 and prepared)
   bool drained = false;                   // wave 0: every queue item handed out
-  bool first = true;                      // thread 0: first item not yet taken
+  bool first = true;                      // first item not yet taken
   bool listing = false;                   // thread 0: now taking deferred down parts
   int ndef = 0;                           // thread 0: length of the deferred list
   // The call's epoch (stamp of the done lines).  It is loaded together with
@@ -534,38 +534,43 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
     // Next piece of work: first item blockIdx.x, then item < n_main from the
     // queue of the items past the grid; once that is empty, n_main + d for
     // deferred down part d (after the item flag, when the list is complete);
-    // -1 when there is nothing left.  (Nothing of the last item is still in
-    // flight here; the wait says so to the compiler, which otherwise assumes
-    // loads of skipped paths pending and waits for them inside the phases.)
-    vm_drain();
-    lds_barrier();
-    if (tid == 0) {
-      int it = -1;
-      if (first) {
-        first = false;
-        it = blockIdx.x;
-        if (queued)
-          __hip_atomic_fetch_add(ctr_line(ctr, kStartLine + subq), 1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);   // result unused: no round trip
-      } else if (queued && !listing) {
-        it = (int)gridDim.x + subq + kSubs * add_agent(ctr_line(ctr, kQHeadLine + subq), 1);
-        if (it >= n_main) {
-          listing = true;
-          wait_done_thread(ctr, kItemDoneLine, n_main, get_ep());
-          ndef = ld_agent(ctr_line(ctr, kDefTailLine));
+    // -1 when there is nothing left.  The first item is blockIdx.x, known to
+    // every thread: nothing to drain or hand over.  Later ones: nothing of the
+    // last item is still in flight; the wait says so to the compiler, which
+    // otherwise assumes loads of skipped paths pending and waits for them
+    // inside the phases.
+    int item;
+    if (first) {
+      first = false;
+      item = blockIdx.x;
+      if (queued && tid == 0)
+        __hip_atomic_fetch_add(ctr_line(ctr, kStartLine + subq), 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);   // result unused: no round trip
+    } else {
+      vm_drain();
+      lds_barrier();
+      if (tid == 0) {
+        int it = -1;
+        if (queued && !listing) {
+          it = (int)gridDim.x + subq + kSubs * add_agent(ctr_line(ctr, kQHeadLine + subq), 1);
+          if (it >= n_main) {
+            listing = true;
+            wait_done_thread(ctr, kItemDoneLine, n_main, get_ep());
+            ndef = ld_agent(ctr_line(ctr, kDefTailLine));
+          }
         }
-      }
-      if (listing) {
-        it = -1;
-        if (ndef > 0) {
-          const int j = add_agent(ctr_line(ctr, kDefHeadLine), 1);
-          if (j < ndef) it = n_main + ld_agent(a.dlist + j);
+        if (listing) {
+          it = -1;
+          if (ndef > 0) {
+            const int j = add_agent(ctr_line(ctr, kDefHeadLine), 1);
+            if (j < ndef) it = n_main + ld_agent(a.dlist + j);
+          }
         }
+        s_item = it;
       }
-      s_item = it;
+      lds_barrier();
+      item = s_item;
     }
-    lds_barrier();
-    const int item = s_item;
     if (item < 0) break;
 
     // What the item holds (all workgroup-uniform): router rows item,
