@@ -151,7 +151,7 @@ bool mfma_supported(int H, int I, int bits, int group) {
 
 hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st) {
   const int N = mode == 0 ? a.I : a.H;
-  const int grid = a.maxA * (N / 64);
+  const int grid = a.maxA * (N / (mode == 0 ? kMoeGuRows : 64));
   if (grid <= 0) return hipSuccess;
   VCall c = make_call(VCall::EXPERT_MFMA, f, 1, grid, st);
   c.mf = &a;

@@ -123,6 +123,13 @@ constexpr int kMfmaTokens = 1;        // an expert with at least this many token
 constexpr int kMfmaMaxGroups = 128;   // K / G the path admits
 constexpr int kMfmaMaxI = 2048;       // down input images of a 16-token pass held in LDS
 constexpr int kMfmaMaxH = 8192;       // gate/up input images built in one pass of registers
+#ifndef FMOE_MOE_GU_SPLIT
+#define FMOE_MOE_GU_SPLIT 2
+#endif
+// Gate/up matrix-core workgroups: kMoeGuSplit waves share each 16-row tile,
+// each taking a part of K, so a workgroup covers kMoeGuRows rows.
+constexpr int kMoeGuSplit = FMOE_MOE_GU_SPLIT;
+constexpr int kMoeGuRows = 64 / kMoeGuSplit;
 constexpr int kMoeLdsTokens = 2;      // gate/up passes with at most this many tokens read A from LDS
 struct MfmaArgs {
   ExpertSrc src;

@@ -20,8 +20,10 @@
 // bytes) of its row, one 16-byte load, and feeds them to 4 MFMA steps; the
 // activation words follow the same k order.  Codes (and the gate/up
 // activation words of passes with many tokens) stream through a register
-// ring of blocks; the scales of the workgroup's 64 rows and the other
-// activation images sit in LDS.
+// ring of blocks; the scales of the workgroup's rows and the other
+// activation images sit in LDS.  Gate/up workgroups are smaller (64 /
+// kMoeGuSplit rows, kMoeGuSplit waves splitting K per 16-row tile), so that
+// the last of the many workgroups a layer needs leave fewer compute units idle.
 #pragma once
 
 #include <type_traits>
@@ -129,14 +131,19 @@ __device__ __forceinline__ f16x8 weights_f16x8(uint32_t w, f16x2 s2, f16x2 b2) {
   return __builtin_bit_cast(f16x8, make_uint4(p[0], p[1], p[2], p[3]));
 }
 
-// LDS of k_moe_mfma: scales and biases of the workgroup's 64 rows
-// ([NM][2][64] rows of NG*SB bytes, padded by 4), then the images of the
-// pass's inputs that are read from LDS ([kMoeLdsTokens or 16][K/8 + 1] words).
+// LDS of k_moe_mfma: scales and biases of the workgroup's RW rows
+// ([NM][2][RW] rows of NG*SB bytes, padded by 4), then the images of the
+// pass's inputs that are read from LDS ([kMoeLdsTokens or 16][K/8 + 1] words),
+// an area that gate/up reuses for the sums of its waves' K shares.
 __host__ __device__ inline int moe_scl_row(int K, int G, int SB) { return (K / G) * SB + 4; }
 __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, int SB) {
   const int nm = mode == 0 ? 2 : 1, K = mode == 0 ? H : I;
-  const size_t scl = ((size_t)nm * 2 * 64 * moe_scl_row(K, G, SB) + 15) / 16 * 16;
-  return scl + (size_t)(mode == 0 ? kMoeLdsTokens : 16) * (K / 8 + 1) * 16;
+  const int rw = mode == 0 ? kMoeGuRows : 64;
+  const size_t scl = ((size_t)nm * 2 * rw * moe_scl_row(K, G, SB) + 15) / 16 * 16;
+  const size_t img = (size_t)(mode == 0 ? kMoeLdsTokens : 16) * (K / 8 + 1) * 16;
+  const size_t red =
+      mode == 0 ? (size_t)(kThreads / kWave / kMoeGuSplit) * (kMoeGuSplit - 1) * nm * kWave * 16 : 0;
+  return scl + (img > red ? img : red);
 }
 
 // Blocks of 128 k a wave keeps in flight.  A ring slot holds the lane's 16
@@ -153,11 +160,13 @@ __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, in
 #endif
 
 // Workgroup (ai, rb): active expert ai (every expert with at least
-// a.mfma_thr tokens), rows 64 rb .. 64 rb + 63 (N % 64 == 0), wave w the tile
-// of 16 rows 64 rb + 16 w.  MODE 0: gate and up (K = H) with SwiGLU into abuf;
-// the activation words come from the token images in LDS when the pass has
-// at most kMoeLdsTokens tokens, else from global memory through the register
-// ring.  MODE 1: down (K = I) into yslot, the images of the pass's SwiGLU
+// a.mfma_thr tokens).  MODE 0: rows RW rb .. RW rb + RW - 1 (RW = kMoeGuRows),
+// wave w the tile of 16 rows RW rb + 16 (w / S) over its part w % S of the
+// blocks of K (S = kMoeGuSplit), the S partial tiles added in wave order; gate
+// and up (K = H) with SwiGLU into abuf; the activation words come from the
+// token images in LDS when the pass has at most kMoeLdsTokens tokens, else
+// from global memory through the register ring.  MODE 1 rows: 64 rb .. 64 rb
+// + 63 (N % 64 == 0), wave w the tile of 16 rows 64 rb + 16 w, all of K.  MODE 1: down (K = I) into yslot, the images of the pass's SwiGLU
 // rows built in LDS first.  Lane l: B column (weight row) l % 16, A row
 // (token) l % 16, k sub-block l / 16; D element i is token 4 (l / 16) + i,
 // weight row l % 16.  Needs K % 128 == 0.
@@ -167,8 +176,12 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   extern __shared__ __align__(16) uint4 lds4[];
   __shared__ float s_sc[16];
   __shared__ int s_ent[16];
+  // Gate/up: kMoeGuRows rows per workgroup, S waves per 16-row tile, each
+  // over a part of K; down: 64 rows, a wave's 16 rows over the whole K.
+  constexpr int S = MODE == 0 ? kMoeGuSplit : 1;
+  constexpr int RW = 64 / S;   // rows per workgroup
   const int N = MODE == 0 ? a.I : a.H, K = MODE == 0 ? a.H : a.I;
-  const int nrb = N / 64;
+  const int nrb = N / RW;
   const int ai = blockIdx.x / nrb, rb = blockIdx.x - ai * nrb;
   const ActView av{a.act, a.maxA};
   // The list header and this workgroup's entry in one round trip (ai < maxA:
@@ -180,27 +193,32 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   const uint8_t* base = a.src.base + e * a.src.stride;
   const int tid = tid_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = rb * 64 + wave * 16 + (lane & 15);
+  const int tile = wave / S, part = wave - tile * S;   // 16-row tile, part of K
+  const int n = rb * RW + tile * 16 + (lane & 15);
   const int jg = lane >> 4, am = lane & 15;
-  const int NG = K / G, NW = K / 8, NBK = K / 128;
+  const int NG = K / G, NW = K / 8;
+  // The wave's blocks of 128 k: [kb0, kb0 + NBK), its part of K (empty for
+  // some waves when K has fewer than S blocks).
+  const int kb0 = (part * (K / 128)) / S;
+  const int NBK = ((part + 1) * (K / 128)) / S - kb0;
   const int SROW = moe_scl_row(K, G, SB);
-  const int nl = wave * 16 + (lane & 15);       // row within the workgroup's 64
+  const int nl = tile * 16 + (lane & 15);   // row within the workgroup's
   const int om = MODE == 0 ? 0 : 6;
   uint8_t* s_scl = reinterpret_cast<uint8_t*>(lds4);
-  uint4* s_img = reinterpret_cast<uint4*>(s_scl + ((size_t)NM * 2 * 64 * SROW + 15) / 16 * 16);
+  uint4* s_img = reinterpret_cast<uint4*>(s_scl + ((size_t)NM * 2 * RW * SROW + 15) / 16 * 16);
 
-  // Scales and biases of rows rb*64 .. +63: contiguous in the slab, copied
+  // Scales and biases of the workgroup's RW rows: contiguous in the slab, copied
   // into padded LDS rows.  When they fit in kSR 16-byte words per thread they
   // are loaded into registers first and stored later (scales_load,
   // scales_store), else copied in one loop (stage_scales).
   constexpr int kSR = 1;
   const int rowb = NG * SB;
-  const int sper = 64 * rowb / 16, stot = 2 * NM * sper;
+  const int sper = RW * rowb / 16, stot = 2 * NM * sper;
   // (Down only: gate/up has no registers to spare for it.)
   const bool sfast = MODE == 1 && rowb % 16 == 0 && stot <= kSR * kThreads;   // uniform
   uint4 sreg[kSR];
   auto scl_src = [&](int arr) {
-    return base + a.src.off[om + 3 * (arr >> 1) + 1 + (arr & 1)] + (int64_t)rb * 64 * rowb;
+    return base + a.src.off[om + 3 * (arr >> 1) + 1 + (arr & 1)] + (int64_t)rb * RW * rowb;
   };
   auto scales_load = [&]() {
 #pragma unroll
@@ -217,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
       if (i < stot) {
         const int arr = i / sper, k = i - arr * sper;
         const int r = (k * 16) / rowb, c = k * 16 - r * rowb;
-        uint32_t* d = reinterpret_cast<uint32_t*>(s_scl + (size_t)arr * 64 * SROW + r * SROW + c);
+        uint32_t* d = reinterpret_cast<uint32_t*>(s_scl + (size_t)arr * RW * SROW + r * SROW + c);
         d[0] = sreg[j].x; d[1] = sreg[j].y; d[2] = sreg[j].z; d[3] = sreg[j].w;
       }
     }
@@ -226,17 +244,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
 #pragma unroll
     for (int arr = 0; arr < 2 * NM; ++arr) {
       const uint8_t* src = base + a.src.off[om + 3 * (arr >> 1) + 1 + (arr & 1)] +
-                           (int64_t)rb * 64 * rowb;
-      uint8_t* dst = s_scl + (size_t)arr * 64 * SROW;
+                           (int64_t)rb * RW * rowb;
+      uint8_t* dst = s_scl + (size_t)arr * RW * SROW;
       if (rowb % 16 == 0) {
-        for (int i = tid; i < 64 * rowb / 16; i += kThreads) {
+        for (int i = tid; i < RW * rowb / 16; i += kThreads) {
           const uint4 v = reinterpret_cast<const uint4*>(src)[i];
           const int r = (i * 16) / rowb, c = (i * 16) - r * rowb;
           uint32_t* d = reinterpret_cast<uint32_t*>(dst + r * SROW + c);
           d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
         }
       } else {
-        for (int i = tid; i < 64 * rowb / 4; i += kThreads) {
+        for (int i = tid; i < RW * rowb / 4; i += kThreads) {
           const uint32_t v = reinterpret_cast<const uint32_t*>(src)[i];
           const int r = (i * 4) / rowb, c = (i * 4) - r * rowb;
           *reinterpret_cast<uint32_t*>(dst + r * SROW + c) = v;
@@ -246,10 +264,11 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   };
   // Addresses: the wave's first row as a wave-uniform base (SGPRs) and one
   // 32-bit offset per lane, so that a ring slot costs no address registers.
-  const int64_t row0 = (int64_t)rb * 64 + wave * 16;
+  const int64_t row0 = (int64_t)rb * RW + tile * 16;
   const uint8_t* qm[NM];
 #pragma unroll
-  for (int mi = 0; mi < NM; ++mi) qm[mi] = uniform_gptr(base + a.src.off[om + 3 * mi] + row0 * (K / 2));
+  for (int mi = 0; mi < NM; ++mi)
+    qm[mi] = uniform_gptr(base + a.src.off[om + 3 * mi] + row0 * (K / 2) + kb0 * 64);
   const uint32_t lq = (uint32_t)(lane & 15) * (uint32_t)(K / 2) + (uint32_t)jg * 16u;
 
   for (int c0 = 0; c0 < cnt; c0 += 16) {
@@ -274,8 +293,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
       constexpr bool AL = decltype(al_c)::value;          // activation words from LDS
       constexpr int PB = MODE == 1 ? FMOE_MOE_PB_DN : (AL ? FMOE_MOE_PB_GU : FMOE_MOE_PB_REG);
       constexpr int NXW = AL ? 1 : 4;
-      const uint4* xrow = a.ximg + (int64_t)(MODE == 0 ? s_ent[ar] / a.kp1 : 0) * NW + jg * 4;
-      const uint4* lrow = s_img + ar * (NW + 1) + jg * 4;
+      const uint4* xrow = a.ximg + (int64_t)(MODE == 0 ? s_ent[ar] / a.kp1 : 0) * NW + kb0 * 16 + jg * 4;
+      const uint4* lrow = s_img + ar * (NW + 1) + kb0 * 16 + jg * 4;
       uint4 rq[PB][NM], rx[PB][NXW];
       auto issue = [&](int u, int b) {
 #pragma unroll
@@ -290,11 +309,11 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         uint4 xw[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) xw[s] = AL ? lrow[b * 16 + s] : rx[u][s % NXW];
-        const int gi = (b * 128 + jg * 32) / G;
+        const int gi = ((kb0 + b) * 128 + jg * 32) / G;
 #pragma unroll
         for (int mi = 0; mi < NM; ++mi) {
-          const uint8_t* sr = s_scl + ((size_t)(2 * mi) * 64 + nl) * SROW + gi * SB;
-          const uint8_t* br = s_scl + ((size_t)(2 * mi + 1) * 64 + nl) * SROW + gi * SB;
+          const uint8_t* sr = s_scl + ((size_t)(2 * mi) * RW + nl) * SROW + gi * SB;
+          const uint8_t* br = s_scl + ((size_t)(2 * mi + 1) * RW + nl) * SROW + gi * SB;
           const float sv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(sr))
                                    : *reinterpret_cast<const float*>(sr);
           const float bv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(br))
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         }
       }
 #pragma unroll
-      for (int u = 0; u < PB; ++u) issue(u, min(u, NBK - 1));
+      for (int u = 0; u < PB; ++u) issue(u, max(0, min(u, NBK - 1)));
       if (stage_s && sfast) scales_store();
       else if (stage_s) stage_scales();
       if (MODE == 1) {
@@ -378,6 +397,28 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
     };
     if (MODE == 1 || pc <= kMoeLdsTokens) run(std::true_type{});
     else run(std::false_type{});
+
+    if constexpr (S > 1) {
+      // The parts of K of a tile are added in part order through LDS (the
+      // image area, free once every wave is past its products); the part-0
+      // wave keeps the sums and stores.
+      f32x4* s_red = reinterpret_cast<f32x4*>(s_img);
+      __syncthreads();
+      if (part > 0) {
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi)
+          s_red[((tile * (S - 1) + part - 1) * NM + mi) * kWave + lane] = acc[mi];
+      }
+      __syncthreads();
+      if (part > 0) continue;
+#pragma unroll
+      for (int j = 1; j < S; ++j)
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+          const f32x4 v = s_red[((tile * (S - 1) + j - 1) * NM + mi) * kWave + lane];
+          acc[mi] = f32x4{acc[mi][0] + v[0], acc[mi][1] + v[1], acc[mi][2] + v[2], acc[mi][3] + v[3]};
+        }
+    }
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
