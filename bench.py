@@ -80,11 +80,18 @@ def layer_bytes(cfg):
 
 
 def source_hash():
+    """Hash of the kernel sources with comments and white space removed, so
+    that a profile stays matched to code whose comments were edited since."""
+    import re
     h = hashlib.sha256()
     d = os.path.join(ROOT, "bit_dequant_expert_amd", "csrc")
     for name in sorted(os.listdir(d)):
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(d, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = re.sub(r"\s+", " ", text).strip()
+        h.update(name.encode() + text.encode())
     return h.hexdigest()[:16]
 
 

@@ -32,14 +32,15 @@
 // each gate/up part then finishes without waiting on any down part.
 // Otherwise (fewer resident workgroups than items) it defers its down part to
 // a list worked off once the queue is empty; the flag counts every item's
-// decision, so after it the list is complete.  The last down part computes
-// the RMSNorm; the last workgroup to leave resets counters and flags.
+// decision, so after it the list is complete.  Each down part publishes the
+// sum of squares of its rows; once all are in, every workgroup scales its own
+// rows (RMSNorm).  With a queue, the last workgroup to leave resets it.
 //
 // Hardware facts this layout answers (measured on MI355X): atomics on one
 // address serialise at ~11 ns each (far slower while HBM is saturated), so
-// every counter is split into 64 sub-counters plus a top counter, each on its
-// own 256-byte line, and phase completion is broadcast through 64 flags on
-// separate lines (each waiting workgroup polls its own).  A wave's loads
+// every phase counter is split into 64 sub-counters, each on its own 256-byte
+// line, and phase completion is a done line of 64 words (one per sub-counter)
+// kept in 8 copies, so that few workgroups poll each copy.  A wave's loads
 // complete in issue order, so a small load the critical path needs is never
 // issued behind bulk loads it does not need (the down tiles go out after the
 // gate/up part is published).  A load whose data is used at once behind a
