@@ -185,8 +185,8 @@ size_t route_ws(int T, int E) {
   return fmoe::kWsReserved + align256((size_t)fmoe::route_ksplit(T, E) * T * E * 8);
 }
 
-// FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers (debug and
-// cross-checking only).
+// FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers and the
+// two-launch single-expert FFN (debug and cross-checking only).
 // FMOE_NO_MFMA=1 keeps every expert of a batch on the multi-token GEMV path
 // (cross-checking only).  FMOE_MFMA_MIN_TOKENS=n sends only experts with at
 // least n tokens of the batch to the matrix cores and the rest to the GEMV
@@ -206,6 +206,7 @@ bool fused_disabled() {
   const char* v = getenv("FMOE_NO_FUSED");
   return v && v[0] == '1';
 }
+bool expert1_enabled() { return !fused_disabled(); }
 
 fmoe_status check_router(int T, int H, int E, int k) {
   if (T < 0) return fail(FMOE_ERR_SHAPE, "T=%d must be >= 0", T);
@@ -319,9 +320,19 @@ fmoe_status fmoe_expert_ffn(const fmoe_expert* e, const fmoe_qformat* fmt, const
   uint8_t* wsb = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
 
-  // Two launches: gate and up with SwiGLU into the workspace, then down.
+  // One launch when the shape and the resident workgroups admit it (the
+  // SwiGLU image in abuf); else two: gate and up with SwiGLU into the
+  // workspace, then down.
   float* abuf = (float*)(wsb + L.abuf);
-  hipError_t he = fmoe::launch_gemv_swiglu(
+  fmoe::Expert1Args ea{};
+  ea.gq = (const uint8_t*)e->gate.q; ea.gs = (const uint8_t*)e->gate.scale; ea.gb = (const uint8_t*)e->gate.bias;
+  ea.uq = (const uint8_t*)e->up.q; ea.us = (const uint8_t*)e->up.scale; ea.ub = (const uint8_t*)e->up.bias;
+  ea.dq = (const uint8_t*)e->down.q; ea.ds = (const uint8_t*)e->down.scale; ea.db = (const uint8_t*)e->down.bias;
+  ea.x = x; ea.y = y; ea.img = (uint8_t*)abuf; ea.ctr = (int*)(wsb + L.ctr); ea.H = H; ea.I = I;
+  hipError_t he = expert1_enabled() ? fmoe::launch_expert1(f, ea, s) : hipErrorNotSupported;
+  if (he == hipSuccess) return FMOE_OK;
+  if (he != hipErrorNotSupported) return hip_fail(he, "expert kernel");
+  he = fmoe::launch_gemv_swiglu(
       f, (const uint8_t*)e->gate.q, (const uint8_t*)e->gate.scale, (const uint8_t*)e->gate.bias,
       (const uint8_t*)e->up.q, (const uint8_t*)e->up.scale, (const uint8_t*)e->up.bias, I, H, x,
       abuf, s);

@@ -170,6 +170,42 @@ bool fused1_supported(int H, int I, int E, int bits) {
   return (H + dr - 1) / dr <= kFusedMaxNormParts;
 }
 
+hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st) {
+  const int H = a.H, I = a.I, bits = f.bits;
+  const int sh = H * bits / 128, si = I * bits / 128;
+  const int gr = fused_gu_rows(H, bits), dr = fused_d_rows(I, bits);
+  if (!((sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64) && I % gr == 0 &&
+        gr % (32 / bits) == 0 && gr <= kWave && H % dr == 0 &&
+        wimg_bytes(I, bits) <= (int64_t)kFusedImgPer * kThreads * 8))
+    return hipErrorNotSupported;
+  a.gu_rows = gr;
+  a.d_rows = dr;
+  a.nGU = I / gr;
+  a.nD = H / dr;
+  const int grid = a.nGU > a.nD ? a.nGU : a.nD;
+  const size_t lds = expert1_lds_bytes(H, I, bits);
+  const int ns = segs_per_lane(H, bits);
+  int occ = 0;
+  if (bits == 4 && f.group == 32) occ = expert1_occupancy_4_32(f.sb, ns, lds);
+  if (bits == 4 && f.group == 64) occ = expert1_occupancy_4_64(f.sb, ns, lds);
+  if (bits == 2 && f.group == 32) occ = expert1_occupancy_2_32(f.sb, ns, lds);
+  if (bits == 2 && f.group == 64) occ = expert1_occupancy_2_64(f.sb, ns, lds);
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu < 1)
+      n_cu = 1;
+  }
+  // Every workgroup waits for all the others' arrivals: all must be resident.
+  if (grid > occ * n_cu) return hipErrorNotSupported;
+  VCall c = make_call(VCall::EXPERT1, f, ns, grid, st);
+  c.ex = &a;
+  c.lds = lds;
+  return run_variant(c);
+}
+
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
   if (!fused1_supported(a.H, a.I, a.E, f.bits)) return hipErrorNotSupported;
   const size_t lds = fused_lds_bytes(a.H, a.I, f.bits);

@@ -846,4 +846,101 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
   }
 }
 
+// ------------------------------------------------------------ one expert
+// The single-expert FFN y = down . (silu(gate . x) * (up . x)) in one launch
+// ([WAS] "3. Handoptimierte Metal Compute-Shader": gate/up with SwiGLU, then
+// down).  Workgroup b: gate/up part b (rows b*gu_rows .. of gate and up, for
+// b < nGU), published as a word-blocked SwiGLU image; then down part b (rows
+// b*d_rows .., for b < nD), whose tiles are requested and converted before
+// the wait for the image.  Every workgroup arrives once (after its gate/up
+// part, if any), so the done line also says that every workgroup has read
+// the call's epoch.  The counter lines are this kernel's own: its epochs never
+// mix with the layer kernel's on a shared workspace.  The launcher admits
+// grids whose workgroups are all resident at once.
+constexpr int kExpSubLine = kDownDoneLine + kDoneCopies;   // kSubs sub-counters
+constexpr int kExpDoneLine = kExpSubLine + kSubs;          // kDoneCopies lines
+static_assert(kExpDoneLine + kDoneCopies <= kFusedCtrLines, "counter block too small");
+
+inline size_t expert1_lds_bytes(int H, int I, int bits) {
+  return (size_t)xprep_bytes(H) + (size_t)wimg_bytes(I, bits);
+}
+
+template <int BITS, int G, int SB, int NSH>
+__global__ __launch_bounds__(kThreads) void k_expert1(Expert1Args a) {
+  extern __shared__ __align__(16) uint8_t lds[];   // [x prepared | SwiGLU image]
+  __shared__ float s_act[kWave];
+  using TileH = Tile<BITS, G, SB, NSH>;
+  using TileI = Tile<BITS, G, SB, 1>;
+  constexpr int kUG = fused_ug(NSH);
+  constexpr int kQ = 8 * NSH / BITS;   // float4 of x per thread
+  const int tid = tid_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x;
+  const RowGeo geoH(a.H, BITS), geoI(a.I, BITS);
+  uint8_t* lds_xp = lds;
+  uint8_t* lds_ap = lds + xprep_bytes(a.H);
+  int* ctr = a.ctr;
+  int ep;
+  if (b < a.nGU) {   // workgroup-uniform
+    // x first (it is staged while the tiles stream in), then the tiles.
+    float4 xq[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) xq[q] = reinterpret_cast<const float4*>(a.x)[q * kThreads + tid];
+    TileH tg[kUG], tu[kUG];
+    const int n0 = b * a.gu_rows + wave * kUG;
+#pragma unroll
+    for (int u = 0; u < kUG; ++u) {
+      tg[u].load(a.gq, a.gs, a.gb, a.H, n0 + u, geoH);
+      tu[u].load(a.uq, a.us, a.ub, a.H, n0 + u, geoH);
+    }
+    const int ep_v = ld_agent(ctr_line(ctr, kExpDoneLine));
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
+    lds_barrier();
+    XRegs<BITS, NSH> xr;
+    xr.load(lds_xp, a.H, geoH);
+#pragma unroll
+    for (int u = 0; u < kUG; ++u) {
+      const float gs = sum_lanes(tile_dot(tg[u], xr), kWave);
+      const float us = sum_lanes(tile_dot(tu[u], xr), kWave);
+      if (lane == kWave - 1) s_act[wave * kUG + u] = silu(gs) * us;
+    }
+    lds_barrier();
+    if (wave == 0) {   // the part's rows are whole code-word blocks of the image
+      const bool live = lane < a.gu_rows;
+      wimg_publish<BITS>(s_act[live ? lane : 0], live, a.img, a.I, b * a.gu_rows + lane);
+    }
+    ep = __builtin_amdgcn_readfirstlane(ep_v) + 1;
+  } else {
+    ep = __builtin_amdgcn_readfirstlane(ld_agent(ctr_line(ctr, kExpDoneLine))) + 1;
+  }
+  // Arrival (wave 0's image stores drained first).
+  if (wave == 0) vm_drain();
+  lds_barrier();
+  if (tid == 0) arrive_done(ctr, kExpSubLine, kExpDoneLine, b, (int)gridDim.x, ep);
+  if (b >= a.nD) return;   // workgroup-uniform
+  const int m = b * a.d_rows + wave * geoI.RPI + geoI.lane_row;
+  TileI tl;
+  tl.load(a.dq, a.ds, a.db, a.I, m, geoI);
+  float v;
+  auto finish = [&](const auto& t) {
+    if (wave == 0) wait_done(ctr, kExpDoneLine, (int)gridDim.x, ep);
+    lds_barrier();
+    copy_wimgs_to_lds_agent<BITS, kThreads, 1, kFusedImgPer>(
+        reinterpret_cast<uint64_t*>(lds_ap), reinterpret_cast<const uint64_t*>(a.img), a.I, 1);
+    lds_barrier();
+    XRegsW<BITS> xw;
+    xw.load(lds_ap, a.I, geoI);
+    v = sum_lanes(tile_dot_w(t, xw), geoI.LPR);
+  };
+  if constexpr (BITS == 4) {
+    TileDq4<G, SB> tq;   // fp16 pairs before the wait: only the dot2s remain after it
+    tq.from(tl);
+    finish(tq);
+  } else {
+    finish(tl);
+  }
+  if (geoI.lane_seg == geoI.LPR - 1) a.y[m] = v;
+}
+
 }  // namespace fmoe

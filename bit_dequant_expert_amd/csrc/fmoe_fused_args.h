@@ -59,4 +59,18 @@ struct FusedArgs {
   int d_rows;        // down rows per part
 };
 
+// Arguments of the one-launch single-expert FFN.
+struct Expert1Args {
+  const uint8_t *gq, *gs, *gb;   // gate [I x H]: codes, scales, biases
+  const uint8_t *uq, *us, *ub;   // up   [I x H]
+  const uint8_t *dq, *ds, *db;   // down [H x I]
+  const float* x;                // [H]
+  float* y;                      // [H]
+  uint8_t* img;                  // wimg_bytes(I, bits): the SwiGLU output
+  int* ctr;                      // counter block (kFusedCtrBytes)
+  int H, I;
+  int nGU, gu_rows;              // gate/up parts and their rows
+  int nD, d_rows;                // down parts and their rows
+};
+
 }  // namespace fmoe

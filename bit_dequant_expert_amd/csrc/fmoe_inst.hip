@@ -100,6 +100,14 @@ hipError_t run_one(const VCall& c) {
       }
       break;
     }
+    case VCall::EXPERT1: {
+      if constexpr (NS > 2) {
+        return hipErrorNotSupported;
+      } else {
+        hipLaunchKernelGGL((k_expert1<B, G, SB, NS>), dim3(c.grid), dim3(kThreads), c.lds, c.st, *c.ex);
+      }
+      break;
+    }
     default:
       return hipErrorInvalidValue;
   }
@@ -121,7 +129,30 @@ int fused_occupancy(size_t lds) {
   return cached;
 }
 
+// Resident workgroups of the one-launch expert kernel per CU.
+template <int SB, int NS>
+int expert1_occupancy(size_t lds) {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&k_expert1<FMOE_BITS, FMOE_GROUP, SB, NS>), kThreads,
+            lds) != hipSuccess || n < 1)
+      n = 0;
+    cached = n;
+  }
+  return cached;
+}
+
 }  // namespace
+
+int FMOE_CAT(expert1_occupancy_, FMOE_BITS, FMOE_GROUP)(int sb, int ns, size_t lds) {
+  if (sb == 4 && ns == 1) return expert1_occupancy<4, 1>(lds);
+  if (sb == 4 && ns == 2) return expert1_occupancy<4, 2>(lds);
+  if (sb == 2 && ns == 1) return expert1_occupancy<2, 1>(lds);
+  if (sb == 2 && ns == 2) return expert1_occupancy<2, 2>(lds);
+  return 0;
+}
 
 int FMOE_CAT(fused_occupancy_, FMOE_BITS, FMOE_GROUP)(int sb, int ns, int E, size_t lds) {
   if (sb == 4 && ns == 1) return E <= 512 ? fused_occupancy<4, 1, 8>(lds) : fused_occupancy<4, 1, 32>(lds);

@@ -161,7 +161,7 @@ inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane re
 // One launch of a format-templated kernel; run_variant_<bits>_<group> (one
 // translation unit per pair, compiled in parallel) instantiates the kernels.
 struct VCall {
-  enum Kind { GEMV, GEMV_SWIGLU, GATEUP, DOWN_COMBINE, DOWN_SLOTS, EXPERT_MFMA, FUSED1 } kind;
+  enum Kind { GEMV, GEMV_SWIGLU, GATEUP, DOWN_COMBINE, DOWN_SLOTS, EXPERT_MFMA, FUSED1, EXPERT1 } kind;
   QFmt f;
   int ns;
   int grid;
@@ -176,6 +176,7 @@ struct VCall {
   const struct MfmaArgs* mf;
   int mode;
   const struct FusedArgs* fu;
+  const struct Expert1Args* ex;
   size_t lds;
 };
 hipError_t run_variant_4_32(const VCall& c);
@@ -186,6 +187,10 @@ int fused_occupancy_4_32(int sb, int ns, int E, size_t lds);
 int fused_occupancy_4_64(int sb, int ns, int E, size_t lds);
 int fused_occupancy_2_32(int sb, int ns, int E, size_t lds);
 int fused_occupancy_2_64(int sb, int ns, int E, size_t lds);
+int expert1_occupancy_4_32(int sb, int ns, size_t lds);
+int expert1_occupancy_4_64(int sb, int ns, size_t lds);
+int expert1_occupancy_2_32(int sb, int ns, size_t lds);
+int expert1_occupancy_2_64(int sb, int ns, size_t lds);
 
 hipError_t launch_gemv(QFmt f, const uint8_t* q, const uint8_t* s, const uint8_t* b, int N,
                        int K, const float* x, float* y, hipStream_t st);
@@ -207,6 +212,9 @@ hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st);
 // One-token layer in one persistent launch; returns hipErrorNotSupported when
 // the row geometry is outside what the fused kernel is instantiated for.
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st);
+// The single-expert FFN in one launch; hipErrorNotSupported when the shape
+// or the resident workgroups do not admit it (the caller then uses two).
+hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st);
 bool fused1_supported(int H, int I, int E, int bits);
 
 // Row-block sizing shared by host and launchers.  RPI = rows one wave covers

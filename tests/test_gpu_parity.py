@@ -345,6 +345,70 @@ def layer2():
     return GpuLayer(synth.CONFIGS["layer2"], random_gamma=False)
 
 
+def _expert_of(gl, e):
+    """fmoe_expert over expert e's slab of a GPU layer (device pointers)."""
+    off, _ = gl.cfg.spec.layout()
+    base = gl.slabs.data_ptr() + e * gl.stride
+    mats = [fm.qmat(base + off[3 * m], base + off[3 * m + 1], base + off[3 * m + 2], n, k)
+            for m, (n, k) in enumerate(gl.cfg.spec.mats())]
+    return fm.fmoe_expert(*mats)
+
+
+def test_expert_ffn_and_layer_share_workspace(layer4):
+    """The one-launch expert FFN and the one-token layer keep separate counters
+    and epochs: calls of both, interleaved on one workspace, each give the
+    same bits as on a workspace of their own, and the expert FFN matches the
+    oracle."""
+    cfg = layer4.cfg
+    e = _expert_of(layer4, 11)
+    xe = synth.normal(42, 3, 7, (cfg.H,))
+    xl = synth.activations(cfg, 1, pool=1)
+    rl = synth.activations(cfg, 2, pool=1)[1:2]   # another token as the residual
+    wsz = max(fm.fmoe_expert_ffn_workspace_size(e, layer4.fmt), fm.fmoe_workspace_size(layer4.L, 1))
+    shared = torch.zeros(wsz, dtype=torch.uint8, device="cuda")
+
+    def ffn(ws):
+        y = torch.empty(cfg.H, device="cuda")
+        fm.fmoe_expert_ffn(e, layer4.fmt, dev(xe), y, ws)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+
+    own_e = ffn(torch.zeros(wsz, dtype=torch.uint8, device="cuda"))
+    own_l = layer4.forward(xl, rl, ws=torch.zeros(wsz, dtype=torch.uint8, device="cuda"))
+    for rep in range(3):
+        note(f"shared workspace round {rep}")
+        got_e = ffn(shared)
+        got_l = layer4.forward(xl, rl, ws=shared)
+        assert np.array_equal(got_e, own_e)
+        for k in ("h", "y", "idx", "w"):
+            assert np.array_equal(got_l[k], own_l[k]), k
+    ref = oracle.expert_ffn(layer4.slab_host(11), cfg.H, cfg.I, cfg.spec.bits, cfg.spec.group,
+                            cfg.spec.sbytes, xe.astype(np.float64))
+    assert rel_l2(own_e, ref) <= TOL
+
+
+def test_expert_ffn_one_and_two_launches_agree(layer4, monkeypatch):
+    """The one-launch expert FFN and the two-launch form (FMOE_NO_FUSED=1) agree
+    within the tolerance, and each matches the oracle."""
+    cfg = layer4.cfg
+    e = _expert_of(layer4, 200)
+    x = synth.normal(42, 4, 7, (cfg.H,))
+    ref = oracle.expert_ffn(layer4.slab_host(200), cfg.H, cfg.I, cfg.spec.bits, cfg.spec.group,
+                            cfg.spec.sbytes, x.astype(np.float64))
+    outs = []
+    for flag in ("0", "1"):
+        monkeypatch.setenv("FMOE_NO_FUSED", flag)
+        ws = torch.zeros(fm.fmoe_expert_ffn_workspace_size(e, layer4.fmt), dtype=torch.uint8,
+                         device="cuda")
+        y = torch.empty(cfg.H, device="cuda")
+        fm.fmoe_expert_ffn(e, layer4.fmt, dev(x), y, ws)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+        assert rel_l2(outs[-1], ref) <= TOL, flag
+    monkeypatch.delenv("FMOE_NO_FUSED")
+    assert rel_l2(outs[0], outs[1].astype(np.float64)) <= TOL
+
+
 def test_layer4_single_token(layer4):
     cfg = layer4.cfg
     x = synth.activations(cfg, 6, pool=1)
