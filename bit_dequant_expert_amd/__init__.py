@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "FMOE_OK", 1: "FMOE_ERR_NULL", 2: "FMOE_ERR_SHAPE", 3: "FMOE_
 ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_route_topk",
                "fmoe_route_workspace_size", "fmoe_dequant_gemv", "fmoe_expert_ffn",
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
-               "fmoe_workspace_size")
+               "fmoe_workspace_size", "fmoe_wait_timeout_offset")
 
 
 class FmoeError(RuntimeError):
@@ -73,6 +73,7 @@ def lib() -> C.CDLL:
         P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
         L.fmoe_abi_version.argtypes, L.fmoe_abi_version.restype = [], i32
         L.fmoe_last_error.argtypes, L.fmoe_last_error.restype = [], C.c_char_p
+        L.fmoe_wait_timeout_offset.argtypes, L.fmoe_wait_timeout_offset.restype = [], sz
         L.fmoe_slab_layout.argtypes = [i32, i32, C.POINTER(fmoe_qformat), C.POINTER(C.c_int64)]
         L.fmoe_slab_layout.restype = i64
         L.fmoe_route_topk.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, sz, P]

@@ -229,6 +229,8 @@ int32_t fmoe_abi_version(void) { return FMOE_ABI_VERSION; }
 
 const char* fmoe_last_error(void) { return g_err; }
 
+size_t fmoe_wait_timeout_offset(void) { return fmoe::wait_timeout_offset(); }
+
 int64_t fmoe_slab_layout(int32_t hidden, int32_t inter, const fmoe_qformat* fmt, int64_t off[9]) {
   QFmt f;
   if (check_fmt(fmt, &f) != FMOE_OK) return -1;

@@ -170,6 +170,8 @@ bool fused1_supported(int H, int I, int E, int bits) {
   return (H + dr - 1) / dr <= kFusedMaxNormParts;
 }
 
+size_t wait_timeout_offset() { return (size_t)kTimeoutLine * kLine * sizeof(int); }
+
 hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st) {
   const int H = a.H, I = a.I, bits = f.bits;
   const int sh = H * bits / 128, si = I * bits / 128;
@@ -183,6 +185,7 @@ hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st) {
   a.nGU = I / gr;
   a.nD = H / dr;
   const int grid = a.nGU > a.nD ? a.nGU : a.nD;
+  if (grid < kSubs) return hipErrorNotSupported;   // the epoch needs every sub-counter in use
   const size_t lds = expert1_lds_bytes(H, I, bits);
   const int ns = segs_per_lane(H, bits);
   int occ = 0;

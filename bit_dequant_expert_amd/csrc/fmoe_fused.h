@@ -855,10 +855,13 @@ __global__ __launch_bounds__(kThreads) void k_layer1(FusedArgs a_in) {
 // b < nGU), published as a word-blocked SwiGLU image; then down part b (rows
 // b*d_rows .., for b < nD), whose tiles are requested and converted before
 // the wait for the image.  Every workgroup arrives once (after its gate/up
-// part, if any), so the done line also says that every workgroup has read
-// the call's epoch.  The counter lines are this kernel's own: its epochs never
-// mix with the layer kernel's on a shared workspace.  The launcher admits
-// grids whose workgroups are all resident at once.
+// part, if any).  The call's epoch is the stamp of the workgroup's own
+// sub-counter plus one: that word cannot change in this call before this
+// workgroup has arrived (another sub-counter's word can), and every call of
+// this kernel uses all kSubs sub-counters (grid >= 128), so all words hold the
+// last call's epoch when a call starts.  The counter lines are this kernel's
+// own: its epochs never mix with the layer kernel's on a shared workspace.
+// The launcher admits grids whose workgroups are all resident at once.
 constexpr int kExpSubLine = kDownDoneLine + kDoneCopies;   // kSubs sub-counters
 constexpr int kExpDoneLine = kExpSubLine + kSubs;          // kDoneCopies lines
 static_assert(kExpDoneLine + kDoneCopies <= kFusedCtrLines, "counter block too small");
@@ -895,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void k_expert1(Expert1Args a) {
       tg[u].load(a.gq, a.gs, a.gb, a.H, n0 + u, geoH);
       tu[u].load(a.uq, a.us, a.ub, a.H, n0 + u, geoH);
     }
-    const int ep_v = ld_agent(ctr_line(ctr, kExpDoneLine));
+    const int ep_v = ld_agent(ctr_line(ctr, kExpDoneLine) + b % kSubs);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) prep_x4<BITS, false, true>(xq[q], lds_xp, a.H, q * (kThreads / 8) + tid / 8);
     lds_barrier();
@@ -914,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void k_expert1(Expert1Args a) {
     }
     ep = __builtin_amdgcn_readfirstlane(ep_v) + 1;
   } else {
-    ep = __builtin_amdgcn_readfirstlane(ld_agent(ctr_line(ctr, kExpDoneLine))) + 1;
+    ep = __builtin_amdgcn_readfirstlane(ld_agent(ctr_line(ctr, kExpDoneLine) + b % kSubs)) + 1;
   }
   // Arrival (wave 0's image stores drained first).
   if (wave == 0) vm_drain();

@@ -215,6 +215,8 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st);
 // The single-expert FFN in one launch; hipErrorNotSupported when the shape
 // or the resident workgroups do not admit it (the caller then uses two).
 hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st);
+// Byte offset of the counter block's wait-timeout word.
+size_t wait_timeout_offset();
 bool fused1_supported(int H, int I, int E, int bits);
 
 // Row-block sizing shared by host and launchers.  RPI = rows one wave covers

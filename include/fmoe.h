@@ -126,6 +126,12 @@ int32_t fmoe_abi_version(void);
 /* Message for the last non-OK status returned on the calling thread. */
 const char *fmoe_last_error(void);
 
+/* Diagnostics: byte offset, within any workspace, of the 32-bit word that the
+ * one-launch kernels set to 1 when one of their bounded waits for another
+ * workgroup gives up instead of hanging (the call's outputs are then not
+ * valid).  It stays 0 otherwise; the caller may read it and clear it. */
+size_t fmoe_wait_timeout_offset(void);
+
 /* Section offsets off[9] of an expert slab in the canonical layout and the
  * slab size in bytes (the return value; -1 with the message set if the
  * arguments are unsupported).  Host-only; enqueues nothing. */

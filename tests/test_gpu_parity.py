@@ -385,6 +385,35 @@ def test_expert_ffn_and_layer_share_workspace(layer4):
     ref = oracle.expert_ffn(layer4.slab_host(11), cfg.H, cfg.I, cfg.spec.bits, cfg.spec.group,
                             cfg.spec.sbytes, xe.astype(np.float64))
     assert rel_l2(own_e, ref) <= TOL
+    assert _wait_timeouts(shared) == 0
+
+
+def _wait_timeouts(ws):
+    off = fm.lib().fmoe_wait_timeout_offset()
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
+def test_expert_ffn_many_calls_no_wait_timeout(layer4):
+    """Hundreds of one-launch expert FFN calls back to back on one workspace
+    (four experts and inputs in turn) end with the same bits as single calls,
+    and no bounded wait in them gave up (the workspace's timeout word stays 0)."""
+    cfg, fmt = layer4.cfg, layer4.fmt
+    experts = [_expert_of(layer4, e) for e in (3, 100, 257, 511)]
+    xs = [dev(synth.normal(42, 5, 7 + i, (cfg.H,))) for i in range(4)]
+    ws = torch.zeros(fm.fmoe_expert_ffn_workspace_size(experts[0], fmt), dtype=torch.uint8,
+                     device="cuda")
+    ref = []
+    for i in range(4):
+        y = torch.empty(cfg.H, device="cuda")
+        fm.fmoe_expert_ffn(experts[i], fmt, xs[i], y, ws)
+        ref.append(y)
+    ys = [torch.empty(cfg.H, device="cuda") for _ in range(4)]
+    for it in range(400):
+        fm.fmoe_expert_ffn(experts[it % 4], fmt, xs[it % 4], ys[it % 4], ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(ys[i], ref[i]), i
+    assert _wait_timeouts(ws) == 0
 
 
 def test_expert_ffn_one_and_two_launches_agree(layer4, monkeypatch):
