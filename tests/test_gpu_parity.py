@@ -416,6 +416,42 @@ def test_expert_ffn_many_calls_no_wait_timeout(layer4):
     assert _wait_timeouts(ws) == 0
 
 
+def test_expert_ffn_graph_replays_match_eager(layer4):
+    """The one-launch expert FFN captured in a HIP graph (8 calls over 4 experts):
+    every replay, with eager calls and synchronisations between replays, gives
+    the eager results bit for bit, and no wait gives up."""
+    cfg, fmt = layer4.cfg, layer4.fmt
+    experts = [_expert_of(layer4, e) for e in (5, 77, 300, 420)]
+    xs = [dev(synth.normal(42, 6, 7 + i, (cfg.H,))) for i in range(4)]
+    ws = torch.zeros(fm.fmoe_expert_ffn_workspace_size(experts[0], fmt), dtype=torch.uint8,
+                     device="cuda")
+    eager = []
+    for i in range(8):
+        y = torch.empty(cfg.H, device="cuda")
+        fm.fmoe_expert_ffn(experts[i % 4], fmt, xs[i % 4], y, ws)
+        eager.append(y)
+    torch.cuda.synchronize()
+    outs = [torch.empty(cfg.H, device="cuda") for _ in range(8)]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(8):
+            fm.fmoe_expert_ffn(experts[i % 4], fmt, xs[i % 4], outs[i], ws,
+                               stream=torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(8):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        y = torch.empty(cfg.H, device="cuda")   # eager work between replays
+        fm.fmoe_expert_ffn(experts[rep % 4], fmt, xs[rep % 4], y, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager[rep % 4])
+    assert _wait_timeouts(ws) == 0
+
+
 def test_expert_ffn_one_and_two_launches_agree(layer4, monkeypatch):
     """The one-launch expert FFN and the two-launch form (FMOE_NO_FUSED=1) agree
     within the tolerance, and each matches the oracle."""
