@@ -41,16 +41,18 @@ METRIC = ("µs per MoE layer & achieved HBM GB/s (% of peak), 4-bit, hidden 4096
           "512 experts")
 GRAPH_LEN = 64
 XPOOL = 64
-DEFAULT_STEPS = {"layer4": (6400, 640), "layer2": (6400, 640), "expert": (4096, 640),
-                 "stack60": (40, 4)}
+DEFAULT_STEPS = {"layer4": (640, 64), "layer2": (640, 64), "expert": (640, 64),
+                 "stack60": (20, 2)}
+SPIN_US = 2000          # GPU busy-wait queued ahead of a timed region
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None,
-                   help="timed steps (default 6400 layers; 64 expert passes x 64; 40 stacks)")
-    p.add_argument("--warmup", type=int, default=None)
+                   help="timed steps, any positive count (default 640 layers / expert passes, "
+                        "20 stacks)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps before (>= 0)")
     p.add_argument("--workload", default="layer4",
                    choices=["layer4", "layer2", "expert", "stack60"],
                    help="layer4/layer2: one batch-1 layer per step; expert: one expert's "
@@ -65,7 +67,102 @@ def parse():
                         "byte counters of a profiler) and exit")
     p.add_argument("--no-stream-probe", action="store_true",
                    help="skip measuring the streaming-read ceiling")
-    return p.parse_args()
+    return p.parse_args(argv)
+
+
+def resolve_steps(args):
+    """Fill in the workload's default step counts; any positive --steps and any
+    --warmup >= 0 is valid."""
+    dsteps, dwarm = DEFAULT_STEPS[args.workload]
+    args.steps = dsteps if args.steps is None else args.steps
+    args.warmup = dwarm if args.warmup is None else args.warmup
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    return args
+
+
+def step_chunks(n, start=0, size=GRAPH_LEN):
+    """(first step, count) pieces of at most `size` steps that cover steps
+    start .. start+n-1 in order: full graphs, then one shorter graph for the
+    remainder."""
+    return [(start + i, min(size, n - i)) for i in range(0, n, size)]
+
+
+class GraphRunner:
+    """HIP graphs of consecutive steps, keyed by (first step mod period, count):
+    steps whose inputs repeat with `period` share one captured graph."""
+
+    def __init__(self, torch, stream, step, period):
+        self.torch, self.stream, self.step, self.period = torch, stream, step, period
+        self.graphs = {}
+
+    def graph(self, first, count):
+        key = (first % self.period, count)
+        if key not in self.graphs:
+            torch = self.torch
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(first, first + count):
+                    self.step(i, cs)
+            self.graphs[key] = g
+        return self.graphs[key]
+
+    def prepare(self, chunks):
+        for f, c in chunks:
+            self.graph(f, c)
+        self.torch.cuda.synchronize()
+
+    def run(self, chunks):
+        with self.torch.cuda.stream(self.stream):
+            for f, c in chunks:
+                self.graph(f, c).replay()
+
+    def timed(self, chunks):
+        """Exactly the steps of `chunks` between two HIP events on the stream the
+        kernels run on.  A bounded busy-wait is queued first so that the GPU is
+        still busy while the host queues the start event and the graphs, and the
+        region holds no host launch latency.  Returns (event ms, host wall ms of
+        the synchronised region)."""
+        torch = self.torch
+        import probes
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.stream):
+            probes.spin(SPIN_US, self.stream.cuda_stream)
+            ev0.record(self.stream)
+            for f, c in chunks:
+                self.graph(f, c).replay()
+            ev1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return ev0.elapsed_time(ev1), wall
+
+    def spread(self, first, count, reps=20):
+        """Per-replay ms of `reps` single replays of one graph (context only)."""
+        torch = self.torch
+        g = self.graph(first, count)
+        per = []
+        with torch.cuda.stream(self.stream):
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(self.stream)
+                g.replay()
+                b.record(self.stream)
+                per.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in per)
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def layer_bytes(cfg):
@@ -150,42 +247,85 @@ def stack_traffic_from_profiles(kernel_hash, n_layers):
     return int(total * n_layers)
 
 
-def cpu_baseline(cfg, n_tokens):
-    """The CPU oracle (single-threaded C, fp64) on a bounded sample of tokens of
-    the same workload: routing over all 512 experts plus the 5 active experts'
-    dequantise-and-multiply, combine, residual and RMSNorm."""
+def _rel(a, ref):
+    import numpy as np
+    a, ref = np.asarray(a, np.float64), np.asarray(ref, np.float64)
+    n = np.linalg.norm(ref)
+    d = np.linalg.norm(a - ref)
+    return float(d if n == 0 else d / n)
+
+
+def cpu_baseline(cfg, sample, xhost, gpu=None):
+    """The CPU oracle (single-threaded C, fp64) on a bounded sample of steps of the
+    timed workload: step t is (replica r, input j) -- routing over all E experts,
+    then the k routed and the shared expert's dequantise-and-multiply, combine,
+    residual and RMSNorm.  Only the oracle calls are timed.
+
+    When `gpu` holds the library's outputs (idx, w, moe, h, y) for the first
+    steps of the sample, they are compared with the oracle's: routing sets
+    exactly (a step whose k-th/(k+1)-th logit gap is under 1e-6 is counted as
+    excluded and checked with the GPU's own selection), weights to 1e-5 and
+    moe/h/y by rel-L2 against 2e-3.  Returns (us per token, GB/s, parity)."""
     import numpy as np
     import oracle
     import synth
     sp = cfg.spec
-    Wr, wsg, gamma = synth.router(cfg, 0), synth.shared_gate(cfg, 0), synth.gamma(cfg, 0)
-    x = synth.activations(cfg, n_tokens, pool=9)
-    shared = synth.slab(sp, cfg.seed, 0, cfg.E)
+    gpu = gpu or []
+    per_layer = {}
     total = 0.0
-    for t in range(n_tokens):
+    parity = {"tokens": len(gpu), "index_mismatch": 0, "excluded_near_ties": 0,
+              "max_w_abs_err": 0.0, "max_rel_l2": {"moe": 0.0, "h": 0.0, "y": 0.0}}
+    for t, (r, j) in enumerate(sample):
+        if r not in per_layer:
+            per_layer[r] = (synth.router(cfg, r), synth.shared_gate(cfg, r), synth.gamma(cfg, r),
+                            synth.slab(sp, cfg.seed, r, cfg.E))
+        Wr, wsg, gamma, shared = per_layer[r]
+        x = xhost[j]
         t0 = time.perf_counter()
-        idx, w, _, _, _ = oracle.route(Wr, x[t:t + 1], cfg.k)
+        idx, w, lg, gap, _ = oracle.route(Wr, x[None, :], cfg.k)
         total += time.perf_counter() - t0
-        slabs = [synth.slab(sp, cfg.seed, 0, int(e)) for e in idx[0]]     # untimed input prep
+        sel, wsel = idx[0], w[0]
+        if t < len(gpu):
+            gidx, gw, gmoe, gh, gy = gpu[t]
+            if gap[0] < 1e-6:
+                parity["excluded_near_ties"] += 1
+                sel = np.asarray(gidx, np.int32)
+                z = lg[0][sel] - lg[0][sel].max()
+                wsel = np.exp(z) / np.exp(z).sum()
+            elif sorted(gidx.tolist()) != sorted(sel.tolist()):
+                parity["index_mismatch"] += 1
+        slabs = [synth.slab(sp, cfg.seed, r, int(e)) for e in sel]     # untimed input prep
         t0 = time.perf_counter()
-        oracle.moe_token(slabs, w[0], shared, cfg.H, cfg.I, sp.bits, sp.group, sp.sbytes, wsg,
-                         gamma, cfg.eps, x[t], x[t])
+        ref = oracle.moe_token(slabs, wsel, shared, cfg.H, cfg.I, sp.bits, sp.group, sp.sbytes,
+                               wsg, gamma, cfg.eps, x, x)
         total += time.perf_counter() - t0
-    us = total / n_tokens * 1e6
+        if t < len(gpu):
+            order = {int(e): i for i, e in enumerate(gidx)}
+            werr = max(abs(float(gw[order[int(e)]]) - float(wv)) for e, wv in zip(sel, wsel)
+                       if int(e) in order) if order else 0.0
+            parity["max_w_abs_err"] = max(parity["max_w_abs_err"], werr)
+            for name, got in (("moe", gmoe), ("h", gh), ("y", gy)):
+                parity["max_rel_l2"][name] = max(parity["max_rel_l2"][name],
+                                                 _rel(got, ref[name]))
+    us = total / len(sample) * 1e6
     nbytes, _ = layer_bytes(cfg)
-    return us, nbytes / (us * 1e-6) / 1e9
+    if gpu:
+        parity["max_w_abs_err"] = float(f"{parity['max_w_abs_err']:.3e}")
+        parity["max_rel_l2"] = {k: float(f"{v:.3e}") for k, v in parity["max_rel_l2"].items()}
+        parity["pass"] = (parity["index_mismatch"] == 0 and parity["max_w_abs_err"] <= 1e-5
+                          and max(parity["max_rel_l2"].values()) <= 2e-3)
+    return us, nbytes / (us * 1e-6) / 1e9, parity
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        msg = (f"--gpus {args.gpus}: this build runs the layer on one GPU only (no multi-GPU "
+               "path; the expert-sharded design is described, not built); use --gpus 1")
+        print(json.dumps({"error": msg}))
+        print(msg, file=sys.stderr)
         sys.exit(2)
-    dsteps, dwarm = DEFAULT_STEPS[args.workload]
-    args.steps = dsteps if args.steps is None else args.steps
-    args.warmup = dwarm if args.warmup is None else args.warmup
-    if args.workload != "stack60" and (args.steps % GRAPH_LEN or args.warmup % GRAPH_LEN):
-        sys.exit(f"--steps and --warmup must be multiples of {GRAPH_LEN}")
+    resolve_steps(args)
 
     import torch
 
@@ -223,33 +363,15 @@ def stream_probe(args, torch):
         return None
 
 
-def time_replays(torch, graphs, reps, warmup_reps, stream):
-    """Replay graphs[i % len] warmup_reps times untimed, then reps times between
-    two HIP events on `stream`; then up to 20 single replays for the spread.
-    Returns (total ms, sorted per-replay ms)."""
-    with torch.cuda.stream(stream):
-        for i in range(warmup_reps):
-            graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(reps):
-            graphs[i % len(graphs)].replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    per = []
-    with torch.cuda.stream(stream):
-        for i in range(min(reps, 20)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            graphs[i % len(graphs)].replay()
-            b.record(stream)
-            per.append((a, b))
-    torch.cuda.synchronize()
-    return total_ms, sorted(a.elapsed_time(b) for a, b in per)
+def empty_gap(args, torch):
+    if args.no_stream_probe:
+        return None
+    try:
+        import probes
+        return round(probes.empty_gap_us(torch), 3)
+    except Exception as exc:  # context only
+        print(f"[bench] gap probe skipped: {exc}", file=sys.stderr)
+        return None
 
 
 def spread(vals):
@@ -257,7 +379,7 @@ def spread(vals):
 
 
 def bench_layer(args, torch):
-    import numpy as np
+    import math
     import bit_dequant_expert_amd as fm
     import synth
 
@@ -278,7 +400,8 @@ def bench_layer(args, torch):
         gam = torch.from_numpy(synth.gamma(cfg, r)).to(dev)
         layers.append(fm.fmoe_layer_desc(cfg.H, cfg.I, cfg.E, cfg.k, fmt, Wr, slabs, stride,
                                          wsg, gam, cfg.eps))
-    xpool = torch.from_numpy(synth.activations(cfg, XPOOL, pool=0)).to(dev)
+    xhost = synth.activations(cfg, XPOOL, pool=0)
+    xpool = torch.from_numpy(xhost).to(dev)
     h = torch.empty(XPOOL, cfg.H, device=dev)
     y = torch.empty(XPOOL, cfg.H, device=dev)
     ws_bytes = fm.fmoe_workspace_size(layers[0], 1)
@@ -291,6 +414,7 @@ def bench_layer(args, torch):
     row = cfg.H * 4
 
     def step(i, stream):
+        # step i: replica i mod R, input vector i mod XPOOL (x is also the residual)
         r, j = i % R, i % XPOOL
         xi = xb + j * row
         rc = fm.fmoe_moe_layer_forward_raw(Lp[r], 1, xi, xi, hb + j * row, yb + j * row, None,
@@ -308,26 +432,20 @@ def bench_layer(args, torch):
         print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
         return
 
-    # Graphs: one per 64-step window, so a replay sweeps every replica pairing.
-    n_graphs = max(1, (R * XPOOL // GRAPH_LEN) // max(1, np.gcd(R, XPOOL)))
-    n_graphs = min(n_graphs, 8)
-    graphs = []
     with torch.cuda.stream(s):
         for i in range(8):                      # eager warm-up before capture
             step(i, s.cuda_stream)
     torch.cuda.synchronize()
-    for gi in range(n_graphs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            cs = torch.cuda.current_stream().cuda_stream
-            for i in range(GRAPH_LEN):
-                step(gi * GRAPH_LEN + i, cs)
-        graphs.append(g)
+    period = R * XPOOL // math.gcd(R, XPOOL)
+    runner = GraphRunner(torch, s, step, period)
+    timed = step_chunks(args.steps, 0)
+    warm = step_chunks(args.warmup, args.steps)
+    runner.prepare(warm + timed + [(0, GRAPH_LEN)])
+    runner.run(warm)
     torch.cuda.synchronize()
-
-    total_ms, rep_ms = time_replays(torch, graphs, args.steps // GRAPH_LEN,
-                                    args.warmup // GRAPH_LEN, s)
-    rep_us = [v * 1000.0 / GRAPH_LEN for v in rep_ms]
+    total_ms, wall_ms = runner.timed(timed)
+    rep_us = [v * 1000.0 / GRAPH_LEN for v in runner.spread(0, GRAPH_LEN)]
+    timeout_word = int(ws[fm.fmoe_wait_timeout_offset():][:4].view(torch.int32).item())
 
     ms_per_step = total_ms / args.steps
     us = ms_per_step * 1000.0
@@ -336,6 +454,7 @@ def bench_layer(args, torch):
     khash = source_hash()
     traffic = traffic_from_profiles(khash, args.workload)
     stream = stream_probe(args, torch)
+    gap = empty_gap(args, torch)
     out = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -347,7 +466,8 @@ def bench_layer(args, torch):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 codes x f16 activations, f32 accumulation (router f64)",
+        "dtype": "u4 codes x f16 activations, f32 accumulation (router f64)"
+                 if sp.bits == 4 else "u2 codes x f16 activations, f32 accumulation (router f64)",
         "data": "synthetic",
         "config": {"workload": f"moe_layer_{args.workload}_h{cfg.H}_e{cfg.E}_i{cfg.I}"
                                f"_top{cfg.k}+1_batch1",
@@ -355,31 +475,65 @@ def bench_layer(args, torch):
                    "bits": sp.bits, "group": sp.group, "scale_dtype": "bf16",
                    "batch": 1, "replicas": R, "graph_len": GRAPH_LEN},
         "us_per_layer": round(us, 3),
+        "timed_region": {"event_ms": round(total_ms, 4), "host_wall_ms": round(wall_ms, 4),
+                         "graphs": [c for _, c in timed],
+                         "note": f"exactly {args.steps} layer forwards between two HIP events on "
+                                 f"the launch stream, after a {SPIN_US} us GPU busy-wait that "
+                                 "keeps host launch latency out of the region; host wall time "
+                                 "includes that wait and both synchronisations"},
         "us_per_layer_min_median_p90": spread(rep_us),
+        "spread_note": f"20 further replays of one {GRAPH_LEN}-layer graph, outside the timed "
+                       "region",
         "moe_layer_tokens_per_s": round(1e6 / us, 1),
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "pct_of_measured_stream_ceiling": None if not stream else round(100.0 * gbps / stream, 2),
         "algorithmic_bytes_per_layer": nbytes,
         "expert_bytes_per_layer": ebytes,
-        "roofline": {"bound": "hbm", "kernel": "k_layer1 (whole layer, one launch)",
+        "roofline": {"bound": "hbm", "kernel": "k_layer1 (whole layer, one launch per step)",
                      "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
+        "wait_timeout_word": timeout_word,
         "kernel_source_hash": khash,
         "context": {"hbm_stream_read_gbps_measured": stream,
-                    "note": "best of 10 passes of a plain 4 GiB streaming read on this GPU"},
+                    "stream_note": "best of 10 passes of a plain 4 GiB streaming read on this GPU",
+                    "empty_kernel_gap_us": gap,
+                    "gap_note": "per launch, 2000 empty one-wave kernels replayed from one graph"},
         "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:
-        import multiprocessing
-        cus, cgb = cpu_baseline(cfg, args.cpu_sample)
+        sample = [(t % R, t % XPOOL) for t in range(args.cpu_sample)]
+        gpu = gpu_sample_outputs(torch, fm, layers, xpool, cfg, sample[:PARITY_TOKENS], ws)
+        cus, cgb, parity = cpu_baseline(cfg, sample, xhost, gpu)
         out["cpu_baseline"] = {"value": round(cgb, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"{args.cpu_sample} tokens of the same layer "
-                                         f"(route over 512 + 5 experts), {cus:.0f} us/token, "
-                                         f"1 thread of {multiprocessing.cpu_count()} host "
-                                         f"logical cores"}
+                               "sample": f"{len(sample)} steps of the timed workload (replica "
+                                         f"t mod {R}, input t mod {XPOOL}; route over 512 + 5 "
+                                         f"experts), {cus:.0f} us/token",
+                               "threads": f"1 thread of {os.cpu_count()} host logical cores",
+                               "cpu_model": host_cpu_model()}
+        out["parity_vs_oracle"] = parity
     return out
 
+
+PARITY_TOKENS = 4
+
+
+def gpu_sample_outputs(torch, fm, layers, xpool, cfg, sample, ws):
+    """Eager layer forwards on (replica, input) pairs of the timed workload, with
+    the routing and moe outputs kept, for comparison with the oracle."""
+    out = []
+    for r, j in sample:
+        x = xpool[j:j + 1]
+        h = torch.empty(1, cfg.H, device=x.device)
+        y = torch.empty(1, cfg.H, device=x.device)
+        moe = torch.empty(1, cfg.H, device=x.device)
+        idx = torch.empty(1, cfg.k, dtype=torch.int32, device=x.device)
+        w = torch.empty(1, cfg.k, device=x.device)
+        fm.fmoe_moe_layer_forward(layers[r], 1, x, x, h, y, idx, w, moe, ws)
+        out.append((idx, w, moe, h, y))
+    torch.cuda.synchronize()
+    return [tuple(t.cpu().numpy()[0] for t in o) for o in out]
 
 
 def _fmt_and_layers(torch, fm, synth, cfg, layer_ids, dev):
@@ -467,21 +621,17 @@ def bench_expert(args, torch):
             for i in range(8):
                 call(kind, i, s.cuda_stream)
         torch.cuda.synchronize()
-        graphs = []
-        for gi in range(NE // GRAPH_LEN):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                cs = torch.cuda.current_stream().cuda_stream
-                for i in range(GRAPH_LEN):
-                    call(kind, gi * GRAPH_LEN + i, cs)
-            graphs.append(g)
-        torch.cuda.synchronize()
-        total_ms, rep_ms = time_replays(torch, graphs, args.steps // GRAPH_LEN,
-                                        args.warmup // GRAPH_LEN, s)
+        runner = GraphRunner(torch, s, lambda i, cs, kind=kind: call(kind, i, cs), NE)
+        timed = step_chunks(args.steps, 0)
+        warm = step_chunks(args.warmup, args.steps)
+        runner.prepare(warm + timed + [(0, GRAPH_LEN)])
+        runner.run(warm)
+        total_ms, wall_ms = runner.timed(timed)
         us = total_ms * 1000.0 / args.steps
         res[kind] = {"us": round(us, 3), "gbps": round(nbytes[kind] / (us * 1e-6) / 1e9, 1),
-                     "bytes": nbytes[kind],
-                     "us_min_median_p90": spread([v * 1000.0 / GRAPH_LEN for v in rep_ms])}
+                     "bytes": nbytes[kind], "host_wall_ms": round(wall_ms, 4),
+                     "us_min_median_p90": spread([v * 1000.0 / GRAPH_LEN
+                                                  for v in runner.spread(0, GRAPH_LEN)])}
     us = res["ffn"]["us"]
     gbps = res["ffn"]["gbps"]
     out = {
@@ -511,7 +661,6 @@ def bench_expert(args, torch):
         "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
     }
     if not args.no_cpu_baseline:
-        import multiprocessing
         import oracle
         n = max(1, args.cpu_sample // 2)
         x = synth.activations(cfg, n, pool=1)
@@ -525,8 +674,9 @@ def bench_expert(args, torch):
         out["cpu_baseline"] = {"value": round(nbytes["ffn"] / (cus * 1e-6) / 1e9, 4),
                                "unit": "GB/s", "cores": 1, "kind": "oracle",
                                "sample": f"{n} experts' gate/up/down on the host, "
-                                         f"{cus:.0f} us/expert, 1 thread of "
-                                         f"{multiprocessing.cpu_count()} host logical cores"}
+                                         f"{cus:.0f} us/expert",
+                               "threads": f"1 thread of {os.cpu_count()} host logical cores",
+                               "cpu_model": host_cpu_model()}
     return out
 
 
@@ -551,7 +701,8 @@ def bench_stack(args, torch):
     print(f"[bench] generating {NL} layers ({NL * stride * (cfg.E + 1) / 1e9:.1f} GB)",
           file=sys.stderr, flush=True)
     fmt, layers = _fmt_and_layers(torch, fm, synth, cfg, range(NL), dev)
-    xs = torch.from_numpy(synth.activations(cfg, NL * T, pool=4)).to(dev).view(NL, T, cfg.H)
+    xs_host = synth.activations(cfg, NL * T, pool=4)
+    xs = torch.from_numpy(xs_host).to(dev).view(NL, T, cfg.H)
     hbuf = [torch.empty(T, cfg.H, device=dev) for _ in range(2)]
     ybuf = [torch.empty(T, cfg.H, device=dev) for _ in range(2)]
     idx = {m: torch.empty(NL, T, cfg.k, dtype=torch.int32, device=dev) for m in MODES}
@@ -589,11 +740,14 @@ def bench_stack(args, torch):
         with torch.cuda.stream(s):
             step(mode, s.cuda_stream)                 # eager warm-up before capture
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            step(mode, torch.cuda.current_stream().cuda_stream)
-        torch.cuda.synchronize()
-        total_ms, rep_ms = time_replays(torch, [g], args.steps, args.warmup, s)
+        # one graph holds one whole 60-layer step; a chunk of 1 step per graph
+        runner = GraphRunner(torch, s, lambda i, cs, mode=mode: step(mode, cs), 1)
+        timed = step_chunks(args.steps, 0, size=1)
+        warm = step_chunks(args.warmup, 0, size=1)
+        runner.prepare([(0, 1)])
+        runner.run(warm)
+        total_ms, wall_ms = runner.timed(timed)
+        rep_ms = runner.spread(0, 1, reps=min(args.steps, 10))
         ms = total_ms / args.steps
         sel = idx[mode].cpu().numpy()
         distinct = [int(np.unique(sel[l]).size) for l in range(NL)]
@@ -601,6 +755,7 @@ def bench_stack(args, torch):
         nbytes = (sum(distinct) + NL) * stride + NL * cfg.E * cfg.H * 4 \
             + NL * (4 * T + 2) * cfg.H * 4
         res[mode] = {"ms_per_step": round(ms, 6), "ms_min_median_p90": spread(rep_ms),
+                     "host_wall_ms": round(wall_ms, 3),
                      "tokens_per_s": round(T / (ms * 1e-3), 1),
                      "us_per_layer": round(ms * 1000.0 / NL, 3),
                      "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -610,7 +765,7 @@ def bench_stack(args, torch):
                          "max": max(distinct)},
                      "routed_experts_on_matrix_cores_per_layer": round(
                          float(np.mean([int((c >= 16).sum()) for c in counts])), 3)}
-        del g
+        del runner
     main_res = res["independent"]
     ms, gbps = main_res["ms_per_step"], main_res["gbps"]
     out = {
@@ -646,15 +801,17 @@ def bench_stack(args, torch):
         "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
     }
     if not args.no_cpu_baseline:
-        import multiprocessing
         n = max(1, args.cpu_sample // 2)
-        cus, _ = cpu_baseline(cfg, n)
+        # layer-token t: layer t mod 60, token (7 t) mod 32 of that layer's independent batch
+        sample = [(t % NL, (t % NL) * T + (7 * t) % T) for t in range(n)]
+        cus, _, _ = cpu_baseline(cfg, sample, xs_host)
         out["cpu_baseline"] = {"value": round(1e6 / (NL * cus), 4), "unit": "tokens/s",
                                "cores": 1, "kind": "oracle",
-                               "sample": f"{n} layer-tokens of a 4-bit layer (route over 512 + "
-                                         f"5 experts), {cus:.0f} us per layer-token, scaled to "
-                                         f"60 layers; 1 thread of "
-                                         f"{multiprocessing.cpu_count()} host logical cores"}
+                               "sample": f"{n} layer-tokens of the stack's independent-routing "
+                                         f"pass (route over 512 + 5 experts), {cus:.0f} us per "
+                                         f"layer-token, scaled to 60 layers",
+                               "threads": f"1 thread of {os.cpu_count()} host logical cores",
+                               "cpu_model": host_cpu_model()}
     return out
 
 

@@ -1,5 +1,6 @@
-"""Measurement probes used by bench.py: HBM streaming-read ceiling, shader
-clock, empty-kernel launch gap.  Not part of the MoE layer."""
+"""Measurement probes used by bench.py: HBM streaming-read ceiling, empty-kernel
+launch gap, and a bounded spin that keeps the GPU busy while the host queues a
+timed region.  Not part of the MoE layer."""
 import ctypes as C
 import os
 
@@ -25,8 +26,8 @@ def lib():
     if _lib is None:
         L = C.CDLL(LIB)
         L.probe_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
-        L.probe_clock.argtypes = [C.c_void_p, C.c_int, C.c_void_p]
         L.probe_empty.argtypes = [C.c_int, C.c_void_p]
+        L.probe_spin.argtypes = [C.c_int, C.c_void_p]
         _lib = L
     return _lib
 
@@ -51,15 +52,9 @@ def stream_read_gbps(torch, nbytes=4 << 30, reps=10, grid=None):
     return best
 
 
-def shader_clock_mhz(torch, iters=2_000_000):
-    out = torch.zeros(4, dtype=torch.int64, device="cuda")
-    lib().probe_clock(out.data_ptr(), iters, torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
-    c, w = out[0].item(), out[1].item()
-    return c / (w / 100.0) if w else 0.0   # wall clock ticks at 100 MHz
-
-
 def empty_gap_us(torch, n=2000):
+    """Average time per launch of an empty one-wave kernel, n launches replayed
+    from one HIP graph: the fixed cost of a kernel boundary on this GPU."""
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
@@ -74,3 +69,11 @@ def empty_gap_us(torch, n=2000):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1000.0 / n
+
+
+def spin(us, stream):
+    """Enqueue one wave that busy-waits about `us` microseconds on `stream` (an
+    integer hipStream_t)."""
+    rc = lib().probe_spin(int(us), stream)
+    if rc != 0:
+        raise RuntimeError(f"probe_spin launch failed: {rc}")

@@ -1,7 +1,8 @@
 // probes.hip -- measurement probes for the benchmark (not part of the layer):
 //   probe_stream_read : read a buffer once with 16-byte loads (HBM ceiling)
-//   probe_clock       : shader-clock ticks vs 100 MHz wall-clock ticks
 //   probe_empty       : an empty kernel, for launch-gap measurements
+//   probe_spin        : one wave that busy-waits a given number of microseconds
+//                       (keeps the queue ahead of the host before a timed region)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,19 +25,13 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p
   if (acc == 0x9E3779B9u) sink[0] = acc;  // practically never: keeps the loads alive
 }
 
-__global__ void k_clock(uint64_t* out, int iters) {
-  const uint64_t c0 = clock64(), w0 = wall_clock64();
-  float v = (float)threadIdx.x;
-  for (int i = 0; i < iters; ++i) v = v * 1.0000001f + 0.5f;
-  const uint64_t c1 = clock64(), w1 = wall_clock64();
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    out[0] = c1 - c0;
-    out[1] = w1 - w0;
-    out[2] = (uint64_t)(v == 12345.f);
-  }
-}
-
 __global__ void k_empty() {}
+
+// Bounded: the wave leaves once the 100 MHz wall clock has advanced `ticks`.
+__global__ void k_spin(uint64_t ticks) {
+  const uint64_t w0 = wall_clock64();
+  while (wall_clock64() - w0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
 
 }  // namespace
 
@@ -46,12 +41,14 @@ extern "C" int probe_stream_read(const void* p, int64_t bytes, void* sink, int g
   return (int)hipGetLastError();
 }
 
-extern "C" int probe_clock(void* out, int iters, void* stream) {
-  hipLaunchKernelGGL(k_clock, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint64_t*)out, iters);
+extern "C" int probe_empty(int grid, void* stream) {
+  hipLaunchKernelGGL(k_empty, dim3(grid), dim3(64), 0, (hipStream_t)stream);
   return (int)hipGetLastError();
 }
 
-extern "C" int probe_empty(int grid, void* stream) {
-  hipLaunchKernelGGL(k_empty, dim3(grid), dim3(64), 0, (hipStream_t)stream);
+extern "C" int probe_spin(int us, void* stream) {
+  if (us < 0) us = 0;
+  if (us > 100000) us = 100000;
+  hipLaunchKernelGGL(k_spin, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint64_t)us * 100u);
   return (int)hipGetLastError();
 }
