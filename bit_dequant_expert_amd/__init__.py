@@ -141,6 +141,10 @@ def fmoe_last_error() -> str:
     return lib().fmoe_last_error().decode()
 
 
+def fmoe_wait_timeout_offset() -> int:
+    return int(lib().fmoe_wait_timeout_offset())
+
+
 def fmoe_slab_layout(hidden: int, inter: int, fmt: fmoe_qformat):
     off = (C.c_int64 * 9)()
     size = lib().fmoe_slab_layout(hidden, inter, C.byref(fmt), off)
