@@ -156,8 +156,9 @@ void or_gemv_groupsum(const uint8_t *q, const void *s, const void *b, or_fmt f,
     }
 }
 
-/* The pages' naive form, "float x = nibble * scale + bias" then multiply,
- * accumulated in fp32 in input order. */
+/* The unfused form that [WAS] "2. FMA-optimierte Dequantisierungs-Kernel"
+ * starts from: each weight is dequantised on its own, then multiplied by its
+ * input and accumulated, all in fp32 and in input order. */
 void or_gemv_naive_f32(const uint8_t *q, const void *s, const void *b, or_fmt f,
                        int N, int K, const float *x, float *y)
 {

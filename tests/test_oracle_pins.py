@@ -300,21 +300,119 @@ def test_layer_forced_routing():
 
 
 def test_slab_layout_page_sizes():
+    # One unit reading for every size the pages print: their "MB" and "GB" are
+    # binary units (MiB, GiB).  The slab is the exact pin (6.75 MiB); the model
+    # totals are the pages' rounded figures for 60 x 512 slabs plus the 5.5 GiB
+    # of non-expert weights, and agree with this layout within 2%.
     facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
     off, size4 = oracle.slab_layout(4096, 1024, 4, 64, 2)
-    # one expert = 6.75 MB, read as MiB: 7,077,888 bytes
     assert size4 == 7_077_888 == int(facts["expert_bytes_mb"]["value"] * 2 ** 20)
     assert list(off) == [0, 2097152, 2228224, 2359296, 4456448, 4587520, 4718592, 6815744,
                          6946816]
     L, E = facts["layers"]["value"], facts["experts_per_layer"]["value"]
-    total4 = size4 * E * L / 2 ** 30 + facts["non_expert_bytes_gb"]["value"]
-    assert abs(total4 / facts["model_bytes_4bit_gb"]["value"] - 1) < 0.01
+    non_expert = facts["non_expert_bytes_gb"]["value"]
     _, size2 = oracle.slab_layout(4096, 1024, 2, 64, 2)
-    assert size2 == 3_932_160
-    total2 = size2 * E * L / 1e9
-    assert abs(total2 / facts["model_bytes_2bit_gb"]["value"] - 1) < 0.01
+    assert size2 == 3_932_160 == int(3.75 * 2 ** 20)
+    for size, key in ((size4, "model_bytes_4bit_gb"), (size2, "model_bytes_2bit_gb")):
+        total_gib = size * E * L / 2 ** 30 + non_expert
+        assert abs(total_gib / facts[key]["value"] - 1) < 0.02, (key, total_gib)
     _, size0 = oracle.slab_layout(256, 128, 4, 32, 4)
     assert size0 == 73_728
+
+
+def _row_const_mat(n, k, G, sb, rowvals):
+    """Zero scales and bias rowvals[r] in every group of row r: every weight of
+    row r equals rowvals[r]."""
+    q = np.zeros((n, k * 4 // 8), np.uint8)
+    s = store_sb(np.zeros((n, k // G)), sb)
+    b = store_sb(np.repeat(np.asarray(rowvals, np.float64)[:, None], k // G, axis=1), sb)
+    return q, s, b
+
+
+@pytest.mark.parametrize("sb", [4, 2])
+def test_layer_combine_gate_and_pairing_closed_form(sb):
+    # Closed form of the whole layer at x = 1 (length H = 128):
+    #   every gate weight 1/128 and every up weight 1/256 -> gate = 1, up = 1/2,
+    #   so every SwiGLU output is a0 = silu(1)/2 = 1/(2 (1 + e^-1));
+    #   down row m of expert e is the constant d_e[m] -> FFN_e(x)[m] = I a0 d_e[m];
+    #   router rows are constants making the logits ln 2, -3, ln 4, 0, -4, ln 3
+    #   for experts 0..5, so with k = 4 the selection is (2, 5, 0, 3) with
+    #   weights 0.4, 0.3, 0.2, 0.1; the shared-gate vector gives wsg . x = ln 3,
+    #   so g = sigmoid(ln 3) = 3/4.
+    # A flipped sigmoid (g = 1/4), a gate taken on the residual, or weights
+    # paired with the wrong experts each change moe by far more than 1e-12.
+    H, I, G, E, k = 128, 64, 32, 6, 4
+    rng = np.random.default_rng(21)
+    spec = synth.QSpec(H, I, 4, G, sb, 0.001, 0.01, -8.0)
+    # down rows: small integers / 64, exact in bf16, distinct per expert and row
+    d = rng.integers(-64, 65, size=(E + 1, H)).astype(np.float64) / 64.0
+    slabs = []
+    for e in range(E + 1):
+        slabs.append(build_slab(spec, [_row_const_mat(I, H, G, sb, np.full(I, 1 / 128)),
+                                       _row_const_mat(I, H, G, sb, np.full(I, 1 / 256)),
+                                       _row_const_mat(H, I, G, sb, d[e])]))
+    size = slabs[0].size
+    target = np.array([math.log(2), -3.0, math.log(4), 0.0, -4.0, math.log(3)])
+    Wr = np.repeat((target / H).astype(np.float32)[:, None], H, axis=1)
+    wsg = np.full(H, np.float32(math.log(3) / H), np.float32)
+    gamma = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    x = np.ones((1, H), np.float32)
+    r = rng.standard_normal((1, H)).astype(np.float32)
+    out = oracle.layer_forward(Wr, np.concatenate(slabs), size, wsg, gamma, 1e-6, H, I, E, k,
+                               4, G, sb, x, r)
+    assert out["status"] == 0
+    assert out["idx"][0].tolist() == [2, 5, 0, 3]
+    # the stored router values are fp32: the logits are H times them, exactly
+    logit = H * Wr[:, 0].astype(np.float64)
+    assert np.array_equal(out["logits"][0], logit)
+    sel = logit[[2, 5, 0, 3]]
+    w = np.exp(sel - sel.max()) / np.exp(sel - sel.max()).sum()
+    assert np.allclose(out["w"][0], w, rtol=1e-14)
+    assert np.allclose(w, [0.4, 0.3, 0.2, 0.1], atol=1e-6)
+    gl = H * np.float64(wsg[0])
+    g = 1.0 / (1.0 + math.exp(-gl))
+    assert abs(g - 0.75) < 1e-6 and abs(out["g"][0] - g) < 1e-15
+    a0 = 1.0 / (2.0 * (1.0 + math.exp(-1.0)))
+    moe = I * a0 * (sum(wi * d[e] for wi, e in zip(w, [2, 5, 0, 3])) + g * d[E])
+    assert np.allclose(out["moe"][0], moe, rtol=1e-12, atol=1e-14)
+    h = r[0].astype(np.float64) + moe
+    assert np.allclose(out["h"][0], h, rtol=1e-12, atol=1e-12)
+    yref = gamma.astype(np.float64) * h / math.sqrt(np.mean(h * h) + 1e-6)
+    assert np.allclose(out["y"][0], yref, rtol=1e-12)
+    # the alternatives this rules out differ from the oracle's result by far more
+    wrong_g = I * a0 * (sum(wi * d[e] for wi, e in zip(w, [2, 5, 0, 3])) + (1 - g) * d[E])
+    reversed_pairs = I * a0 * (sum(wi * d[e] for wi, e in zip(w, [3, 0, 5, 2])) + g * d[E])
+    for alt in (wrong_g, reversed_pairs):
+        assert rel_l2(alt, out["moe"][0]) > 1e-3
+
+
+def test_layer_matches_separate_expert_calls():
+    # Random distinct experts and random x, r: the layer's moe equals the
+    # routing-weighted sum of separate single-expert FFNs of the selected slabs,
+    # in the selection's order, plus sigmoid(wsg . x) times the shared FFN.
+    rng = np.random.default_rng(22)
+    cfg, size, slabs, Wr = _tiny_layer(rng, E=8, k=3)
+    wsg = (rng.standard_normal(cfg.H) * 0.1).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, cfg.H).astype(np.float32)
+    x = rng.standard_normal((2, cfg.H)).astype(np.float32)
+    r = rng.standard_normal((2, cfg.H)).astype(np.float32)
+    out = oracle.layer_forward(Wr, slabs, size, wsg, gamma, 1e-6, cfg.H, cfg.I, cfg.E, cfg.k,
+                               4, 32, 4, x, r)
+    for t in range(2):
+        xt = x[t].astype(np.float64)
+        f = {e: oracle.expert_ffn(slabs[e * size:(e + 1) * size], cfg.H, cfg.I, 4, 32, 4, xt)
+             for e in range(cfg.E + 1)}
+        gl = float(np.dot(wsg.astype(np.float64), xt))
+        g = 1.0 / (1.0 + math.exp(-gl))
+        moe = sum(out["w"][t][i] * f[int(e)] for i, e in enumerate(out["idx"][t])) \
+            + g * f[cfg.E]
+        assert abs(out["g"][t] - g) < 1e-15
+        assert rel_l2(out["moe"][t], moe) < 1e-14
+        # every expert's output differs, so any other pairing of weights and
+        # experts would not match
+        perm = out["idx"][t][::-1]
+        alt = sum(out["w"][t][i] * f[int(e)] for i, e in enumerate(perm)) + g * f[cfg.E]
+        assert rel_l2(alt, moe) > 1e-3
 
 
 def test_layer_tiny_config_runs():
