@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "FMOE_OK", 1: "FMOE_ERR_NULL", 2: "FMOE_ERR_SHAPE", 3: "FMOE_
 ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_route_topk",
                "fmoe_route_workspace_size", "fmoe_dequant_gemv", "fmoe_expert_ffn",
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
-               "fmoe_workspace_size", "fmoe_wait_timeout_offset")
+               "fmoe_workspace_size", "fmoe_wait_timeout_offset", "fmoe_get_paths",
+               "fmoe_set_paths")
 
 
 class FmoeError(RuntimeError):
@@ -59,6 +60,11 @@ class fmoe_layer(C.Structure):
                 ("norm_eps", C.c_float)]
 
 
+class fmoe_paths(C.Structure):
+    _fields_ = [("no_fused", C.c_int32), ("no_mfma", C.c_int32), ("mfma_min_tokens", C.c_int32),
+                ("debug_sync", C.c_int32)]
+
+
 _lib = None
 
 
@@ -74,6 +80,8 @@ def lib() -> C.CDLL:
         L.fmoe_abi_version.argtypes, L.fmoe_abi_version.restype = [], i32
         L.fmoe_last_error.argtypes, L.fmoe_last_error.restype = [], C.c_char_p
         L.fmoe_wait_timeout_offset.argtypes, L.fmoe_wait_timeout_offset.restype = [], sz
+        L.fmoe_get_paths.argtypes, L.fmoe_get_paths.restype = [C.POINTER(fmoe_paths)], None
+        L.fmoe_set_paths.argtypes, L.fmoe_set_paths.restype = [C.POINTER(fmoe_paths)], C.c_int
         L.fmoe_slab_layout.argtypes = [i32, i32, C.POINTER(fmoe_qformat), C.POINTER(C.c_int64)]
         L.fmoe_slab_layout.restype = i64
         L.fmoe_route_topk.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
@@ -143,6 +151,36 @@ def fmoe_last_error() -> str:
 
 def fmoe_wait_timeout_offset() -> int:
     return int(lib().fmoe_wait_timeout_offset())
+
+
+def fmoe_get_paths() -> fmoe_paths:
+    p = fmoe_paths()
+    lib().fmoe_get_paths(C.byref(p))
+    return p
+
+
+def fmoe_set_paths(p: fmoe_paths):
+    _check(lib().fmoe_set_paths(C.byref(p)))
+
+
+class paths:
+    """Context manager that changes the kernel-path selection (fmoe_paths
+    fields as keywords) and restores the previous one on exit."""
+
+    def __init__(self, **kw):
+        self.kw = kw
+
+    def __enter__(self):
+        self.saved = fmoe_get_paths()
+        p = fmoe_get_paths()
+        for k, v in self.kw.items():
+            setattr(p, k, int(v))
+        fmoe_set_paths(p)
+        return p
+
+    def __exit__(self, *exc):
+        fmoe_set_paths(self.saved)
+        return False
 
 
 def fmoe_slab_layout(hidden: int, inter: int, fmt: fmoe_qformat):

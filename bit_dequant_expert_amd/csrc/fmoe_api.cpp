@@ -185,28 +185,40 @@ size_t route_ws(int T, int E) {
   return fmoe::kWsReserved + align256((size_t)fmoe::route_ksplit(T, E) * T * E * 8);
 }
 
-// FMOE_NO_FUSED=1 forces the multi-launch path for one-token layers and the
-// two-launch single-expert FFN (debug and cross-checking only).
-// FMOE_NO_MFMA=1 keeps every expert of a batch on the multi-token GEMV path
-// (cross-checking only).  FMOE_MFMA_MIN_TOKENS=n sends only experts with at
-// least n tokens of the batch to the matrix cores and the rest to the GEMV
-// kernels (cross-checking only; the default sends every expert).
-bool mfma_disabled() {
-  const char* v = getenv("FMOE_NO_MFMA");
+// Kernel-path selection (include/fmoe.h, fmoe_paths): read from the
+// environment once when the library is loaded, changed only by fmoe_set_paths.
+fmoe_paths g_paths = {0, 0, fmoe::kMfmaTokens, 0};
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
   return v && v[0] == '1';
 }
 
-int mfma_min_tokens() {
-  const char* v = getenv("FMOE_MFMA_MIN_TOKENS");
-  const int n = v ? atoi(v) : 0;
-  return n >= 1 ? n : fmoe::kMfmaTokens;
-}
+struct PathsFromEnv {
+  PathsFromEnv() {
+    g_paths.no_fused = env_flag("FMOE_NO_FUSED");
+    g_paths.no_mfma = env_flag("FMOE_NO_MFMA");
+    const char* v = getenv("FMOE_MFMA_MIN_TOKENS");
+    const int n = v ? atoi(v) : 0;
+    g_paths.mfma_min_tokens = n >= 1 ? n : fmoe::kMfmaTokens;
+    g_paths.debug_sync = env_flag("FMOE_DEBUG_SYNC");
+  }
+} g_paths_from_env;
 
-bool fused_disabled() {
-  const char* v = getenv("FMOE_NO_FUSED");
-  return v && v[0] == '1';
-}
+bool mfma_disabled() { return g_paths.no_mfma != 0; }
+int mfma_min_tokens() { return g_paths.mfma_min_tokens; }
+bool fused_disabled() { return g_paths.no_fused != 0; }
 bool expert1_enabled() { return !fused_disabled(); }
+
+// With debug_sync set, an entry point that enqueued its kernels waits for them
+// and reports a fault or launch failure as FMOE_ERR_HIP.
+fmoe_status finish(fmoe_status st, void* stream, const char* what) {
+  if (st != FMOE_OK || !g_paths.debug_sync) return st;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  return FMOE_OK;
+}
 
 fmoe_status check_router(int T, int H, int E, int k) {
   if (T < 0) return fail(FMOE_ERR_SHAPE, "T=%d must be >= 0", T);
@@ -226,6 +238,18 @@ fmoe_status check_router(int T, int H, int E, int k) {
 extern "C" {
 
 int32_t fmoe_abi_version(void) { return FMOE_ABI_VERSION; }
+
+void fmoe_get_paths(fmoe_paths* p) {
+  if (p) *p = g_paths;
+}
+
+fmoe_status fmoe_set_paths(const fmoe_paths* p) {
+  if (!p) return fail(FMOE_ERR_NULL, "paths is NULL");
+  if (p->mfma_min_tokens < 1)
+    return fail(FMOE_ERR_SHAPE, "mfma_min_tokens=%d must be >= 1", p->mfma_min_tokens);
+  g_paths = *p;
+  return FMOE_OK;
+}
 
 const char* fmoe_last_error(void) { return g_err; }
 
@@ -248,7 +272,7 @@ size_t fmoe_route_workspace_size(int32_t T, int32_t E) {
   return route_ws(T, E);
 }
 
-fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, int32_t H, int32_t E,
+static fmoe_status fmoe_route_topk_impl(const float* router_w, const float* x, int32_t T, int32_t H, int32_t E,
                             int32_t k, int32_t* idx, float* w, float* logits_out, void* ws,
                             size_t ws_bytes, void* stream) {
   fmoe_status st = check_router(T, H, E, k);
@@ -282,7 +306,7 @@ fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, in
   return FMOE_OK;
 }
 
-fmoe_status fmoe_dequant_gemv(const fmoe_qmat* W, const fmoe_qformat* fmt, const float* x,
+static fmoe_status fmoe_dequant_gemv_impl(const fmoe_qmat* W, const fmoe_qformat* fmt, const float* x,
                               float* y, void* stream) {
   QFmt f;
   fmoe_status st = check_fmt(fmt, &f);
@@ -302,7 +326,7 @@ size_t fmoe_expert_ffn_workspace_size(const fmoe_expert* e, const fmoe_qformat* 
   return ffn_ws(e->gate.k, e->gate.n).total;
 }
 
-fmoe_status fmoe_expert_ffn(const fmoe_expert* e, const fmoe_qformat* fmt, const float* x,
+static fmoe_status fmoe_expert_ffn_impl(const fmoe_expert* e, const fmoe_qformat* fmt, const float* x,
                             float* y, void* ws, size_t ws_bytes, void* stream) {
   QFmt f;
   fmoe_status st = check_fmt(fmt, &f);
@@ -350,7 +374,7 @@ size_t fmoe_workspace_size(const fmoe_layer* L, int32_t T) {
   return layer_ws(T, L->hidden, L->inter, L->n_experts, L->top_k, L->fmt.bits).total;
 }
 
-fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* x,
+static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, const float* x,
                                    const float* residual, float* h_out, float* y_out,
                                    int32_t* idx_out, float* w_out, float* moe_out, void* ws,
                                    size_t ws_bytes, void* stream) {
@@ -511,6 +535,33 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
     if (he != hipSuccess) return hip_fail(he, "combine kernel");
   }
   return FMOE_OK;
+}
+
+fmoe_status fmoe_route_topk(const float* router_w, const float* x, int32_t T, int32_t H, int32_t E,
+                            int32_t k, int32_t* idx, float* w, float* logits_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return finish(fmoe_route_topk_impl(router_w, x, T, H, E, k, idx, w, logits_out, ws, ws_bytes,
+                                     stream), stream, "route kernel (debug sync)");
+}
+
+fmoe_status fmoe_dequant_gemv(const fmoe_qmat* W, const fmoe_qformat* fmt, const float* x,
+                              float* y, void* stream) {
+  return finish(fmoe_dequant_gemv_impl(W, fmt, x, y, stream), stream, "gemv (debug sync)");
+}
+
+fmoe_status fmoe_expert_ffn(const fmoe_expert* e, const fmoe_qformat* fmt, const float* x,
+                            float* y, void* ws, size_t ws_bytes, void* stream) {
+  return finish(fmoe_expert_ffn_impl(e, fmt, x, y, ws, ws_bytes, stream), stream,
+                "expert FFN (debug sync)");
+}
+
+fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* x,
+                                   const float* residual, float* h_out, float* y_out,
+                                   int32_t* idx_out, float* w_out, float* moe_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return finish(fmoe_moe_layer_forward_impl(L, T, x, residual, h_out, y_out, idx_out, w_out,
+                                            moe_out, ws, ws_bytes, stream),
+                stream, "layer (debug sync)");
 }
 
 }  // extern "C"

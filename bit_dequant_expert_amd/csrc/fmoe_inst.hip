@@ -15,6 +15,21 @@ namespace fmoe {
 
 namespace {
 
+// Raises a matrix-core kernel's dynamic LDS limit to everything the CU has
+// beside its static LDS; done on the first launch of each kernel only.
+template <int G, int SB, int MODE>
+hipError_t allow_all_lds() {
+  static const hipError_t once = [] {
+    const void* fn = reinterpret_cast<const void*>(&k_moe_mfma<G, SB, MODE>);
+    hipFuncAttributes at{};
+    hipError_t e = hipFuncGetAttributes(&at, fn);
+    if (e != hipSuccess) return e;
+    const int dyn = kLdsPerCu - (int)at.sharedSizeBytes;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+  }();
+  return once;
+}
+
 template <int SB, int NS>
 hipError_t run_one(const VCall& c) {
   constexpr int B = FMOE_BITS, G = FMOE_GROUP;
@@ -76,11 +91,10 @@ hipError_t run_one(const VCall& c) {
       if constexpr (B != 4) {
         return hipErrorNotSupported;
       } else {
-        // More than 64 KB of dynamic LDS must be allowed per kernel first.
+        // More than 64 KB of dynamic LDS must be allowed per kernel first
+        // (once per kernel, for all the LDS a workgroup can have).
         const size_t lds = moe_mfma_lds(c.mode, c.mf->H, c.mf->I, G, SB);
-        const void* fn = c.mode == 0 ? reinterpret_cast<const void*>(&k_moe_mfma<G, SB, 0>)
-                                     : reinterpret_cast<const void*>(&k_moe_mfma<G, SB, 1>);
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = c.mode == 0 ? allow_all_lds<G, SB, 0>() : allow_all_lds<G, SB, 1>();
         if (e != hipSuccess) return e;
         if (c.mode == 0)
           hipLaunchKernelGGL((k_moe_mfma<G, SB, 0>), dim3(c.grid), dim3(kThreads), lds, c.st, *c.mf);

@@ -120,6 +120,7 @@ struct FusedArgs;
 // (fp16 words, one power-of-two scale per vector, scaled group sums) of the
 // tokens' x and of those experts' SwiGLU outputs, and where results go.
 constexpr int kMfmaTokens = 1;        // an expert with at least this many tokens takes the path
+constexpr int kLdsPerCu = 160 * 1024;  // LDS of one gfx950 compute unit
 constexpr int kMfmaMaxGroups = 128;   // K / G the path admits
 constexpr int kMfmaMaxI = 2048;       // down input images of a 16-token pass held in LDS
 constexpr int kMfmaMaxH = 8192;       // gate/up input images built in one pass of registers

@@ -120,6 +120,30 @@ typedef struct {
     float norm_eps;              /* RMSNorm epsilon (1e-6 in the configs here) */
 } fmoe_layer;
 
+/* Kernel-path selection, for cross-checking one path against another and for
+ * debugging; normal use never changes it.  The library reads the initial
+ * values once, when it is loaded, from the environment:
+ *   FMOE_NO_FUSED=1         multi-launch forms instead of the one-launch layer
+ *                           (T == 1) and single-expert kernels
+ *   FMOE_NO_MFMA=1          every expert of a batch on the multi-token GEMV
+ *                           kernels instead of the matrix cores
+ *   FMOE_MFMA_MIN_TOKENS=n  only experts with at least n tokens of a batch on
+ *                           the matrix cores, the rest on the GEMV kernels
+ *                           (default 1: every expert of a 4-bit batch)
+ *   FMOE_DEBUG_SYNC=1       every call synchronises its stream before returning
+ *                           and reports a kernel fault as FMOE_ERR_HIP (not
+ *                           usable under graph capture)
+ * The setting is process-wide; change it only while no call is in progress.
+ * fmoe_set_paths returns FMOE_ERR_SHAPE for mfma_min_tokens < 1. */
+typedef struct {
+    int32_t no_fused;
+    int32_t no_mfma;
+    int32_t mfma_min_tokens;
+    int32_t debug_sync;
+} fmoe_paths;
+void fmoe_get_paths(fmoe_paths *paths);
+fmoe_status fmoe_set_paths(const fmoe_paths *paths);
+
 /* Version of this interface (FMOE_ABI_VERSION). */
 int32_t fmoe_abi_version(void);
 

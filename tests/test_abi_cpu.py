@@ -149,3 +149,22 @@ def test_ffn_validation():
     e = fm.fmoe_expert(good, good, down)
     rc = fm.lib().fmoe_expert_ffn(C.byref(e), C.byref(f), A, A + 0x100000, A, 10, None)
     assert rc == fm.FMOE_ERR_WORKSPACE
+
+
+def test_path_selection_defaults_and_restore():
+    p = fm.fmoe_get_paths()
+    base = (p.no_fused, p.no_mfma, p.mfma_min_tokens, p.debug_sync)
+    if not any(k.startswith("FMOE_") for k in os.environ):
+        assert base == (0, 0, 1, 0)
+    with fm.paths(no_mfma=1, mfma_min_tokens=16):
+        q = fm.fmoe_get_paths()
+        assert (q.no_mfma, q.mfma_min_tokens) == (1, 16)
+    q = fm.fmoe_get_paths()
+    assert (q.no_fused, q.no_mfma, q.mfma_min_tokens, q.debug_sync) == base
+
+
+def test_path_selection_rejects_bad_threshold():
+    bad = fm.fmoe_get_paths()
+    bad.mfma_min_tokens = 0
+    assert fm.lib().fmoe_set_paths(C.byref(bad)) == fm.FMOE_ERR_SHAPE
+    assert fm.fmoe_get_paths().mfma_min_tokens >= 1

@@ -452,7 +452,7 @@ def test_expert_ffn_graph_replays_match_eager(layer4):
     assert _wait_timeouts(ws) == 0
 
 
-def test_expert_ffn_one_and_two_launches_agree(layer4, monkeypatch):
+def test_expert_ffn_one_and_two_launches_agree(layer4):
     """The one-launch expert FFN and the two-launch form (FMOE_NO_FUSED=1) agree
     within the tolerance, and each matches the oracle."""
     cfg = layer4.cfg
@@ -461,16 +461,15 @@ def test_expert_ffn_one_and_two_launches_agree(layer4, monkeypatch):
     ref = oracle.expert_ffn(layer4.slab_host(200), cfg.H, cfg.I, cfg.spec.bits, cfg.spec.group,
                             cfg.spec.sbytes, x.astype(np.float64))
     outs = []
-    for flag in ("0", "1"):
-        monkeypatch.setenv("FMOE_NO_FUSED", flag)
-        ws = torch.zeros(fm.fmoe_expert_ffn_workspace_size(e, layer4.fmt), dtype=torch.uint8,
-                         device="cuda")
-        y = torch.empty(cfg.H, device="cuda")
-        fm.fmoe_expert_ffn(e, layer4.fmt, dev(x), y, ws)
-        torch.cuda.synchronize()
+    for flag in (0, 1):
+        with fm.paths(no_fused=flag):
+            ws = torch.zeros(fm.fmoe_expert_ffn_workspace_size(e, layer4.fmt), dtype=torch.uint8,
+                             device="cuda")
+            y = torch.empty(cfg.H, device="cuda")
+            fm.fmoe_expert_ffn(e, layer4.fmt, dev(x), y, ws)
+            torch.cuda.synchronize()
         outs.append(y.cpu().numpy())
         assert rel_l2(outs[-1], ref) <= TOL, flag
-    monkeypatch.delenv("FMOE_NO_FUSED")
     assert rel_l2(outs[0], outs[1].astype(np.float64)) <= TOL
 
 
@@ -532,7 +531,7 @@ def test_layer4_correlated_batch(layer4):
     check_layer(layer4, x, x, got, [0, 23])
 
 
-def test_layer4_mfma_matches_gemv_path(layer4, monkeypatch):
+def test_layer4_mfma_matches_gemv_path(layer4):
     # The experts of a batch run on the matrix cores; FMOE_NO_MFMA=1 keeps
     # them on the multi-token GEMV.  Both fp16 activation forms must agree.
     cfg = layer4.cfg
@@ -540,15 +539,14 @@ def test_layer4_mfma_matches_gemv_path(layer4, monkeypatch):
     base = synth.activations(cfg, 1, pool=4)
     x = (base + 0.1 * synth.activations(cfg, 24, pool=5)).astype(np.float32)
     a = layer4.forward(x, x)
-    monkeypatch.setenv("FMOE_NO_MFMA", "1")
-    b = layer4.forward(x, x)
-    monkeypatch.delenv("FMOE_NO_MFMA")
+    with fm.paths(no_mfma=1):
+        b = layer4.forward(x, x)
     assert np.array_equal(a["idx"], b["idx"])
     for name in ("moe", "h", "y"):
         assert rel_l2(a[name], b[name]) <= 1e-3, name
 
 
-def test_layer4_mixed_threshold(layer4, monkeypatch):
+def test_layer4_mixed_threshold(layer4):
     # FMOE_MFMA_MIN_TOKENS=16: experts with >= 16 tokens on the matrix cores,
     # the others on the multi-token GEMV kernels, in the same layer.
     cfg = layer4.cfg
@@ -556,9 +554,8 @@ def test_layer4_mixed_threshold(layer4, monkeypatch):
     base = synth.activations(cfg, 1, pool=4)
     x = (base + 0.1 * synth.activations(cfg, 24, pool=5)).astype(np.float32)
     a = layer4.forward(x, x)
-    monkeypatch.setenv("FMOE_MFMA_MIN_TOKENS", "16")
-    b = layer4.forward(x, x)
-    monkeypatch.delenv("FMOE_MFMA_MIN_TOKENS")
+    with fm.paths(mfma_min_tokens=16):
+        b = layer4.forward(x, x)
     counts = np.bincount(b["idx"].ravel(), minlength=cfg.E)
     assert counts.max() >= 16 and (counts[counts > 0] < 16).any()
     assert np.array_equal(a["idx"], b["idx"])
@@ -648,8 +645,8 @@ def test_layer4_stack_chained_batch32():
 
 
 # ------------------------------------------------ one-launch layer kernel
-def test_fused_matches_multilaunch(layer4, monkeypatch):
-    # The one-token layer runs as one persistent launch; FMOE_NO_FUSED=1 forces
+def test_fused_matches_multilaunch(layer4):
+    # The one-token layer runs as one persistent launch; fmoe_paths.no_fused forces
     # the three-launch path.  Both must match the oracle and each other.
     cfg = layer4.cfg
     x = synth.activations(cfg, 3, pool=8)
@@ -657,9 +654,8 @@ def test_fused_matches_multilaunch(layer4, monkeypatch):
     for t in range(3):
         note(f"fused vs multi token {t}")
         a = layer4.forward(x[t:t + 1], x[t:t + 1], ws=ws)
-        monkeypatch.setenv("FMOE_NO_FUSED", "1")
-        b = layer4.forward(x[t:t + 1], x[t:t + 1], ws=ws)
-        monkeypatch.delenv("FMOE_NO_FUSED")
+        with fm.paths(no_fused=1):
+            b = layer4.forward(x[t:t + 1], x[t:t + 1], ws=ws)
         assert np.array_equal(a["idx"], b["idx"])
         for name in ("moe", "h", "y"):
             assert rel_l2(a[name], b[name]) <= 1e-4, name
