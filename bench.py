@@ -67,6 +67,9 @@ def parse(argv=None):
                         "byte counters of a profiler) and exit")
     p.add_argument("--no-stream-probe", action="store_true",
                    help="skip measuring the streaming-read ceiling")
+    p.add_argument("--phase-trace", type=int, default=0,
+                   help="run this many one-token layer calls on the phase-trace build and print "
+                        "the timeline of the kernel's phases (layer workloads only)")
     return p.parse_args(argv)
 
 
@@ -378,10 +381,56 @@ def spread(vals):
     return [round(vals[0], 3), round(vals[len(vals) // 2], 3), round(vals[int(len(vals) * 0.9)], 3)]
 
 
+TRACE_EVENTS = ["entry", "x staged", "logits stored", "shared SwiGLU published", "top-k known",
+                "routed SwiGLU published", "first images in LDS", "sum of squares published",
+                "every sum in", "exit", "down rows in registers", "wave 0 gate/up dots done",
+                "wave 3 gate/up dots done", "wave 3 down rows requested", "phase A loads issued",
+                "x in registers"]
+
+
+def phase_trace(args, torch, fm, step, R):
+    """Wall-clock stamps of the one-token kernel's phase boundaries (trace
+    build): per call, each workgroup's time of each event after the first
+    workgroup's entry; reported as the min / median / max over workgroups,
+    each the median over calls."""
+    import ctypes as C
+    import numpy as np
+    nwg, nev = 1024, 16
+    buf = torch.zeros(nwg * nev, dtype=torch.int64, device="cuda")
+    fm.lib().fmoe_trace_set.argtypes = [C.c_void_p]
+    fm.lib().fmoe_trace_set(buf.data_ptr())
+    s = torch.cuda.Stream()
+    per = []
+    for i in range(args.phase_trace + 8):
+        buf.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            step(i, s.cuda_stream)
+        torch.cuda.synchronize()
+        if i < 8:
+            continue
+        t = buf.view(nwg, nev).cpu().numpy().astype(np.float64)
+        live = t[:, 0] > 0
+        t0 = t[live, 0].min()
+        rows = []
+        for e in range(len(TRACE_EVENTS)):
+            v = t[live, e]
+            v = (v[v > 0] - t0) / 100.0          # 100 MHz ticks -> us
+            rows.append((v.min(), np.median(v), v.max()) if v.size else (np.nan,) * 3)
+        per.append(rows)
+    arr = np.median(np.array(per), axis=0)
+    return {"calls": args.phase_trace, "unit": "us after the first workgroup's entry",
+            "events": {name: {"min": round(float(a[0]), 3), "median": round(float(a[1]), 3),
+                              "max": round(float(a[2]), 3)}
+                       for name, a in zip(TRACE_EVENTS, arr)}}
+
+
 def bench_layer(args, torch):
     import math
     import bit_dequant_expert_amd as fm
     import synth
+    if args.phase_trace:
+        fm.use_trace_library()
 
     cfg = synth.CONFIGS[args.workload]
     sp = cfg.spec
@@ -430,6 +479,10 @@ def bench_layer(args, torch):
                 step(i, s.cuda_stream)
         torch.cuda.synchronize()
         print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
+        return
+    if args.phase_trace:
+        print(json.dumps({"phase_trace": phase_trace(args, torch, fm, step, R),
+                          "workload": args.workload, "kernel_source_hash": source_hash()}))
         return
 
     with torch.cuda.stream(s):

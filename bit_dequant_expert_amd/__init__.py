@@ -16,6 +16,17 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfmoe.so")
+# The phase-trace build (same kernels, plus wall-clock stamps of the one-token
+# kernel's phases); selected by use_trace_library() before the first call.
+TRACE_LIB_PATH = os.path.join(PKG, "libfmoe_trace.so")
+
+
+def use_trace_library():
+    """Load the phase-trace build instead of the plain one (before lib())."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = TRACE_LIB_PATH
 
 FMOE_OK, FMOE_ERR_NULL, FMOE_ERR_SHAPE, FMOE_ERR_ALIGN = 0, 1, 2, 3
 FMOE_ERR_UNSUPPORTED, FMOE_ERR_WORKSPACE, FMOE_ERR_HIP = 4, 5, 6
@@ -62,7 +73,8 @@ class fmoe_layer(C.Structure):
 
 class fmoe_paths(C.Structure):
     _fields_ = [("no_fused", C.c_int32), ("no_mfma", C.c_int32), ("mfma_min_tokens", C.c_int32),
-                ("debug_sync", C.c_int32)]
+                ("debug_sync", C.c_int32), ("t1_counters", C.c_int32),
+                ("wait_limit_us", C.c_int32), ("test_stall_part", C.c_int32)]
 
 
 _lib = None

@@ -18,11 +18,17 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfmoe.so")
+# Phase-trace variant (FMOE_TRACE): the one-token kernel stamps the wall clock
+# at its phase boundaries into a buffer given by fmoe_trace_set (bench.py
+# --phase-trace); same kernels otherwise.
+TRACE_BUILD = os.path.join(PKG, "_build_trace")
+TRACE_LIB = os.path.join(PKG, "libfmoe_trace.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
-DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=10"]
 VARIANTS = [(4, 32), (4, 64), (2, 32), (2, 64)]
 
 
@@ -42,41 +48,44 @@ def _run(cmd):
     return out
 
 
-def jobs():
-    os.makedirs(BUILD, exist_ok=True)
+def jobs(trace=False):
+    bdir = TRACE_BUILD if trace else BUILD
+    os.makedirs(bdir, exist_ok=True)
     hc = hipcc()
+    flags = [*COMMON, "-DFMOE_TRACE"] if trace else COMMON
     out = []
     for b, g in VARIANTS:
-        obj = os.path.join(BUILD, f"fmoe_inst_{b}_{g}.o")
-        out.append((obj, [hc, *COMMON, *DEVICE, "-x", "hip", f"-DFMOE_BITS={b}",
+        obj = os.path.join(bdir, f"fmoe_inst_{b}_{g}.o")
+        out.append((obj, [hc, *flags, *DEVICE, "-x", "hip", f"-DFMOE_BITS={b}",
                           f"-DFMOE_GROUP={g}", "-c", os.path.join(CSRC, "fmoe_inst.hip"),
                           "-o", obj]))
-    obj = os.path.join(BUILD, "fmoe_common.o")
-    out.append((obj, [hc, *COMMON, *DEVICE, "-x", "hip", "-c",
+    obj = os.path.join(bdir, "fmoe_common.o")
+    out.append((obj, [hc, *flags, *DEVICE, "-x", "hip", "-c",
                       os.path.join(CSRC, "fmoe_common.hip"), "-o", obj]))
-    obj = os.path.join(BUILD, "fmoe_api.o")
-    out.append((obj, [hc, *COMMON, "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+    obj = os.path.join(bdir, "fmoe_api.o")
+    out.append((obj, [hc, *flags, "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
                       "-x", "c++", "-c", os.path.join(CSRC, "fmoe_api.cpp"),
                       "-o", obj]))
     return out
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    if not force and os.path.exists(LIB):
-        return LIB
-    js = jobs()
+def build(force: bool = True, verbose: bool = False, trace: bool = False) -> str:
+    lib_path = TRACE_LIB if trace else LIB
+    if not force and os.path.exists(lib_path):
+        return lib_path
+    js = jobs(trace)
     workers = min(len(js), max(1, (os.cpu_count() or 4)), 8)
     with cf.ThreadPoolExecutor(workers) as ex:
         logs = list(ex.map(lambda j: _run(j[1]), js))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     logs.append(_run([hipcc(), "-shared", "-fPIC", "-o", tmp, *[o for o, _ in js]]))
     if verbose:
         txt = "\n".join(l for l in logs if l.strip())
         if txt:
             print(txt, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv))

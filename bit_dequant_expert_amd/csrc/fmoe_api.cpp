@@ -187,7 +187,10 @@ size_t route_ws(int T, int E) {
 
 // Kernel-path selection (include/fmoe.h, fmoe_paths): read from the
 // environment once when the library is loaded, changed only by fmoe_set_paths.
-fmoe_paths g_paths = {0, 0, fmoe::kMfmaTokens, 0};
+fmoe_paths g_paths = {0, 0, fmoe::kMfmaTokens, 0, 0, 0, 0};
+#ifdef FMOE_TRACE
+void* g_trace = nullptr;
+#endif
 
 bool env_flag(const char* name) {
   const char* v = getenv(name);
@@ -202,6 +205,10 @@ struct PathsFromEnv {
     const int n = v ? atoi(v) : 0;
     g_paths.mfma_min_tokens = n >= 1 ? n : fmoe::kMfmaTokens;
     g_paths.debug_sync = env_flag("FMOE_DEBUG_SYNC");
+    g_paths.t1_counters = env_flag("FMOE_T1_COUNTERS");
+    const char* w = getenv("FMOE_WAIT_LIMIT_US");
+    const int us = w ? atoi(w) : 0;
+    g_paths.wait_limit_us = us > 0 ? us : 0;
   }
 } g_paths_from_env;
 
@@ -239,6 +246,12 @@ extern "C" {
 
 int32_t fmoe_abi_version(void) { return FMOE_ABI_VERSION; }
 
+#ifdef FMOE_TRACE
+// Trace build only (not part of the interface): device buffer of
+// kTok1TraceEvents 64-bit stamps per workgroup of the one-token kernel.
+void fmoe_trace_set(void* dev_buf) { g_trace = dev_buf; }
+#endif
+
 void fmoe_get_paths(fmoe_paths* p) {
   if (p) *p = g_paths;
 }
@@ -247,6 +260,8 @@ fmoe_status fmoe_set_paths(const fmoe_paths* p) {
   if (!p) return fail(FMOE_ERR_NULL, "paths is NULL");
   if (p->mfma_min_tokens < 1)
     return fail(FMOE_ERR_SHAPE, "mfma_min_tokens=%d must be >= 1", p->mfma_min_tokens);
+  if (p->wait_limit_us < 0 || p->test_stall_part < 0)
+    return fail(FMOE_ERR_SHAPE, "wait_limit_us and test_stall_part must be >= 0");
   g_paths = *p;
   return FMOE_OK;
 }
@@ -432,6 +447,27 @@ static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, c
   src.stride = L->slab_stride;
   memcpy(src.off, off, sizeof off);
 
+  if (T == 1 && !fused_disabled() && !g_paths.t1_counters) {
+    fmoe::Tok1Args ta{};
+    ta.slabs = src.base;
+    ta.stride = src.stride;
+    memcpy(ta.off, src.off, sizeof ta.off);
+    ta.Wr = L->router_w; ta.wsg = L->shared_gate_w; ta.x = x; ta.resid = residual;
+    ta.gamma = L->norm_w; ta.h_out = h_out; ta.y_out = y_out; ta.moe_out = moe_out;
+    ta.w_out = w_out; ta.idx_out = idx_out; ta.eps = L->norm_eps;
+    ta.H = H; ta.I = I; ta.E = E; ta.k = k;
+    ta.area = wsb + fmoe::kFusedCtrBytes;
+    ta.timeout = (int*)(wsb + fmoe::wait_timeout_offset());
+    const uint64_t lim_us = g_paths.wait_limit_us > 0 ? (uint64_t)g_paths.wait_limit_us : 200000u;
+    ta.spin_ticks = lim_us * 100u;   // the wall clock runs at 100 MHz
+    ta.stall_part = g_paths.test_stall_part > 0 ? g_paths.test_stall_part - 1 : -1;
+#ifdef FMOE_TRACE
+    ta.trace = (uint64_t*)g_trace;
+#endif
+    hipError_t te = fmoe::launch_tok1(f, ta, s);
+    if (te == hipSuccess) return FMOE_OK;
+    if (te != hipErrorNotSupported) return hip_fail(te, "one-token layer kernel");
+  }
   if (T == 1 && fmoe::fused1_supported(H, I, E, f.bits) && !fused_disabled()) {
     fmoe::FusedArgs fa{};
     fa.src = src;

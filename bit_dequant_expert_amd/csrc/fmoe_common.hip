@@ -209,6 +209,58 @@ hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st) {
   return run_variant(c);
 }
 
+// The one-token layer with self-checking records (fmoe_tok1.h).  Shapes:
+// hidden rows of 64 or 128 segments, intermediate rows of 16, 32 or 64
+// segments with I <= H, E <= 2048, k + 1 <= 17 slots, at most 1024 down parts.
+// Grid: max(routed gate/up parts, down parts, shared row pairs), capped at the
+// resident workgroups (routed parts and shared pairs past the grid loop).
+// Every workgroup must hold a router row or a shared row pair (b < E or
+// b < I/2): both are published after the workgroup's last read of x and
+// polled by every workgroup before its first write of h_out, which may alias x.
+hipError_t launch_tok1(QFmt f, const Tok1Args& a_in, hipStream_t st) {
+  Tok1Args a = a_in;
+  const int H = a.H, I = a.I, E = a.E, k = a.k, bits = f.bits;
+  const int sh = H * bits / 128, si = I * bits / 128, W = 32 / bits;
+  if (!((sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64))) return hipErrorNotSupported;
+  if (E > kTok1MaxE || k + 1 > kTok1MaxSlots || H % 16 != 0 || I > H || I % 2 != 0)
+    return hipErrorNotSupported;
+  if (I > (bits == 4 ? kTok1MaxI4 : kTok1MaxI2)) return hipErrorNotSupported;
+  const int gr = fused_gu_rows(H, bits);
+  const int dr = 2 * 2 * rows_per_iter(I, bits);   // waves 2-3, two row iterations each
+  if (I % gr != 0 || gr % W != 0 || gr / W > 2 || gr > kWave || H % dr != 0)
+    return hipErrorNotSupported;
+  a.gu_rows = gr;
+  a.d_rows = dr;
+  a.nGUs = I / gr;
+  a.nD = H / dr;
+  if (a.nD > kTok1MaxParts) return hipErrorNotSupported;
+  const int n_gu = k * a.nGUs, n_sp = I / 2;
+  int want = n_gu > a.nD ? n_gu : a.nD;
+  if (n_sp > want) want = n_sp;
+  const size_t lds = fused_lds_bytes(H, I, bits);
+  const int ns = segs_per_lane(H, bits);
+  int occ = 0;
+  if (bits == 4 && f.group == 32) occ = tok1_occupancy_4_32(f.sb, ns, E, lds);
+  if (bits == 4 && f.group == 64) occ = tok1_occupancy_4_64(f.sb, ns, E, lds);
+  if (bits == 2 && f.group == 32) occ = tok1_occupancy_2_32(f.sb, ns, E, lds);
+  if (bits == 2 && f.group == 64) occ = tok1_occupancy_2_64(f.sb, ns, E, lds);
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 0;
+  }
+  const int cap = occ * n_cu;
+  const int grid = want < cap ? want : cap;
+  if (grid < 1 || a.nD > grid) return hipErrorNotSupported;
+  if (grid > (E > n_sp ? E : n_sp)) return hipErrorNotSupported;
+  VCall c = make_call(VCall::TOK1, f, ns, grid, st);
+  c.t1 = &a;
+  c.lds = lds;
+  return run_variant(c);
+}
+
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
   if (!fused1_supported(a.H, a.I, a.E, f.bits)) return hipErrorNotSupported;
   const size_t lds = fused_lds_bytes(a.H, a.I, f.bits);

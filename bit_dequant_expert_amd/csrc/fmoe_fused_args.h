@@ -20,10 +20,29 @@ constexpr size_t kFusedCtrBytes = (size_t)kFusedCtrLines * 256;
 constexpr int kFusedWaves = 4;
 constexpr int kFusedUD = 1;
 constexpr int kFusedMaxNormParts = 4 * 256;   // down parts the final norm sums
+// Record area of the one-token layer kernel (fmoe_tok1.h): the epoch line,
+// then up to kTok1MaxE logit records, up to kTok1MaxI2/2 shared-expert SwiGLU
+// records (two values each), up to kTok1MaxParts sum-of-squares records and
+// the routed SwiGLU block records of up to kTok1MaxSlots images (4 bytes per
+// element of the intermediate size in both code formats).
+constexpr int kTok1MaxE = 2048;
+constexpr int kTok1MaxParts = 1024;
+constexpr int kTok1MaxSlots = 17;
+constexpr int kTok1ImgBytesPerElem = 4;
+constexpr int kTok1MaxI4 = 2048, kTok1MaxI2 = 4096;
+constexpr size_t kTok1LogitOff = 256;
+constexpr size_t kTok1SharedOff = kTok1LogitOff + 16 * (size_t)kTok1MaxE;
+constexpr size_t kTok1PartOff = kTok1SharedOff + 16 * (size_t)(kTok1MaxI2 / 2);
+constexpr size_t kTok1ImgOff = kTok1PartOff + 16 * (size_t)kTok1MaxParts;
+constexpr size_t kTok1AreaBytes =
+    kTok1ImgOff + (size_t)kTok1MaxSlots * kTok1ImgBytesPerElem * kTok1MaxI2;
+
 // Every workspace layout keeps its data past this head, which holds only
-// counters that each call returns to zero: a call of any kind never leaves
-// data where another kind of call keeps its counters.
-constexpr size_t kWsReserved = kFusedCtrBytes;
+// counters that each call returns to zero and the one-token kernel's record
+// area (self-checking records, never read as data by another call kind): a
+// call of any kind never leaves data where another kind of call keeps its
+// counters or records.
+constexpr size_t kWsReserved = kFusedCtrBytes + kTok1AreaBytes;
 __host__ __device__ constexpr int fused_ug(int nsh) { return nsh == 1 ? 4 : 2; }
 inline int fused_gu_rows(int H, int bits) { return kFusedWaves * fused_ug(segs_per_lane(H, bits)); }
 inline int fused_d_rows(int I, int bits) { return kFusedWaves * kFusedUD * rows_per_iter(I, bits); }
@@ -58,6 +77,37 @@ struct FusedArgs {
   int gu_rows;       // gate/up rows per part
   int d_rows;        // down rows per part
 };
+
+// Arguments of the one-token layer kernel with self-checking records (fmoe_tok1.h).
+struct Tok1Args {
+  // The first 64 bytes hold what the kernel's first loads need (they are
+  // preloaded into scalar registers at wave launch where the hardware does so).
+  const float* x;
+  const float* Wr;
+  uint8_t* area;      // record area (kTok1AreaBytes)
+  const float* wsg;
+  const uint8_t* slabs;
+  int64_t stride;     // bytes between expert slabs; slab E is the shared expert
+  int H, I, E, k;
+  // the rest
+  int64_t off[9];     // section offsets within a slab
+  const float* resid;
+  const float* gamma;
+  float* h_out;
+  float* y_out;
+  float* moe_out;
+  float* w_out;
+  int32_t* idx_out;
+  float eps;
+  int* timeout;       // the workspace's timeout word
+  int nGUs;           // gate/up parts per expert (I / gu_rows)
+  int nD;             // down parts (H / d_rows)
+  int gu_rows, d_rows;
+  uint64_t spin_ticks;  // wall-clock limit of one wait (100 MHz ticks)
+  int stall_part;     // >= 0: that down part never publishes its sum (test of the timeout path)
+  uint64_t* trace;    // phase trace (builds with FMOE_TRACE only): kTok1TraceEvents per workgroup
+};
+constexpr int kTok1TraceEvents = 16;
 
 // Arguments of the one-launch single-expert FFN.
 struct Expert1Args {

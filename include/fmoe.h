@@ -134,12 +134,20 @@ typedef struct {
  *                           and reports a kernel fault as FMOE_ERR_HIP (not
  *                           usable under graph capture)
  * The setting is process-wide; change it only while no call is in progress.
- * fmoe_set_paths returns FMOE_ERR_SHAPE for mfma_min_tokens < 1. */
+ * fmoe_set_paths returns FMOE_ERR_SHAPE for mfma_min_tokens < 1 or a negative
+ * wait_limit_us or test_stall_part. */
 typedef struct {
     int32_t no_fused;
     int32_t no_mfma;
     int32_t mfma_min_tokens;
     int32_t debug_sync;
+    int32_t t1_counters;     /* 1: the one-token layer on the arrival-counter kernel instead
+                                of the self-checking-record kernel (FMOE_T1_COUNTERS=1) */
+    int32_t wait_limit_us;   /* bound of one in-kernel wait in microseconds; 0 = 200000
+                                (FMOE_WAIT_LIMIT_US) */
+    int32_t test_stall_part; /* tests of the timeout path only: n > 0 makes down part n-1 of
+                                the one-token kernel never publish, so the waits for it give
+                                up (bounded) and the call's outputs are NaN; 0 = off */
 } fmoe_paths;
 void fmoe_get_paths(fmoe_paths *paths);
 fmoe_status fmoe_set_paths(const fmoe_paths *paths);

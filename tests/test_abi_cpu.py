@@ -156,6 +156,7 @@ def test_path_selection_defaults_and_restore():
     base = (p.no_fused, p.no_mfma, p.mfma_min_tokens, p.debug_sync)
     if not any(k.startswith("FMOE_") for k in os.environ):
         assert base == (0, 0, 1, 0)
+        assert (p.t1_counters, p.wait_limit_us, p.test_stall_part) == (0, 0, 0)
     with fm.paths(no_mfma=1, mfma_min_tokens=16):
         q = fm.fmoe_get_paths()
         assert (q.no_mfma, q.mfma_min_tokens) == (1, 16)

@@ -254,6 +254,7 @@ class GpuLayer:
         fm.fmoe_moe_layer_forward(self.L, T, xd, rd, out["h"], out["y"], out["idx"], out["w"],
                                   out["moe"], ws)
         torch.cuda.synchronize()
+        assert _wait_timeouts(ws) == 0, "a bounded in-kernel wait gave up"
         return {k: v.cpu().numpy() for k, v in out.items()}
 
     def slab_host(self, e):
@@ -678,6 +679,68 @@ def test_fused_other_shapes(cfg):
     for t in range(4):
         got = gl.forward(x[t:t + 1], r[t:t + 1], ws=ws)
         check_layer(gl, x[t:t + 1], r[t:t + 1], got, [0])
+
+
+def test_one_token_kernels_agree(layer4):
+    # The one-token layer on self-checking records (default) and on arrival
+    # counters (fmoe_paths.t1_counters): same selection, outputs within 1e-5 of
+    # each other, both against the oracle.
+    cfg = layer4.cfg
+    x = synth.activations(cfg, 3, pool=11)
+    r = synth.normal(cfg.seed, 0, 59, (3, cfg.H))
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    for t in range(3):
+        note(f"records vs counters token {t}")
+        a = layer4.forward(x[t:t + 1], r[t:t + 1], ws=ws)
+        with fm.paths(t1_counters=1):
+            b = layer4.forward(x[t:t + 1], r[t:t + 1], ws=ws)
+        assert np.array_equal(a["idx"], b["idx"])
+        assert np.allclose(a["w"], b["w"], rtol=0, atol=1e-6)
+        for name in ("moe", "h", "y"):
+            assert rel_l2(a[name], b[name]) <= 1e-5, name
+        check_layer(layer4, x[t:t + 1], r[t:t + 1], a, [0])
+
+
+def test_one_token_many_calls_same_workspace(layer4):
+    # 300 calls back to back on one workspace (every call a new epoch of the
+    # records), cycling through 3 inputs: every call reproduces the first
+    # result of its input bit for bit, and no wait gives up.
+    cfg = layer4.cfg
+    note("one-token kernel, 300 calls")
+    x = dev(synth.activations(cfg, 3, pool=12))
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    h = torch.empty(300, cfg.H, device="cuda")
+    y = torch.empty(300, cfg.H, device="cuda")
+    for i in range(300):
+        j = i % 3
+        fm.fmoe_moe_layer_forward(layer4.L, 1, x[j], x[j], h[i], y[i], None, None, None, ws)
+    torch.cuda.synchronize()
+    assert _wait_timeouts(ws) == 0
+    for i in range(3, 300):
+        assert torch.equal(y[i], y[i % 3]) and torch.equal(h[i], h[i % 3]), i
+
+
+def test_one_token_wait_gives_up_loud(layer4):
+    # Forced from the host: down part 0 never publishes its sum of squares
+    # (fmoe_paths.test_stall_part) and the waits are bounded at 2 ms.  Every
+    # workgroup's norm wait gives up: y is NaN everywhere and the timeout word
+    # is set.  The next call on the same workspace is valid again.
+    cfg = layer4.cfg
+    note("one-token kernel, forced wait timeout")
+    x = synth.activations(cfg, 1, pool=13)
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 1), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    y = torch.empty(1, cfg.H, device="cuda")
+    h = torch.empty(1, cfg.H, device="cuda")
+    with fm.paths(wait_limit_us=2000, test_stall_part=1):
+        fm.fmoe_moe_layer_forward(layer4.L, 1, xd, xd, h, y, None, None, None, ws)
+        torch.cuda.synchronize()
+    assert _wait_timeouts(ws) == 1
+    assert torch.isnan(y).all()
+    off = fm.fmoe_wait_timeout_offset()
+    ws[off:off + 4].zero_()
+    got = layer4.forward(x, x, ws=ws)
+    check_layer(layer4, x, x, got, [0])
 
 
 def test_layer_graph_replays_match_eager(layer4):
