@@ -165,18 +165,15 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
 }
 
 struct FfnWs {
-  size_t ctr, act, xprep, abuf, ccnt, aprep, total;
+  size_t ctr, abuf, total;
 };
 
 FfnWs ffn_ws(int H, int I) {
+  (void)H;
   FfnWs w{};
   size_t pos = 0;
   w.ctr = pos; pos += fmoe::kWsReserved;   // same reserved head as every layout
-  w.act = pos; pos = align256(pos + act_ints(1, 1, 1) * 4);
-  w.xprep = pos; pos = align256(pos + fmoe::xprep_bytes(H));
-  w.abuf = pos; pos = align256(pos + (size_t)I * 4);
-  w.ccnt = pos; pos = align256(pos + (size_t)(I / 32) * 4);
-  w.aprep = pos; pos = align256(pos + fmoe::xprep_bytes(I));
+  w.abuf = pos; pos = align256(pos + (size_t)I * 4);   // SwiGLU output (fp32 or its image)
   w.total = pos;
   return w;
 }
@@ -389,10 +386,11 @@ size_t fmoe_workspace_size(const fmoe_layer* L, int32_t T) {
   return layer_ws(T, L->hidden, L->inter, L->n_experts, L->top_k, L->fmt.bits).total;
 }
 
-static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, const float* x,
-                                   const float* residual, float* h_out, float* y_out,
-                                   int32_t* idx_out, float* w_out, float* moe_out, void* ws,
-                                   size_t ws_bytes, void* stream) {
+// Host-side validation of a layer call's arguments (everything but the
+// workspace); FMOE_OK when the call may proceed.
+static fmoe_status layer_args_check(const fmoe_layer* L, int32_t T, const float* x,
+                                    const float* residual, const float* h_out, const float* y_out,
+                                    const float* moe_out) {
   if (!L) return fail(FMOE_ERR_NULL, "layer is NULL");
   QFmt f;
   fmoe_status st = check_fmt(&L->fmt, &f);
@@ -430,7 +428,20 @@ static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, c
   if (moe_out && (overlap(moe_out, vb, x, vb) || overlap(moe_out, vb, residual, vb) ||
                   overlap(moe_out, vb, h_out, vb) || overlap(moe_out, vb, y_out, vb)))
     return fail(FMOE_ERR_SHAPE, "moe_out overlaps another vector");
+  return FMOE_OK;
+}
 
+static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, const float* x,
+                                   const float* residual, float* h_out, float* y_out,
+                                   int32_t* idx_out, float* w_out, float* moe_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  fmoe_status st = layer_args_check(L, T, x, residual, h_out, y_out, moe_out);
+  if (st != FMOE_OK || T == 0) return st;
+  QFmt f;
+  check_fmt(&L->fmt, &f);
+  const int H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k;
+  int64_t off[9];
+  slab_layout(H, I, f, off);
   const LayerWs W = layer_ws(T, H, I, E, k, f.bits);
   if (!ws) return fail(FMOE_ERR_WORKSPACE, "ws is NULL");
   if (!aligned(ws, 256)) return fail(FMOE_ERR_ALIGN, "ws must be 256-byte aligned");
@@ -509,6 +520,10 @@ static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, c
   ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = mfma_thr;
   ra.xprep = use_gemv ? wsb + W.xprep : nullptr; ra.bits = f.bits;
   ra.n_prep_wgs = use_gemv ? (int)(((int64_t)T * (H / 32) + 31) / 32) : 0;
+  if (use_gemv) {
+    ra.ccnt = (int*)(wsb + W.ccnt);
+    ra.n_ccnt = (int)((size_t)T * kp1 * (I / 32));
+  }
   if (use_mfma) {   // the tokens' matrix-core images, in the same launch
     ra.ximg = (uint4*)(wsb + W.ximg);
     ra.xsc = (float*)(wsb + W.xsc);

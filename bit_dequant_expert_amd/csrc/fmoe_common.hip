@@ -311,16 +311,6 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_ffn_prep(int bits, const float* x, int H, uint8_t* xprep, int32_t* act, int maxA,
-                           hipStream_t st) {
-  const int grid = (H / 32 + kThreads / 8 - 1) / (kThreads / 8);
-  if (bits == 4)
-    hipLaunchKernelGGL(k_ffn_prep<4>, dim3(grid), dim3(kThreads), 0, st, x, H, xprep, act, maxA);
-  else
-    hipLaunchKernelGGL(k_ffn_prep<2>, dim3(grid), dim3(kThreads), 0, st, x, H, xprep, act, maxA);
-  return hipGetLastError();
-}
-
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_combine_norm, dim3(a.T), dim3(kThreads), 0, st, a);
   return hipGetLastError();

@@ -59,6 +59,8 @@ struct RouteArgs {
   int n_prep_wgs;
   uint4* ximg;             // per-token matrix-core images [T][H/8] or null
   float* xsc;              // their scales [T]
+  int* ccnt;               // gate/up completion counters, cleared by the prep workgroups
+  int n_ccnt;
 };
 
 // Slices of the hidden dim for the router's matrix product: enough
@@ -206,8 +208,6 @@ hipError_t launch_gemv_swiglu(QFmt f, const uint8_t* gq, const uint8_t* gs, cons
                               const uint8_t* uq, const uint8_t* us, const uint8_t* ub, int N,
                               int K, const float* x, float* a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
-hipError_t launch_ffn_prep(int bits, const float* x, int H, uint8_t* xprep, int32_t* act,
-                           int maxA, hipStream_t st);
 hipError_t launch_gateup(QFmt f, const GUArgs& a, int grid, hipStream_t st);
 hipError_t launch_down_combine(QFmt f, const DArgs& a, hipStream_t st);
 hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st);

@@ -145,24 +145,6 @@ __device__ __forceinline__ int block_exscan(int v, int* scratch, int& total) {
   return before + inc - v;
 }
 
-// ============================================================= FFN setup
-// Prepare one activation vector and a one-expert, one-entry active list.
-template <int BITS>
-__global__ __launch_bounds__(kThreads) void k_ffn_prep(const float* x, int H, uint8_t* xprep,
-                                                       int32_t* act, int maxA) {
-  const int nblk = H / 32;
-  const int blk = blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
-  prep_blocks<BITS, false>(x, xprep, H, blk < nblk ? blk : -1);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    act[0] = 1;
-    act[1] = 0;
-    act[2] = 0;                 // expert id 0
-    act[2 + maxA] = 0;          // entries offset
-    act[2 + 2 * maxA] = 1;      // one entry
-    act[2 + 4 * maxA] = 0;      // entry 0
-  }
-}
-
 // ================================================================ gate/up
 // [WAS] "3. Handoptimierte Metal Compute-Shader": dequant matrix-vector
 // products with the SwiGLU activation fused.  One launch covers every active

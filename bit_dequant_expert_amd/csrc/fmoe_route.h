@@ -46,6 +46,10 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
     // ---- activation prep for the gate/up products (independent of routing)
     if (!a.xprep) return;
     const int pb = blockIdx.x - nlog;
+    // The gate/up kernel's completion counters live in the workspace's data
+    // region, where a call of another shape may have left data: clear them
+    // here, one launch ahead of their first use.
+    for (int i = pb * kThreads + tid; i < a.n_ccnt; i += a.n_prep_wgs * kThreads) a.ccnt[i] = 0;
     const int per_tok = a.H / 32;
     const int gb = pb * (kThreads / 8) + (tid >> 3);
     const bool ok = gb < a.T * per_tok;

@@ -474,6 +474,23 @@ def test_expert_ffn_one_and_two_launches_agree(layer4):
     assert rel_l2(outs[0], outs[1].astype(np.float64)) <= TOL
 
 
+def test_workspace_shared_across_shapes(layer4):
+    # One workspace serves calls of several shapes and token counts in turn
+    # (batched on the GEMV and matrix-core paths, one-token, then a small
+    # layer whose gate/up counters sit where the others kept data): each call
+    # matches the oracle.
+    tiny = GpuLayer(synth.CONFIGS["tiny"])
+    ws = torch.zeros(fm.fmoe_workspace_size(layer4.L, 8), dtype=torch.uint8, device="cuda")
+    steps = [(tiny, 9), (layer4, 4), (layer4, 1), (tiny, 1), (tiny, 3), (layer4, 1), (tiny, 1)]
+    for i, (gl, T) in enumerate(steps):
+        cfg = gl.cfg
+        note(f"shared workspace step {i}: {cfg.name} T={T}")
+        x = synth.activations(cfg, T, pool=T + i)
+        r = synth.normal(cfg.seed, 3, 80 + i, (T, cfg.H))
+        got = gl.forward(x, r, ws=ws)
+        check_layer(gl, x, r, got, list(range(T)))
+
+
 def test_layer4_single_token(layer4):
     cfg = layer4.cfg
     x = synth.activations(cfg, 6, pool=1)
