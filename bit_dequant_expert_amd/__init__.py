@@ -40,7 +40,7 @@ ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_
                "fmoe_route_workspace_size", "fmoe_dequant_gemv", "fmoe_expert_ffn",
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
                "fmoe_workspace_size", "fmoe_wait_timeout_offset", "fmoe_get_paths",
-               "fmoe_set_paths")
+               "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc")
 
 
 class FmoeError(RuntimeError):
@@ -110,6 +110,9 @@ def lib() -> C.CDLL:
         L.fmoe_moe_layer_forward.argtypes = [C.POINTER(fmoe_layer), i32, P, P, P, P, P, P, P, P,
                                              sz, P]
         L.fmoe_moe_layer_forward.restype = C.c_int
+        L.fmoe_moe_layer_forward_noalloc.argtypes = [C.POINTER(fmoe_layer), i32, P, P, P, P, P,
+                                                     P, P, P]
+        L.fmoe_moe_layer_forward_noalloc.restype = C.c_int
         L.fmoe_workspace_size.argtypes = [C.POINTER(fmoe_layer), i32]
         L.fmoe_workspace_size.restype = sz
         _lib = L
@@ -247,6 +250,16 @@ def fmoe_moe_layer_forward(L: fmoe_layer, T: int, x, residual, h_out, y_out, idx
         C.byref(L), T, _ptr(x), _ptr(residual), _ptr(h_out), _ptr(y_out), _ptr(idx_out),
         _ptr(w_out), _ptr(moe_out), _ptr(ws), 0 if ws is None else _nbytes(ws),
         _stream(stream)))
+
+
+def fmoe_moe_layer_forward_noalloc(L: fmoe_layer, T: int, x, residual, h_out, y_out,
+                                   idx_out=None, w_out=None, moe_out=None, stream=None):
+    _check(lib().fmoe_moe_layer_forward_noalloc(
+        C.byref(L), T, _ptr(x), _ptr(residual), _ptr(h_out), _ptr(y_out), _ptr(idx_out),
+        _ptr(w_out), _ptr(moe_out), _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 16 << 20
 
 
 _raw_fwd = None

@@ -615,4 +615,28 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
                 stream, "layer (debug sync)");
 }
 
+fmoe_status fmoe_moe_layer_forward_noalloc(const fmoe_layer* L, int32_t T, const float* x,
+                                           const float* residual, float* h_out, float* y_out,
+                                           int32_t* idx_out, float* w_out, float* moe_out,
+                                           void* stream) {
+  static_assert(fmoe::kStaticScratchBytes == FMOE_STATIC_SCRATCH_BYTES, "scratch size");
+  fmoe_status st = layer_args_check(L, T, x, residual, h_out, y_out, moe_out);
+  if (st != FMOE_OK || T == 0) return st;
+  const size_t need = fmoe_workspace_size(L, T);
+  if (need > fmoe::kStaticScratchBytes)
+    return fail(FMOE_ERR_WORKSPACE,
+                "T=%d needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use fmoe_moe_layer_forward with a workspace)",
+                (int)T, need, fmoe::kStaticScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = fmoe::static_scratch((hipStream_t)stream, &ws);
+  if (e == hipErrorStreamCaptureUnsupported)
+    return fail(FMOE_ERR_HIP, "the first call on a device clears the static scratch and "
+                              "must not be under graph capture");
+  if (e != hipSuccess) return hip_fail(e, "static scratch set-up");
+  return finish(fmoe_moe_layer_forward_impl(L, T, x, residual, h_out, y_out, idx_out, w_out,
+                                            moe_out, ws, fmoe::kStaticScratchBytes, stream),
+                stream, "layer (debug sync)");
+}
+
 }  // extern "C"

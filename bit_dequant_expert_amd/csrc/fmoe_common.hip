@@ -1,5 +1,7 @@
 // fmoe_common.hip -- launchers of the format-independent kernels and the
 // dispatch of format-templated launches to their translation units.
+#include <mutex>
+
 #include "fmoe_mfma.h"
 #include "fmoe_route.h"
 
@@ -314,6 +316,41 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_combine_norm, dim3(a.T), dim3(kThreads), 0, st, a);
   return hipGetLastError();
+}
+
+// ===================================================== static scratch
+// The workspace of the allocation-free layer call: a file-scope device array
+// that every GPU the library runs on holds until the process ends.  In host
+// code `scratch` names a host-side stand-in; its device address, which differs
+// per GPU, is taken once per device below and only that address is handed to
+// kernels and memory calls.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(hipStream_t st, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // Set-up on the first call on this device: the address, then one clear
+    // (the layer's counters rest at zero between calls), ordered ahead of the
+    // call's kernels on its stream.  Outside graph capture only, so that no
+    // memory-set node is ever recorded.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(st, &cs)) != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    if ((e = hipMemsetAsync(p, 0, kStaticScratchBytes, st)) != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fmoe

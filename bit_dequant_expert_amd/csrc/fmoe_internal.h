@@ -223,6 +223,12 @@ hipError_t launch_tok1(QFmt f, const struct Tok1Args& a, hipStream_t st);
 // The single-expert FFN in one launch; hipErrorNotSupported when the shape
 // or the resident workgroups do not admit it (the caller then uses two).
 hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st);
+// Workspace of the allocation-free layer call: a static device array of
+// kStaticScratchBytes per GPU.  static_scratch returns this device's address
+// of it; the first call on a device takes the address and clears the array on
+// `st` (hipErrorStreamCaptureUnsupported if `st` is capturing then).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(hipStream_t st, void** ptr);
 // Byte offset of the counter block's wait-timeout word.
 size_t wait_timeout_offset();
 bool fused1_supported(int H, int I, int E, int bits);

@@ -220,6 +220,28 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer *L, int32_t T, const float *
                                    void *ws, size_t ws_bytes, void *stream);
 size_t fmoe_workspace_size(const fmoe_layer *L, int32_t T);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): fmoe_moe_layer_forward with
+ * the same arguments and results, minus the workspace.  Its workspace is a
+ * static device array of FMOE_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; the call allocates nothing.
+ *   - A layer that needs more than that (fmoe_workspace_size(L, T) >
+ *     FMOE_STATIC_SCRATCH_BYTES; T up to about 110 at hidden 4096 / inter 1024
+ *     / 512 experts) returns FMOE_ERR_WORKSPACE and enqueues nothing.
+ *   - The first call on each device takes the array's address and clears it
+ *     on `stream`; that first call must not be under graph capture
+ *     (FMOE_ERR_HIP otherwise).  Later calls may be captured.
+ *   - Every call on one GPU shares that GPU's array: calls whose execution
+ *     overlaps (other streams, other threads) race and give undefined results.
+ *     Calls in one stream are ordered and safe.
+ *   - A bounded in-kernel wait that gives up leaves NaN outputs (the timeout
+ *     word lives in the array and is not reachable by the caller). */
+#define FMOE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+fmoe_status fmoe_moe_layer_forward_noalloc(const fmoe_layer *L, int32_t T, const float *x,
+                                           const float *residual, float *h_out, float *y_out,
+                                           int32_t *idx_out, float *w_out, float *moe_out,
+                                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

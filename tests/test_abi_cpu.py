@@ -169,3 +169,23 @@ def test_path_selection_rejects_bad_threshold():
     bad.mfma_min_tokens = 0
     assert fm.lib().fmoe_set_paths(C.byref(bad)) == fm.FMOE_ERR_SHAPE
     assert fm.fmoe_get_paths().mfma_min_tokens >= 1
+
+
+def _fwd_noalloc(L, T=1, x=A, r=A + (1 << 20), h=A + (2 << 20), y=A + (3 << 20), moe=None):
+    return fm.lib().fmoe_moe_layer_forward_noalloc(C.byref(L), T, x, r, h, y, None, None, moe,
+                                                   None)
+
+
+def test_layer_noalloc_validation():
+    # Every argument error is reported before the static scratch is touched
+    # (no HIP call here), and so is a layer too large for the scratch.
+    assert _fwd_noalloc(_layer(bits=3)) == fm.FMOE_ERR_UNSUPPORTED
+    assert _fwd_noalloc(_layer(slabs=0)) == fm.FMOE_ERR_NULL
+    assert _fwd_noalloc(_layer(), y=A) == fm.FMOE_ERR_SHAPE
+    assert _fwd_noalloc(_layer(), T=0) == fm.FMOE_OK
+    L = _layer()
+    big = next(T for T in range(1, 4096) if fm.fmoe_workspace_size(L, T) > fm.STATIC_SCRATCH_BYTES)
+    assert fm.fmoe_workspace_size(L, big - 1) <= fm.STATIC_SCRATCH_BYTES
+    assert _fwd_noalloc(L, T=big, x=A, r=A + (big << 16), h=A + (2 * big << 16),
+                        y=A + (3 * big << 16)) == fm.FMOE_ERR_WORKSPACE
+    assert "static scratch" in fm.fmoe_last_error()
