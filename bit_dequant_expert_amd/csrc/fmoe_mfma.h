@@ -171,11 +171,18 @@ __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, in
 // (token) l % 16, k sub-block l / 16; D element i is token 4 (l / 16) + i,
 // weight row l % 16.  Needs K % 128 == 0.
 template <int G, int SB, int MODE>
-__global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
   constexpr int NM = MODE == 0 ? 2 : 1;   // matrices: gate and up, or down
   extern __shared__ __align__(16) uint4 lds4[];
   __shared__ float s_sc[16];
   __shared__ int s_ent[16];
+  // Per row of the workgroup: the largest |scale| or |bias| of the row in its
+  // matrices (gate and up, or down), as an fp32 bit pattern, gathered while the
+  // scales are staged.  The row's scales and biases enter fp16 times a power of
+  // two that puts that largest value in [2^10, 2^11) (so every dequantised fp16
+  // weight stays below 2^15), and the fp32 result is multiplied back: fp16's
+  // range does not limit the format's.
+  __shared__ uint32_t s_rmax[64];
   // Gate/up: kMoeGuRows rows per workgroup, S waves per 16-row tile, each
   // over a part of K; down: 64 rows, a wave's 16 rows over the whole K.
   constexpr int S = MODE == 0 ? kMoeGuSplit : 1;
@@ -204,6 +211,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
   const int SROW = moe_scl_row(K, G, SB);
   const int nl = tile * 16 + (lane & 15);   // row within the workgroup's
   const int om = MODE == 0 ? 0 : 6;
+  static_assert(RW <= 64, "row maxima");
+  if (tid < RW) s_rmax[tid] = 0u;   // ordered before the staging by the pass barriers
+  // |v| of the scale words of one 4-byte word (fp32: one value; bf16: two,
+  // as the fp32 bit patterns of their magnitudes), for an unsigned max.
+  auto word_max = [](uint32_t w) -> uint32_t {
+    if (SB == 4) return w & 0x7fffffffu;
+    return max(w & 0x7fffu, (w >> 16) & 0x7fffu) << 16;
+  };
+  auto chunk_max = [&](uint4 v) -> uint32_t {
+    return max(max(word_max(v.x), word_max(v.y)), max(word_max(v.z), word_max(v.w)));
+  };
   uint8_t* s_scl = reinterpret_cast<uint8_t*>(lds4);
   uint4* s_img = reinterpret_cast<uint4*>(s_scl + ((size_t)NM * 2 * RW * SROW + 15) / 16 * 16);
 
@@ -237,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         const int r = (k * 16) / rowb, c = k * 16 - r * rowb;
         uint32_t* d = reinterpret_cast<uint32_t*>(s_scl + (size_t)arr * RW * SROW + r * SROW + c);
         d[0] = sreg[j].x; d[1] = sreg[j].y; d[2] = sreg[j].z; d[3] = sreg[j].w;
+        atomicMax(&s_rmax[r], chunk_max(sreg[j]));
       }
     }
   };
@@ -252,12 +271,14 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
           const int r = (i * 16) / rowb, c = (i * 16) - r * rowb;
           uint32_t* d = reinterpret_cast<uint32_t*>(dst + r * SROW + c);
           d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+          atomicMax(&s_rmax[r], chunk_max(v));
         }
       } else {
         for (int i = tid; i < RW * rowb / 4; i += kThreads) {
           const uint32_t v = reinterpret_cast<const uint32_t*>(src)[i];
           const int r = (i * 4) / rowb, c = (i * 4) - r * rowb;
           *reinterpret_cast<uint32_t*>(dst + r * SROW + c) = v;
+          atomicMax(&s_rmax[r], word_max(v));
         }
       }
     }
@@ -288,6 +309,14 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
     f32x4 acc[NM];
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The power of two of the lane's weight row (see s_rmax): 2^-e into fp16.
+    auto row_shift = [&]() {
+      const float mx = __uint_as_float(s_rmax[nl]);
+      int ex = 0;
+      frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
+      return mx > 0.f ? min(max(ex - 11, -100), 100) : 0;
+    };
+    float rin = 1.f;
 
     auto run = [&](auto al_c) {
       constexpr bool AL = decltype(al_c)::value;          // activation words from LDS
@@ -318,7 +347,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
                                    : *reinterpret_cast<const float*>(sr);
           const float bv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(br))
                                    : *reinterpret_cast<const float*>(br);
-          const f16x2 s2 = {(_Float16)sv, (_Float16)sv}, b2 = {(_Float16)bv, (_Float16)bv};
+          const _Float16 sh = (_Float16)(sv * rin), bh = (_Float16)(bv * rin);
+          const f16x2 s2 = {sh, sh}, b2 = {bh, bh};
           const uint32_t cw[4] = {rq[u][mi].x, rq[u][mi].y, rq[u][mi].z, rq[u][mi].w};
 #pragma unroll
           for (int s = 0; s < 4; ++s)
@@ -373,6 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         }
       }
       __syncthreads();
+      rin = ldexpf(1.f, -row_shift());
       // Whole rings without branches while a whole next ring follows (the
       // load waits stay exact); then the ring in flight is computed while the
       // r blocks after it, if any, are requested, and those last.  No block
@@ -420,12 +451,13 @@ __global__ __launch_bounds__(kThreads) void k_moe_mfma(MfmaArgs a) {
         }
     }
 
+    const float rout = ldexpf(1.f, row_shift());
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * jg + i;
       if (m < pc) {
         const int p = s_ent[m];
-        const float sc = s_sc[m];
+        const float sc = s_sc[m] * rout;
         if (MODE == 0)
           a.abuf[(int64_t)p * a.I + n] = silu(acc[0][i] * sc) * (acc[NM - 1][i] * sc);
         else

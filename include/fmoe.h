@@ -51,7 +51,16 @@
  * Arithmetic: dot products accumulate in fp32.  Activations enter the
  *   dequantised products as fp16 values with a power-of-two scale per block
  *   of 32 (no overflow for any finite input); router logits accumulate in
- *   fp64 so that expert selection is exact.
+ *   fp64 so that expert selection is exact.  Calls with T > 1 run 4-bit
+ *   experts on the matrix cores, which form each dequantised weight in fp16
+ *   from fp16 copies of its scale and bias: the scales and biases of one weight
+ *   row (the gate and up rows of one index together) are first multiplied by
+ *   the power of two that puts the row's largest |scale| or |bias| in
+ *   [2^10, 2^11), and the fp32 result by its inverse.  Any finite fp32/bf16
+ *   scale or bias is therefore in range; a value more than 2^24 times smaller
+ *   than the largest of its row is held as an fp16 subnormal (less precise).
+ *   fmoe_paths.no_mfma keeps such batches on the GEMV kernels, which apply
+ *   scales and biases in fp32.
  */
 #ifndef FMOE_H
 #define FMOE_H
