@@ -21,6 +21,9 @@ Other workloads (not the default line):
   stack60  60 distinct 4-bit layers (217.8 GB of slabs) chained on the device
            (x_{l+1} = y_l, r_{l+1} = h_l) for a batch of 32 independent tokens;
            a step is the whole 60-layer pass, captured in one HIP graph.
+  chain60  the same 60 layers for one token (batch-1 decode through the whole
+           MoE stack): a step is the 60-layer pass, one HIP graph of 60
+           one-token layer launches.
 
 Prints one JSON line.  `value` is the achieved HBM throughput (algorithmic
 bytes / time); per-layer microseconds and tokens/s are reported beside it.
@@ -42,7 +45,7 @@ METRIC = ("µs per MoE layer & achieved HBM GB/s (% of peak), 4-bit, hidden 4096
 GRAPH_LEN = 64
 XPOOL = 64
 DEFAULT_STEPS = {"layer4": (640, 64), "layer2": (640, 64), "expert": (640, 64),
-                 "stack60": (20, 2)}
+                 "stack60": (20, 2), "chain60": (20, 2)}
 SPIN_US = 2000          # GPU busy-wait queued ahead of a timed region
 
 
@@ -54,9 +57,10 @@ def parse(argv=None):
                         "20 stacks)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps before (>= 0)")
     p.add_argument("--workload", default="layer4",
-                   choices=["layer4", "layer2", "expert", "stack60"],
+                   choices=["layer4", "layer2", "expert", "stack60", "chain60"],
                    help="layer4/layer2: one batch-1 layer per step; expert: one expert's "
-                        "gate/up/down per step; stack60: 60 chained layers x 32 tokens per step")
+                        "gate/up/down per step; stack60: 60 chained layers x 32 tokens per step; "
+                        "chain60: 60 chained layers x 1 token per step")
     p.add_argument("--replicas", type=int, default=32)
     p.add_argument("--cpu-sample", type=int, default=40, help="tokens timed on the oracle")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,9 +214,9 @@ def source_hash():
 
 def traffic_from_profiles(kernel_hash, workload):
     """HBM bytes per launch of the layer kernel, from the rocprofv3 counter
-    summary profiles/k_layer1_<workload>_traffic.txt when it was taken on this
+    summary profiles/k_layer1t_<workload>_traffic.txt when it was taken on this
     exact kernel source (its `source_hash:` line), else None."""
-    path = os.path.join(ROOT, "profiles", f"k_layer1_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"k_layer1t_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -349,6 +353,8 @@ def main():
         out = bench_expert(args, torch)
     elif args.workload == "stack60":
         out = bench_stack(args, torch)
+    elif args.workload == "chain60":
+        out = bench_chain(args, torch)
     else:
         out = bench_layer(args, torch)
     if out is not None:
@@ -383,7 +389,7 @@ def spread(vals):
 
 TRACE_EVENTS = ["entry", "x staged", "logits stored", "shared SwiGLU published", "top-k known",
                 "routed SwiGLU published", "first images in LDS", "sum of squares published",
-                "every sum in", "exit", "down rows in registers", "wave 0 gate/up dots done",
+                "every sum in", "exit", "(unused)", "wave 0 gate/up dots done",
                 "wave 3 gate/up dots done", "wave 3 down rows requested", "phase A loads issued",
                 "x in registers"]
 
@@ -422,7 +428,7 @@ def phase_trace(args, torch, fm, step, R):
     return {"calls": args.phase_trace, "unit": "us after the first workgroup's entry",
             "events": {name: {"min": round(float(a[0]), 3), "median": round(float(a[1]), 3),
                               "max": round(float(a[2]), 3)}
-                       for name, a in zip(TRACE_EVENTS, arr)}}
+                       for name, a in zip(TRACE_EVENTS, arr) if not np.isnan(a[1])}}
 
 
 def bench_layer(args, torch):
@@ -542,7 +548,7 @@ def bench_layer(args, torch):
         "pct_of_measured_stream_ceiling": None if not stream else round(100.0 * gbps / stream, 2),
         "algorithmic_bytes_per_layer": nbytes,
         "expert_bytes_per_layer": ebytes,
-        "roofline": {"bound": "hbm", "kernel": "k_layer1 (whole layer, one launch per step)",
+        "roofline": {"bound": "hbm", "kernel": "k_layer1t (whole layer, one launch per step)",
                      "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
@@ -863,6 +869,154 @@ def bench_stack(args, torch):
                                "sample": f"{n} layer-tokens of the stack's independent-routing "
                                          f"pass (route over 512 + 5 experts), {cus:.0f} us per "
                                          f"layer-token, scaled to 60 layers",
+                               "threads": f"1 thread of {os.cpu_count()} host logical cores",
+                               "cpu_model": host_cpu_model()}
+    return out
+
+
+def bench_chain(args, torch):
+    """Batch-1 decode through 60 distinct 4-bit layers chained on the device
+    (each layer's y and h are the next layer's x and residual); a step is the
+    whole 60-layer pass for one token, one HIP graph of 60 one-token layer
+    launches.  Each layer writes its own h and y, so that sampled layers can be
+    checked against the oracle fed the GPU's own layer inputs."""
+    import ctypes as C
+    import numpy as np
+    import bit_dequant_expert_amd as fm
+    import oracle
+    import synth
+
+    cfg = synth.CONFIGS["layer4"]
+    sp = cfg.spec
+    NL = 60
+    dev = torch.device("cuda:0")
+    off, stride = sp.layout()
+    print(f"[bench] generating {NL} layers ({NL * stride * (cfg.E + 1) / 1e9:.1f} GB)",
+          file=sys.stderr, flush=True)
+    fmt, layers = _fmt_and_layers(torch, fm, synth, cfg, range(NL), dev)
+    x0_host = synth.activations(cfg, 1, pool=40)
+    x0 = torch.from_numpy(x0_host).to(dev)
+    hs = torch.empty(NL, cfg.H, device=dev)
+    ys = torch.empty(NL, cfg.H, device=dev)
+    idx = torch.empty(NL, cfg.k, dtype=torch.int32, device=dev)
+    wts = torch.empty(NL, cfg.k, device=dev)
+    ws_bytes = fm.fmoe_workspace_size(layers[0], 1)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print("[bench] layers ready", file=sys.stderr, flush=True)
+    Lp = [C.addressof(L) for L in layers]
+
+    def step(i, stream):
+        x = r = x0.data_ptr()
+        for l in range(NL):
+            h, y = hs[l].data_ptr(), ys[l].data_ptr()
+            rc = fm.fmoe_moe_layer_forward_raw(Lp[l], 1, x, r, h, y, idx[l].data_ptr(),
+                                               wts[l].data_ptr(), None, ws.data_ptr(),
+                                               ws_bytes, stream)
+            if rc != 0:
+                raise fm.FmoeError(rc, fm.fmoe_last_error())
+            x, r = y, h
+
+    s = torch.cuda.Stream()
+    if args.kernel_steps:
+        with torch.cuda.stream(s):
+            for i in range(args.kernel_steps):
+                step(i, s.cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
+        return None
+
+    with torch.cuda.stream(s):
+        step(0, s.cuda_stream)                  # eager warm-up before capture
+    torch.cuda.synchronize()
+    runner = GraphRunner(torch, s, lambda i, cs: step(i, cs), 1)
+    timed = step_chunks(args.steps, 0, size=1)
+    warm = step_chunks(args.warmup, 0, size=1)
+    runner.prepare([(0, 1)])
+    runner.run(warm)
+    total_ms, wall_ms = runner.timed(timed)
+    rep_ms = runner.spread(0, 1, reps=min(args.steps, 10))
+    timeout_word = int(ws[fm.fmoe_wait_timeout_offset():][:4].view(torch.int32).item())
+    ms = total_ms / args.steps
+    us_layer = ms * 1000.0 / NL
+    nbytes, ebytes = layer_bytes(cfg)
+    gbps = nbytes / (us_layer * 1e-6) / 1e9
+    khash = source_hash()
+    out = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes x f16 activations, f32 accumulation (router f64)",
+        "data": "synthetic",
+        "config": {"workload": f"moe_chain60_h{cfg.H}_e{cfg.E}_i{cfg.I}_top{cfg.k}+1_batch1",
+                   "layers": NL, "batch": 1, "hidden": cfg.H, "experts": cfg.E,
+                   "inter": cfg.I, "top_k": cfg.k, "bits": sp.bits, "group": sp.group,
+                   "scale_dtype": "bf16", "resident_slab_gb": round(
+                       NL * stride * (cfg.E + 1) / 1e9, 1)},
+        "us_per_layer": round(us_layer, 3),
+        "decode_tokens_per_s_moe_stack": round(1e3 / ms, 2),
+        "ms_min_median_p90": spread(rep_ms),
+        "timed_region": {"event_ms": round(total_ms, 4), "host_wall_ms": round(wall_ms, 4),
+                         "note": f"exactly {args.steps} 60-layer passes (one graph each) between "
+                                 "two HIP events on the launch stream"},
+        "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "algorithmic_bytes_per_layer": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "k_layer1t (one launch per layer)",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_from_profiles(khash, "layer4")},
+        "wait_timeout_word": timeout_word,
+        "kernel_source_hash": khash,
+    }
+    # Parity of the timed pass: sampled layers against the oracle on the GPU's
+    # own inputs of that layer (teacher forcing); their oracle time is the CPU
+    # baseline.
+    hs_h, ys_h = hs.cpu().numpy(), ys.cpu().numpy()
+    idx_h, w_h = idx.cpu().numpy(), wts.cpu().numpy()
+    sample = [0, 1, 29, 58, 59] if args.cpu_sample >= 5 else [0, NL - 1]
+    parity = {"layers": sample, "index_mismatch": 0, "excluded_near_ties": 0,
+              "max_rel_l2": {"h": 0.0, "y": 0.0}}
+    t_oracle = 0.0
+    for l in sample:
+        x = x0_host[0] if l == 0 else ys_h[l - 1]
+        r = x0_host[0] if l == 0 else hs_h[l - 1]
+        Wr = synth.router(cfg, l)
+        t0 = time.perf_counter()
+        ridx, rw, rlg, gap, _ = oracle.route(Wr, x[None, :], cfg.k)
+        t_oracle += time.perf_counter() - t0
+        sel, wsel = ridx[0], rw[0]
+        if gap[0] < 1e-6:
+            parity["excluded_near_ties"] += 1
+            sel = idx_h[l]
+            z = rlg[0][sel] - rlg[0][sel].max()
+            wsel = np.exp(z) / np.exp(z).sum()
+        elif sorted(idx_h[l].tolist()) != sorted(sel.tolist()):
+            parity["index_mismatch"] += 1
+        slabs = [synth.slab(sp, cfg.seed, l, int(e)) for e in sel]
+        shared = synth.slab(sp, cfg.seed, l, cfg.E)
+        t0 = time.perf_counter()
+        ref = oracle.moe_token(slabs, wsel, shared, cfg.H, cfg.I, sp.bits, sp.group, sp.sbytes,
+                               synth.shared_gate(cfg, l), synth.gamma(cfg, l), cfg.eps, x, r)
+        t_oracle += time.perf_counter() - t0
+        parity["max_rel_l2"]["h"] = max(parity["max_rel_l2"]["h"], _rel(hs_h[l], ref["h"]))
+        parity["max_rel_l2"]["y"] = max(parity["max_rel_l2"]["y"], _rel(ys_h[l], ref["y"]))
+    parity["max_rel_l2"] = {k: float(f"{v:.3e}") for k, v in parity["max_rel_l2"].items()}
+    parity["pass"] = parity["index_mismatch"] == 0 and max(parity["max_rel_l2"].values()) <= 2e-3
+    out["parity_vs_oracle"] = parity
+    if not args.no_cpu_baseline:
+        cus = t_oracle / len(sample) * 1e6
+        out["cpu_baseline"] = {"value": round(1e6 / (NL * cus), 4), "unit": "tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{len(sample)} layers of the timed pass ({sample}), "
+                                         f"route over 512 + 5 experts each, {cus:.0f} us per "
+                                         "layer, scaled to 60 layers",
                                "threads": f"1 thread of {os.cpu_count()} host logical cores",
                                "cpu_model": host_cpu_model()}
     return out

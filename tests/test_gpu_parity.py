@@ -891,6 +891,47 @@ def test_layer4_stack60_acceptance():
     assert excluded <= 2
 
 
+def test_layer4_chain60_teacher_forced():
+    # Batch-1 decode through 60 distinct full-size layers chained on the device
+    # with the one-token kernel (y and h of each layer the next one's x and
+    # residual, one workspace): every layer against the oracle fed the GPU's own
+    # inputs of that layer.  One layer's slabs are on the device at a time; the
+    # oracle runs on CPU threads behind the GPU.
+    cfg = synth.CONFIGS["layer4"]
+    NL = 60
+    x = dev(synth.activations(cfg, 1, pool=40))
+    r = x.clone()
+    ws = None
+    ex = cf.ThreadPoolExecutor(max(2, min(14, (os.cpu_count() or 4) - 2)))
+    futs = []
+    try:
+        for l in range(NL):
+            note(f"chain60 layer {l}")
+            gl = GpuLayer(cfg, layer=l, random_gamma=False)
+            if ws is None:
+                ws = torch.zeros(fm.fmoe_workspace_size(gl.L, 1), dtype=torch.uint8,
+                                 device="cuda")
+            h = torch.empty_like(x)
+            y = torch.empty_like(x)
+            idx = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
+            w = torch.empty(1, cfg.k, device="cuda")
+            moe = torch.empty_like(x)
+            fm.fmoe_moe_layer_forward(gl.L, 1, x, r, h, y, idx, w, moe, ws)
+            torch.cuda.synchronize()
+            assert _wait_timeouts(ws) == 0
+            got = dict(h=h.cpu().numpy(), y=y.cpu().numpy(), moe=moe.cpu().numpy(),
+                       idx=idx.cpu().numpy(), w=w.cpu().numpy())
+            futs.append(ex.submit(check_layer, gl.host_side(), x.cpu().numpy(),
+                                  r.cpu().numpy(), got, [0]))
+            del gl
+            x, r = y, h
+        excluded = sum(f.result() for f in futs)
+    finally:
+        ex.shutdown(wait=True, cancel_futures=True)
+    note(f"chain60: {NL} layers checked, {excluded} near ties excluded")
+    assert excluded <= 1
+
+
 # ------------------------------------------------ one-launch layer kernel
 def test_fused_matches_multilaunch(layer4):
     # The one-token layer runs as one persistent launch; fmoe_paths.no_fused forces
