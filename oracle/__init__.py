@@ -61,6 +61,12 @@ def lib():
         L.or_layer_forward.argtypes = [P, P, i64, P, P, dbl, i32, i32, i32, i32, Fmt, i32,
                                        P, P, P, P, P, P, P, P, P, P, P]
         L.or_layer_forward.restype = i32
+        L.or_deltanet_step.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P]
+        L.or_deltanet_step.restype = None
+        L.or_rope_deinterleave.argtypes = [P, i32, i32, dbl, P]
+        L.or_rope_deinterleave.restype = None
+        L.or_attention_decode.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, dbl, P]
+        L.or_attention_decode.restype = None
         _lib = L
     return _lib
 
@@ -217,4 +223,45 @@ def layer_forward(Wr, slabs, slab_stride, wsg, gamma, eps, H, I, E, k,
                                 _p(out["logits"]), _p(out["gap"]), _p(out["g"]),
                                 _p(out["moe"]), _p(out["h"]), _p(out["y"]))
     out["status"] = st
+    return out
+
+
+# ------------------------------------------------- Gated DeltaNet, attention
+def deltanet_step(q, k, v, a, beta, state):
+    """One Gated DeltaNet decode step (fmoe_oracle_next.h).  q, k [B, NH, dk],
+    v [B, NH, dv], a, beta [B, NH], state [B, NH, dk, dv] (all fp32).  Returns
+    (new state, out) in fp64."""
+    B, NH, dk, dv = state.shape
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    a, beta, state = _c(a, np.float32), _c(beta, np.float32), _c(state, np.float32)
+    assert q.shape == (B, NH, dk) and k.shape == (B, NH, dk) and v.shape == (B, NH, dv)
+    assert a.shape == (B, NH) and beta.shape == (B, NH)
+    s_out = np.empty((B, NH, dk, dv), np.float64)
+    out = np.empty((B, NH, dv), np.float64)
+    lib().or_deltanet_step(_p(q), _p(k), _p(v), _p(a), _p(beta), _p(state), B, NH, dk, dv,
+                           _p(s_out), _p(out))
+    return s_out, out
+
+
+def rope_deinterleave(x, pos, base=10000.0):
+    x = _c(x, np.float32)
+    y = np.empty(x.shape[0], np.float64)
+    lib().or_rope_deinterleave(_p(x), x.shape[0], int(pos), float(base), _p(y))
+    return y
+
+
+def attention_decode(q, kc, vc, lens, base=10000.0):
+    """Decode attention (fmoe_oracle_next.h): q [B, NQ, D] fp32 (interleaved
+    pairs, unrotated), kc / vc [B, NKV, cap, D] bf16 bits (uint16), lens [B]
+    (>= 1).  Returns out [B, NQ, D] fp64."""
+    q = _c(q, np.float32)
+    kc, vc = _c(kc, np.uint16), _c(vc, np.uint16)
+    lens = _c(lens, np.int32)
+    B, NQ, D = q.shape
+    _, NKV, cap, _ = kc.shape
+    assert kc.shape == vc.shape == (B, NKV, cap, D) and lens.shape == (B,)
+    assert NQ % NKV == 0 and (lens >= 1).all() and (lens <= cap).all()
+    out = np.empty((B, NQ, D), np.float64)
+    lib().or_attention_decode(_p(q), _p(kc), _p(vc), _p(lens), B, NQ, NKV, D, cap, float(base),
+                              _p(out))
     return out

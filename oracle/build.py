@@ -7,7 +7,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "fmoe_oracle.c")
+SRC = [os.path.join(HERE, "fmoe_oracle.c"), os.path.join(HERE, "fmoe_oracle_next.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 # -O2 without fast-math; no contraction so every expression rounds as written.
@@ -19,7 +19,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(LIB):
         return LIB
     tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"]
+    cmd = ["gcc", *CFLAGS, "-o", tmp, *SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
