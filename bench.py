@@ -24,6 +24,10 @@ Other workloads (not the default line):
   chain60  the same 60 layers for one token (batch-1 decode through the whole
            MoE stack): a step is the 60-layer pass, one HIP graph of 60
            one-token layer launches.
+  deltanet one Gated DeltaNet decode step (fmoe_deltanet_step) of one
+           linear-attention layer for 32 sequences x 64 heads of 128 x 128 fp32
+           state (268 MB), rotating over 8 layers' states so that no step finds
+           its state in the Infinity Cache.
 
 Prints one JSON line.  `value` is the achieved HBM throughput (algorithmic
 bytes / time); per-layer microseconds and tokens/s are reported beside it.
@@ -45,7 +49,7 @@ METRIC = ("µs per MoE layer & achieved HBM GB/s (% of peak), 4-bit, hidden 4096
 GRAPH_LEN = 64
 XPOOL = 64
 DEFAULT_STEPS = {"layer4": (640, 64), "layer2": (640, 64), "expert": (640, 64),
-                 "stack60": (20, 2), "chain60": (20, 2)}
+                 "stack60": (20, 2), "chain60": (20, 2), "deltanet": (640, 64)}
 SPIN_US = 2000          # GPU busy-wait queued ahead of a timed region
 
 
@@ -57,7 +61,7 @@ def parse(argv=None):
                         "20 stacks)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps before (>= 0)")
     p.add_argument("--workload", default="layer4",
-                   choices=["layer4", "layer2", "expert", "stack60", "chain60"],
+                   choices=["layer4", "layer2", "expert", "stack60", "chain60", "deltanet"],
                    help="layer4/layer2: one batch-1 layer per step; expert: one expert's "
                         "gate/up/down per step; stack60: 60 chained layers x 32 tokens per step; "
                         "chain60: 60 chained layers x 1 token per step")
@@ -355,6 +359,8 @@ def main():
         out = bench_stack(args, torch)
     elif args.workload == "chain60":
         out = bench_chain(args, torch)
+    elif args.workload == "deltanet":
+        out = bench_deltanet(args, torch)
     else:
         out = bench_layer(args, torch)
     if out is not None:
@@ -1020,6 +1026,116 @@ def bench_chain(args, torch):
                                "threads": f"1 thread of {os.cpu_count()} host logical cores",
                                "cpu_model": host_cpu_model()}
     return out
+
+
+def bench_deltanet(args, torch):
+    """One Gated DeltaNet decode step per timed step: 32 sequences x 64 heads of a
+    128 x 128 fp32 state, updated in place; step i works on layer i mod 8's
+    state and input set i mod 8.  Algorithmic bytes: the state read and written
+    once, plus q, k, v, decay, beta read and the output written."""
+    import numpy as np
+    import bit_dequant_expert_amd as fm
+    import oracle
+
+    B, NH, DK, DV, NL = 32, 64, 128, 128, 8
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(2027)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    states = [(torch.randn(B, NH, DK, DV, generator=g) * 0.3).to(dev) for _ in range(NL)]
+    ins = []
+    for _ in range(NL):
+        ins.append(dict(q=unit(torch.randn(B, NH, DK, generator=g)).to(dev),
+                        k=unit(torch.randn(B, NH, DK, generator=g)).to(dev),
+                        v=torch.randn(B, NH, DV, generator=g).to(dev),
+                        a=torch.empty(B, NH).uniform_(0.5, 1.0, generator=g).to(dev),
+                        b=torch.empty(B, NH).uniform_(0.0, 1.0, generator=g).to(dev)))
+    out = torch.empty(B, NH, DV, device=dev)
+    # a copy of layer 0's state before any step, for the parity check
+    s0_host = states[0].cpu().numpy()
+    torch.cuda.synchronize()
+    lib = fm.lib()
+
+    def step(i, stream):
+        l = i % NL
+        x = ins[l]
+        rc = lib.fmoe_deltanet_step(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(),
+                                    x["a"].data_ptr(), x["b"].data_ptr(), states[l].data_ptr(),
+                                    out.data_ptr(), B, NH, DK, DV, stream)
+        if rc != 0:
+            raise fm.FmoeError(rc, fm.fmoe_last_error())
+
+    s = torch.cuda.Stream()
+    # parity first: one step on layer 0 against the oracle (sampled heads)
+    with torch.cuda.stream(s):
+        step(0, s.cuda_stream)
+    torch.cuda.synchronize()
+    got_s, got_o = states[0].cpu().numpy(), out.cpu().numpy()
+    x0 = {k: v.cpu().numpy() for k, v in ins[0].items()}
+    sample_b = [0, 7, 31]
+    t0 = time.perf_counter()
+    rs, ro = oracle.deltanet_step(x0["q"][sample_b], x0["k"][sample_b], x0["v"][sample_b],
+                                  x0["a"][sample_b], x0["b"][sample_b], s0_host[sample_b])
+    t_oracle = time.perf_counter() - t0
+    worst = 0.0
+    for j, b in enumerate(sample_b):
+        for h in range(NH):
+            worst = max(worst, _rel(got_o[b, h], ro[j, h]), _rel(got_s[b, h], rs[j, h]))
+    if args.kernel_steps:
+        with torch.cuda.stream(s):
+            for i in range(args.kernel_steps):
+                step(i, s.cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
+        return None
+
+    runner = GraphRunner(torch, s, step, NL)
+    timed = step_chunks(args.steps, 0)
+    warm = step_chunks(args.warmup, args.steps)
+    runner.prepare(warm + timed)
+    runner.run(warm)
+    torch.cuda.synchronize()
+    total_ms, wall_ms = runner.timed(timed)
+    ms = total_ms / args.steps
+    state_bytes = B * NH * DK * DV * 4
+    nbytes = 2 * state_bytes + B * NH * (2 * DK + 2 * DV + 2) * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "µs per Gated DeltaNet decode step (32 sequences x 64 heads) & achieved HBM GB/s",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"deltanet_step_b{B}_h{NH}_dk{DK}_dv{DV}", "sequences": B,
+                   "heads": NH, "dk": DK, "dv": DV, "layers_rotated": NL},
+        "us_per_step": round(ms * 1000.0, 3),
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "k_deltanet_step",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "parity_vs_oracle": {"sequences": sample_b, "heads": NH, "max_rel_l2": float(f"{worst:.3e}"),
+                             "pass": worst <= 2e-5},
+        "timed_region": {"event_ms": round(total_ms, 4), "host_wall_ms": round(wall_ms, 4)},
+        "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
+    }
+    if not args.no_cpu_baseline:
+        us_seq = t_oracle / len(sample_b) * 1e6
+        res["cpu_baseline"] = {"value": round(nbytes / (us_seq * B * 1e-6) / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{len(sample_b)} sequences x {NH} heads of the first "
+                                         f"step, {us_seq:.0f} us per sequence, scaled to {B}",
+                               "threads": f"1 thread of {os.cpu_count()} host logical cores",
+                               "cpu_model": host_cpu_model()}
+    return res
 
 
 if __name__ == "__main__":

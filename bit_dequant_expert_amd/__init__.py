@@ -40,7 +40,7 @@ ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_
                "fmoe_route_workspace_size", "fmoe_dequant_gemv", "fmoe_expert_ffn",
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
                "fmoe_workspace_size", "fmoe_wait_timeout_offset", "fmoe_get_paths",
-               "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc")
+               "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc", "fmoe_deltanet_step")
 
 
 class FmoeError(RuntimeError):
@@ -113,6 +113,8 @@ def lib() -> C.CDLL:
         L.fmoe_moe_layer_forward_noalloc.argtypes = [C.POINTER(fmoe_layer), i32, P, P, P, P, P,
                                                      P, P, P]
         L.fmoe_moe_layer_forward_noalloc.restype = C.c_int
+        L.fmoe_deltanet_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, P]
+        L.fmoe_deltanet_step.restype = C.c_int
         L.fmoe_workspace_size.argtypes = [C.POINTER(fmoe_layer), i32]
         L.fmoe_workspace_size.restype = sz
         _lib = L
@@ -260,6 +262,13 @@ def fmoe_moe_layer_forward_noalloc(L: fmoe_layer, T: int, x, residual, h_out, y_
 
 
 STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def fmoe_deltanet_step(q, k, v, decay, beta, state, out, stream=None):
+    """state [B, NH, dk, dv] is updated in place; shapes are taken from it."""
+    B, NH, dk, dv = state.shape
+    _check(lib().fmoe_deltanet_step(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta),
+                                    _ptr(state), _ptr(out), B, NH, dk, dv, _stream(stream)))
 
 
 _raw_fwd = None

@@ -62,6 +62,10 @@ def jobs(trace=False):
     obj = os.path.join(bdir, "fmoe_common.o")
     out.append((obj, [hc, *flags, *DEVICE, "-x", "hip", "-c",
                       os.path.join(CSRC, "fmoe_common.hip"), "-o", obj]))
+    for name in ("fmoe_deltanet",):
+        obj = os.path.join(bdir, f"{name}.o")
+        out.append((obj, [hc, *flags, *DEVICE, "-x", "hip", "-c",
+                          os.path.join(CSRC, f"{name}.hip"), "-o", obj]))
     obj = os.path.join(bdir, "fmoe_api.o")
     out.append((obj, [hc, *flags, "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
                       "-x", "c++", "-c", os.path.join(CSRC, "fmoe_api.cpp"),

@@ -615,6 +615,46 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
                 stream, "layer (debug sync)");
 }
 
+static fmoe_status fmoe_deltanet_step_impl(const float* q, const float* k, const float* v,
+                                           const float* decay, const float* beta, float* state,
+                                           float* out, int32_t batch, int32_t heads, int32_t dk,
+                                           int32_t dv, void* stream) {
+  if (batch < 0 || heads < 0) return fail(FMOE_ERR_SHAPE, "batch=%d and heads=%d must be >= 0", batch, heads);
+  if (!fmoe::deltanet_supported(dk, dv))
+    return fail(FMOE_ERR_UNSUPPORTED, "dk=%d must be 32, 64, 128 or 256 and dv=%d a positive "
+                "multiple of 32", dk, dv);
+  const size_t nbh = (size_t)batch * heads;
+  if (nbh == 0) return FMOE_OK;   // nothing to read or write
+  fmoe_status st;
+  if ((st = check_vec(q, "q")) != FMOE_OK) return st;
+  if ((st = check_vec(k, "k")) != FMOE_OK) return st;
+  if ((st = check_vec(v, "v")) != FMOE_OK) return st;
+  if ((st = check_vec(state, "state")) != FMOE_OK) return st;
+  if ((st = check_vec(out, "out")) != FMOE_OK) return st;
+  if (!decay) return fail(FMOE_ERR_NULL, "decay is NULL");
+  if (!beta) return fail(FMOE_ERR_NULL, "beta is NULL");
+  const size_t sb = nbh * dk * dv * 4, ob = nbh * dv * 4;
+  if (overlap(out, ob, state, sb) || overlap(out, ob, q, nbh * dk * 4) ||
+      overlap(out, ob, k, nbh * dk * 4) || overlap(out, ob, v, ob))
+    return fail(FMOE_ERR_SHAPE, "out overlaps the state or an input");
+  if (overlap(state, sb, q, nbh * dk * 4) || overlap(state, sb, k, nbh * dk * 4) ||
+      overlap(state, sb, v, ob) || overlap(state, sb, decay, nbh * 4) ||
+      overlap(state, sb, beta, nbh * 4))
+    return fail(FMOE_ERR_SHAPE, "state overlaps an input");
+  fmoe::DeltaNetArgs p{q, k, v, decay, beta, state, out, batch, heads, dk, dv};
+  const hipError_t e = fmoe::launch_deltanet(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "deltanet kernel");
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_deltanet_step(const float* q, const float* k, const float* v, const float* decay,
+                               const float* beta, float* state, float* out, int32_t batch,
+                               int32_t heads, int32_t dk, int32_t dv, void* stream) {
+  return finish(fmoe_deltanet_step_impl(q, k, v, decay, beta, state, out, batch, heads, dk, dv,
+                                        stream),
+                stream, "deltanet (debug sync)");
+}
+
 fmoe_status fmoe_moe_layer_forward_noalloc(const fmoe_layer* L, int32_t T, const float* x,
                                            const float* residual, float* h_out, float* y_out,
                                            int32_t* idx_out, float* w_out, float* moe_out,

@@ -229,6 +229,16 @@ hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st);
 // `st` (hipErrorStreamCaptureUnsupported if `st` is capturing then).
 constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 hipError_t static_scratch(hipStream_t st, void** ptr);
+// One Gated DeltaNet decode step (fmoe_deltanet.hip): B sequences x NH heads,
+// state [B][NH][dk][dv] updated in place, out [B][NH][dv].
+struct DeltaNetArgs {
+  const float *q, *k, *v, *decay, *beta;
+  float* state;
+  float* out;
+  int B, NH, dk, dv;
+};
+bool deltanet_supported(int dk, int dv);
+hipError_t launch_deltanet(const DeltaNetArgs& p, hipStream_t st);
 // Byte offset of the counter block's wait-timeout word.
 size_t wait_timeout_offset();
 bool fused1_supported(int H, int I, int E, int bits);

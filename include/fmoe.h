@@ -229,6 +229,24 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer *L, int32_t T, const float *
                                    void *ws, size_t ws_bytes, void *stream);
 size_t fmoe_workspace_size(const fmoe_layer *L, int32_t T);
 
+/* One decode step of the Gated DeltaNet state update for `batch` sequences x
+ * `heads` heads ([WAS] "4. Accelerate BLAS fuer Gated DeltaNet-Schichten": the
+ * 64-head state matrix of a linear-attention layer updated by a scale, a
+ * matrix-vector product and a rank-1 update).  Per (b, h), with the head's
+ * state S [dk x dv] (row-major: S[i][j] at i*dv + j), key k and query q [dk],
+ * value v [dv], decay a and write strength beta:
+ *   S <- a S;   u = S^T k;   S <- S + beta k (v - u)^T;   out = S^T q.
+ *   q, k [batch, heads, dk], v [batch, heads, dv], decay, beta [batch, heads],
+ *   state [batch, heads, dk, dv] (updated in place), out [batch, heads, dv];
+ *   all fp32; q, k, v, state and out 16-byte aligned.  dk in {32, 64, 128, 256},
+ *   dv a positive multiple of 32 (FMOE_ERR_UNSUPPORTED otherwise).  out must
+ *   not overlap anything, the state no input.  batch * heads == 0 is a no-op
+ *   (no pointer is read or checked).
+ * The step is one pass over the state (read once, written once), in fp32. */
+fmoe_status fmoe_deltanet_step(const float *q, const float *k, const float *v,
+                               const float *decay, const float *beta, float *state, float *out,
+                               int32_t batch, int32_t heads, int32_t dk, int32_t dv, void *stream);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): fmoe_moe_layer_forward with
  * the same arguments and results, minus the workspace.  Its workspace is a

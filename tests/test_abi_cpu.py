@@ -189,3 +189,22 @@ def test_layer_noalloc_validation():
     assert _fwd_noalloc(L, T=big, x=A, r=A + (big << 16), h=A + (2 * big << 16),
                         y=A + (3 * big << 16)) == fm.FMOE_ERR_WORKSPACE
     assert "static scratch" in fm.fmoe_last_error()
+
+
+def _dn(q=A, k=A + (1 << 20), v=A + (2 << 20), decay=A + (3 << 20), beta=A + (4 << 20),
+        state=A + (8 << 20), out=A + (64 << 20), B=2, NH=4, dk=128, dv=128):
+    return fm.lib().fmoe_deltanet_step(q, k, v, decay, beta, state, out, B, NH, dk, dv, None)
+
+
+def test_deltanet_validation():
+    assert _dn(dk=96) == fm.FMOE_ERR_UNSUPPORTED
+    assert _dn(dv=48) == fm.FMOE_ERR_UNSUPPORTED
+    assert _dn(dv=0) == fm.FMOE_ERR_UNSUPPORTED
+    assert _dn(B=-1) == fm.FMOE_ERR_SHAPE
+    assert _dn(q=0) == fm.FMOE_ERR_NULL
+    assert _dn(beta=0) == fm.FMOE_ERR_NULL
+    assert _dn(state=A + (8 << 20) + 4) == fm.FMOE_ERR_ALIGN
+    assert _dn(out=A + (8 << 20)) == fm.FMOE_ERR_SHAPE           # out inside the state
+    assert _dn(q=A + (8 << 20)) == fm.FMOE_ERR_SHAPE             # the state over q
+    assert _dn(B=0) == fm.FMOE_OK
+    assert _dn(NH=0) == fm.FMOE_OK
