@@ -28,6 +28,10 @@ Other workloads (not the default line):
            linear-attention layer for 32 sequences x 64 heads of 128 x 128 fp32
            state (268 MB), rotating over 8 layers' states so that no step finds
            its state in the Infinity Cache.
+  attention decode attention of one new token (fmoe_attention_decode) for 32
+           sequences, 32 query heads over 2 KV heads of dimension 256, a bf16
+           cache of up to 8192 positions with lengths drawn in [2048, 8192],
+           rotating over 4 layers' caches.
 
 Prints one JSON line.  `value` is the achieved HBM throughput (algorithmic
 bytes / time); per-layer microseconds and tokens/s are reported beside it.
@@ -49,7 +53,8 @@ METRIC = ("µs per MoE layer & achieved HBM GB/s (% of peak), 4-bit, hidden 4096
 GRAPH_LEN = 64
 XPOOL = 64
 DEFAULT_STEPS = {"layer4": (640, 64), "layer2": (640, 64), "expert": (640, 64),
-                 "stack60": (20, 2), "chain60": (20, 2), "deltanet": (640, 64)}
+                 "stack60": (20, 2), "chain60": (20, 2), "deltanet": (640, 64),
+                 "attention": (640, 64)}
 SPIN_US = 2000          # GPU busy-wait queued ahead of a timed region
 
 
@@ -61,7 +66,8 @@ def parse(argv=None):
                         "20 stacks)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps before (>= 0)")
     p.add_argument("--workload", default="layer4",
-                   choices=["layer4", "layer2", "expert", "stack60", "chain60", "deltanet"],
+                   choices=["layer4", "layer2", "expert", "stack60", "chain60", "deltanet",
+                            "attention"],
                    help="layer4/layer2: one batch-1 layer per step; expert: one expert's "
                         "gate/up/down per step; stack60: 60 chained layers x 32 tokens per step; "
                         "chain60: 60 chained layers x 1 token per step")
@@ -361,6 +367,8 @@ def main():
         out = bench_chain(args, torch)
     elif args.workload == "deltanet":
         out = bench_deltanet(args, torch)
+    elif args.workload == "attention":
+        out = bench_attention(args, torch)
     else:
         out = bench_layer(args, torch)
     if out is not None:
@@ -1133,6 +1141,115 @@ def bench_deltanet(args, torch):
                                "cores": 1, "kind": "oracle",
                                "sample": f"{len(sample_b)} sequences x {NH} heads of the first "
                                          f"step, {us_seq:.0f} us per sequence, scaled to {B}",
+                               "threads": f"1 thread of {os.cpu_count()} host logical cores",
+                               "cpu_model": host_cpu_model()}
+    return res
+
+
+def bench_attention(args, torch):
+    """Decode attention per timed step: 32 sequences, 32 query heads over 2 KV
+    heads of dimension 256, bf16 caches of capacity 8192 with lengths drawn in
+    [2048, 8192]; step i uses layer i mod 4's caches.  Algorithmic bytes: the
+    used part of K and V read once, q read, the output written."""
+    import numpy as np
+    import bit_dequant_expert_amd as fm
+    import oracle
+    import synth
+
+    B, NQ, NKV, D, CAP, NL = 32, 32, 2, 256, 8192, 4
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(2028)
+    lens_h = rng.integers(2048, CAP + 1, size=B).astype(np.int32)
+    g = torch.Generator(device="cpu").manual_seed(2028)
+    caches = []
+    for _ in range(NL):
+        k = torch.randn(B, NKV, CAP, D, generator=g).to(dev).to(torch.bfloat16).view(torch.int16)
+        v = torch.randn(B, NKV, CAP, D, generator=g).to(dev).to(torch.bfloat16).view(torch.int16)
+        caches.append((k, v))
+    qs = [torch.randn(B, NQ, D, generator=g).to(dev) for _ in range(NL)]
+    lens = torch.from_numpy(lens_h).to(dev)
+    out = torch.empty(B, NQ, D, device=dev)
+    wsb = fm.fmoe_attention_workspace_size(B, NKV, D, CAP)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    lib = fm.lib()
+
+    def step(i, stream):
+        l = i % NL
+        kc, vc = caches[l]
+        rc = lib.fmoe_attention_decode(qs[l].data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                                       lens.data_ptr(), B, NQ, NKV, D, CAP, 10000.0,
+                                       out.data_ptr(), ws.data_ptr(), wsb, stream)
+        if rc != 0:
+            raise fm.FmoeError(rc, fm.fmoe_last_error())
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(0, s.cuda_stream)
+    torch.cuda.synchronize()
+    # parity: sampled sequences of the first step against the oracle
+    sample_b = [0, 13, 31]
+    got = out.cpu().numpy()
+    q0 = qs[0].cpu().numpy()
+    k0 = caches[0][0].cpu().numpy().view(np.uint16)
+    v0 = caches[0][1].cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    ref = oracle.attention_decode(q0[sample_b], k0[sample_b], v0[sample_b], lens_h[sample_b])
+    t_oracle = time.perf_counter() - t0
+    worst = max(_rel(got[b, h], ref[j, h]) for j, b in enumerate(sample_b) for h in range(NQ))
+    if args.kernel_steps:
+        with torch.cuda.stream(s):
+            for i in range(args.kernel_steps):
+                step(i, s.cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
+        return None
+
+    runner = GraphRunner(torch, s, step, NL)
+    timed = step_chunks(args.steps, 0)
+    warm = step_chunks(args.warmup, args.steps)
+    runner.prepare(warm + timed)
+    runner.run(warm)
+    torch.cuda.synchronize()
+    total_ms, wall_ms = runner.timed(timed)
+    ms = total_ms / args.steps
+    used = int(lens_h.sum())
+    nbytes = 2 * NKV * used * D * 2 + 2 * B * NQ * D * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "µs per decode-attention step (32 sequences) & achieved HBM GB/s",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 cache x f32 query (matrix cores, query as two bf16 halves), f32 softmax",
+        "data": "synthetic",
+        "config": {"workload": f"attention_decode_b{B}_q{NQ}_kv{NKV}_d{D}_cap{CAP}",
+                   "sequences": B, "q_heads": NQ, "kv_heads": NKV, "head_dim": D,
+                   "cap": CAP, "lens": "uniform [2048, 8192], seed 2028",
+                   "mean_len": round(float(lens_h.mean()), 1), "layers_rotated": NL},
+        "us_per_step": round(ms * 1000.0, 3),
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "k_attn_chunk + k_attn_merge",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "parity_vs_oracle": {"sequences": sample_b, "max_rel_l2": float(f"{worst:.3e}"),
+                             "pass": worst <= 1e-4},
+        "timed_region": {"event_ms": round(total_ms, 4), "host_wall_ms": round(wall_ms, 4)},
+        "context": {"hbm_stream_read_gbps_measured": stream_probe(args, torch)},
+    }
+    if not args.no_cpu_baseline:
+        frac = float(lens_h[sample_b].sum()) / used
+        res["cpu_baseline"] = {"value": round(nbytes * frac / t_oracle / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"sequences {sample_b} of the first step "
+                                         f"({int(lens_h[sample_b].sum())} positions), "
+                                         f"{t_oracle * 1e3:.0f} ms",
                                "threads": f"1 thread of {os.cpu_count()} host logical cores",
                                "cpu_model": host_cpu_model()}
     return res

@@ -40,7 +40,8 @@ ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_
                "fmoe_route_workspace_size", "fmoe_dequant_gemv", "fmoe_expert_ffn",
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
                "fmoe_workspace_size", "fmoe_wait_timeout_offset", "fmoe_get_paths",
-               "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc", "fmoe_deltanet_step")
+               "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc", "fmoe_deltanet_step",
+               "fmoe_attention_decode", "fmoe_attention_workspace_size")
 
 
 class FmoeError(RuntimeError):
@@ -115,6 +116,11 @@ def lib() -> C.CDLL:
         L.fmoe_moe_layer_forward_noalloc.restype = C.c_int
         L.fmoe_deltanet_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, P]
         L.fmoe_deltanet_step.restype = C.c_int
+        L.fmoe_attention_decode.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, C.c_float, P,
+                                            P, sz, P]
+        L.fmoe_attention_decode.restype = C.c_int
+        L.fmoe_attention_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.fmoe_attention_workspace_size.restype = sz
         L.fmoe_workspace_size.argtypes = [C.POINTER(fmoe_layer), i32]
         L.fmoe_workspace_size.restype = sz
         _lib = L
@@ -262,6 +268,20 @@ def fmoe_moe_layer_forward_noalloc(L: fmoe_layer, T: int, x, residual, h_out, y_
 
 
 STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def fmoe_attention_workspace_size(batch, n_kv_heads, head_dim, cap) -> int:
+    return lib().fmoe_attention_workspace_size(batch, n_kv_heads, head_dim, cap)
+
+
+def fmoe_attention_decode(q, k_cache, v_cache, lens, out, ws, rope_base=10000.0, stream=None):
+    """q [B, NQ, D] fp32, caches [B, NKV, cap, D] bf16 bits (int16/uint16 tensors),
+    lens [B] int32 on the device, out [B, NQ, D]; shapes taken from q and the cache."""
+    B, NQ, D = q.shape
+    _, NKV, cap, _ = k_cache.shape
+    _check(lib().fmoe_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), B, NQ,
+                                       NKV, D, cap, float(rope_base), _ptr(out), _ptr(ws),
+                                       0 if ws is None else _nbytes(ws), _stream(stream)))
 
 
 def fmoe_deltanet_step(q, k, v, decay, beta, state, out, stream=None):

@@ -655,6 +655,57 @@ fmoe_status fmoe_deltanet_step(const float* q, const float* k, const float* v, c
                 stream, "deltanet (debug sync)");
 }
 
+size_t fmoe_attention_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                                     int32_t cap) {
+  if (batch < 0 || n_kv_heads <= 0 || head_dim <= 0 || cap < 0) return 0;
+  return fmoe::attention_ws_bytes(batch, n_kv_heads, head_dim, cap);
+}
+
+static fmoe_status fmoe_attention_decode_impl(const float* q, const uint16_t* k_cache,
+                                              const uint16_t* v_cache, const int32_t* lens,
+                                              int32_t batch, int32_t n_q_heads,
+                                              int32_t n_kv_heads, int32_t head_dim, int32_t cap,
+                                              float rope_base, float* out, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  if (batch < 0 || cap < 1) return fail(FMOE_ERR_SHAPE, "batch=%d must be >= 0 and cap=%d >= 1", batch, cap);
+  if (!fmoe::attention_supported(n_q_heads, n_kv_heads, head_dim))
+    return fail(FMOE_ERR_UNSUPPORTED, "head_dim=%d must be 64, 128 or 256 and n_q_heads=%d a "
+                "multiple of n_kv_heads=%d by at most 16", head_dim, n_q_heads, n_kv_heads);
+  if (!(rope_base > 1.f)) return fail(FMOE_ERR_SHAPE, "rope_base must be > 1");
+  if (batch == 0) return FMOE_OK;
+  fmoe_status st;
+  if ((st = check_vec(q, "q")) != FMOE_OK) return st;
+  if ((st = check_vec(k_cache, "k_cache")) != FMOE_OK) return st;
+  if ((st = check_vec(v_cache, "v_cache")) != FMOE_OK) return st;
+  if ((st = check_vec(out, "out")) != FMOE_OK) return st;
+  if (!lens) return fail(FMOE_ERR_NULL, "lens is NULL");
+  const size_t ob = (size_t)batch * n_q_heads * head_dim * 4;
+  const size_t cb = (size_t)batch * n_kv_heads * cap * head_dim * 2;
+  if (overlap(out, ob, q, ob) || overlap(out, ob, k_cache, cb) || overlap(out, ob, v_cache, cb))
+    return fail(FMOE_ERR_SHAPE, "out overlaps an input");
+  const size_t need = fmoe::attention_ws_bytes(batch, n_kv_heads, head_dim, cap);
+  if (!ws) return fail(FMOE_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(FMOE_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < need) return fail(FMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  if (overlap(ws, need, out, ob)) return fail(FMOE_ERR_SHAPE, "ws overlaps out");
+  fmoe::AttnArgs p{q, k_cache, v_cache, lens, out, (float*)ws, batch, n_q_heads, n_kv_heads,
+                   head_dim, cap, rope_base};
+  const hipError_t e = fmoe::launch_attention(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernels");
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_attention_decode(const float* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* lens, int32_t batch, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t cap,
+                                  float rope_base, float* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return finish(fmoe_attention_decode_impl(q, k_cache, v_cache, lens, batch, n_q_heads,
+                                           n_kv_heads, head_dim, cap, rope_base, out, ws,
+                                           ws_bytes, stream),
+                stream, "attention (debug sync)");
+}
+
 fmoe_status fmoe_moe_layer_forward_noalloc(const fmoe_layer* L, int32_t T, const float* x,
                                            const float* residual, float* h_out, float* y_out,
                                            int32_t* idx_out, float* w_out, float* moe_out,

@@ -239,6 +239,20 @@ struct DeltaNetArgs {
 };
 bool deltanet_supported(int dk, int dv);
 hipError_t launch_deltanet(const DeltaNetArgs& p, hipStream_t st);
+// Decode attention over a bf16 KV cache (fmoe_attention.hip).
+struct AttnArgs {
+  const float* q;          // [B][NQ][D], rotation pairs interleaved
+  const uint16_t* kc;      // [B][NKV][cap][D] bf16 bits, keys rotated (half-split order)
+  const uint16_t* vc;      // [B][NKV][cap][D] bf16 bits
+  const int32_t* lens;     // [B] positions in use (the new token's is lens - 1)
+  float* out;              // [B][NQ][D]
+  float* ws;               // attention_ws_bytes
+  int B, NQ, NKV, D, cap;
+  float base;              // rotary base
+};
+bool attention_supported(int NQ, int NKV, int D);
+size_t attention_ws_bytes(int B, int NKV, int D, int cap);
+hipError_t launch_attention(const AttnArgs& p, hipStream_t st);
 // Byte offset of the counter block's wait-timeout word.
 size_t wait_timeout_offset();
 bool fused1_supported(int H, int I, int E, int bits);

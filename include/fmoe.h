@@ -247,6 +247,35 @@ fmoe_status fmoe_deltanet_step(const float *q, const float *k, const float *v,
                                const float *decay, const float *beta, float *state, float *out,
                                int32_t batch, int32_t heads, int32_t dk, int32_t dv, void *stream);
 
+/* Decode attention of one new token per sequence over a bf16 KV cache, with
+ * the query's rotary embedding applied on the fly ([WAS] "3. Handoptimierte
+ * Metal Compute-Shader": GPU-side RoPE with the query de-interleaved, batched
+ * attention for the full-attention layers; the products Q K^T, softmax and
+ * scores V).  For sequence b, query head h and its KV head h / (n_q_heads /
+ * n_kv_heads), with L = lens[b] cached positions (the new token's key and
+ * value already at position L - 1) and D = head_dim:
+ *   q'[i] = q[2i] cos t_i - q[2i+1] sin t_i,  q'[i + D/2] = q[2i] sin t_i + q[2i+1] cos t_i,
+ *           t_i = (L - 1) rope_base^(-2i/D)
+ *   out[b,h] = sum_t softmax_t(q' . K_t / sqrt(D)) V_t,   t < L.
+ *   q [batch, n_q_heads, D] fp32 (rotation pairs interleaved, not yet rotated);
+ *   k_cache, v_cache [batch, n_kv_heads, cap, D] bf16 bits (keys rotated, in
+ *   half-split order); lens [batch] int32 DEVICE array with 1 <= lens[b] <= cap
+ *   (read by the kernels: a length outside that range is clamped into [0, cap],
+ *   and 0 gives NaN for that sequence); out [batch, n_q_heads, D] fp32.
+ *   D in {64, 128, 256}; n_q_heads a multiple of n_kv_heads by at most 16.
+ *   q, caches and out 16-byte aligned, out overlapping no input.
+ *   ws: fmoe_attention_workspace_size(batch, n_kv_heads, D, cap) bytes,
+ *   256-byte aligned, no initial contents needed.  batch == 0 is a no-op.
+ * Q K^T runs on the matrix cores with the rotated query split into two bf16
+ * halves (16 significant bits); the softmax and P V in fp32. */
+fmoe_status fmoe_attention_decode(const float *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                                  const int32_t *lens, int32_t batch, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t cap,
+                                  float rope_base, float *out, void *ws, size_t ws_bytes,
+                                  void *stream);
+size_t fmoe_attention_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                                     int32_t cap);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): fmoe_moe_layer_forward with
  * the same arguments and results, minus the workspace.  Its workspace is a

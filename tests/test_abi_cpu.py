@@ -208,3 +208,25 @@ def test_deltanet_validation():
     assert _dn(q=A + (8 << 20)) == fm.FMOE_ERR_SHAPE             # the state over q
     assert _dn(B=0) == fm.FMOE_OK
     assert _dn(NH=0) == fm.FMOE_OK
+
+
+def _att(q=A, kc=A + (1 << 24), vc=A + (2 << 24), lens=A + (3 << 24), B=2, NQ=32, NKV=2, D=256,
+         cap=512, base=10000.0, out=A + (4 << 24), ws=A + (5 << 24), ws_bytes=1 << 30):
+    return fm.lib().fmoe_attention_decode(q, kc, vc, lens, B, NQ, NKV, D, cap, base, out, ws,
+                                          ws_bytes, None)
+
+
+def test_attention_validation():
+    assert _att(D=96) == fm.FMOE_ERR_UNSUPPORTED
+    assert _att(NQ=48, NKV=2) == fm.FMOE_ERR_UNSUPPORTED     # 24 query heads per KV head
+    assert _att(NQ=30, NKV=4) == fm.FMOE_ERR_UNSUPPORTED
+    assert _att(cap=0) == fm.FMOE_ERR_SHAPE
+    assert _att(base=1.0) == fm.FMOE_ERR_SHAPE
+    assert _att(lens=0) == fm.FMOE_ERR_NULL
+    assert _att(q=A + 8) == fm.FMOE_ERR_ALIGN
+    assert _att(ws_bytes=100) == fm.FMOE_ERR_WORKSPACE
+    assert _att(ws=A + (5 << 24) + 16) == fm.FMOE_ERR_ALIGN
+    assert _att(out=A) == fm.FMOE_ERR_SHAPE                   # out over q
+    assert _att(B=0) == fm.FMOE_OK
+    # query operands (2 x 2 heads x 8 k-steps x 2 halves x 1 KiB), then 4 chunks of 128 per head
+    assert fm.fmoe_attention_workspace_size(2, 2, 256, 512) == 65536 + 2 * 2 * 4 * (32 + 16 * 256) * 4

@@ -1,7 +1,8 @@
 """GPU parity of the decode steps beside the MoE layer, through the C ABI,
-against the CPU oracle: the Gated DeltaNet state update (fmoe_deltanet_step).
+against the CPU oracle: the Gated DeltaNet state update (fmoe_deltanet_step)
+and decode attention with rotary embedding (fmoe_attention_decode).
 
-Bar: the step runs in fp32 with dot products over dk <= 256 terms; against the
+DeltaNet bar: the step runs in fp32 with dot products over dk <= 256 terms; against the
 fp64 oracle on the same fp32 inputs each head's output and new state must be
 within relative L2 2e-5 (fp32 rounding of a dk-term sum is about
 sqrt(dk) 2^-24 relative; the bar leaves a wide margin and still fails any
@@ -113,4 +114,91 @@ def test_deltanet_empty_is_noop():
     out = torch.zeros(0, 64, 128, device="cuda")
     z = torch.zeros(1, device="cuda")
     fm.fmoe_deltanet_step(z, z, z, z, z, st, out)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- attention
+# Bar: the rotated query enters the matrix cores as two bf16 halves (16
+# significant bits, relative rounding below 2^-16); scores, softmax and P V are
+# fp32.  A score error of e moves the probabilities by about e relative, so each
+# head's output must be within relative L2 1e-4 of the fp64 oracle (scores here
+# are O(1): a wrong term, index or rotation is off by far more).
+ATT_TOL = 1e-4
+
+
+def bf16_bits(x):
+    import synth
+    return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def att_inputs(rng, B, NQ, NKV, D, cap, qscale=1.0):
+    q = (rng.standard_normal((B, NQ, D)) * qscale).astype(np.float32)
+    kc = bf16_bits(rng.standard_normal((B, NKV, cap, D)))
+    vc = bf16_bits(rng.standard_normal((B, NKV, cap, D)))
+    return q, kc, vc
+
+
+def run_att(q, kc, vc, lens, base=10000.0):
+    B, NQ, D = q.shape
+    _, NKV, cap, _ = kc.shape
+    out = torch.empty(B, NQ, D, device="cuda")
+    ws = torch.empty(max(1, fm.fmoe_attention_workspace_size(B, NKV, D, cap)), dtype=torch.uint8,
+                     device="cuda")
+    kd = torch.from_numpy(kc.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc.view(np.int16)).cuda()
+    ld = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    fm.fmoe_attention_decode(dev(q), kd, vd, ld, out, ws, rope_base=base)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_att(got, ref):
+    worst = 0.0
+    for b in range(got.shape[0]):
+        for h in range(got.shape[1]):
+            e = rel_l2(got[b, h], ref[b, h])
+            worst = max(worst, e)
+            assert e <= ATT_TOL, (b, h, e)
+    return worst
+
+
+@pytest.mark.parametrize("B,NQ,NKV,D,cap,lens", [
+    (2, 32, 2, 256, 600, [600, 1]),          # 16 query heads per KV head, two chunks + a tail
+    (3, 8, 8, 128, 300, [1, 257, 300]),      # one query head per KV head, ragged lengths
+    (1, 16, 4, 64, 1000, [513]),             # head_dim 64, length just past two chunks
+    (2, 12, 3, 128, 256, [256, 255]),        # 4 heads per KV head, one full chunk
+])
+def test_attention_matches_oracle(B, NQ, NKV, D, cap, lens):
+    note(f"attention B={B} NQ={NQ} NKV={NKV} D={D} cap={cap} lens={lens}")
+    rng = np.random.default_rng(B * 100 + NQ + D + cap)
+    q, kc, vc = att_inputs(rng, B, NQ, NKV, D, cap)
+    got = run_att(q, kc, vc, lens)
+    ref = oracle.attention_decode(q, kc, vc, lens)
+    check_att(got, ref)
+
+
+def test_attention_long_context_and_peaked_scores():
+    # Positions up to 8191 (rotation angles far past 2 pi) and a query scaled so
+    # that each head's softmax is concentrated on a few positions.
+    B, NQ, NKV, D, cap = 2, 32, 2, 256, 8192
+    note("attention long context")
+    rng = np.random.default_rng(91)
+    q, kc, vc = att_inputs(rng, B, NQ, NKV, D, cap, qscale=4.0)
+    lens = [8192, 5000]
+    got = run_att(q, kc, vc, lens)
+    ref = oracle.attention_decode(q, kc, vc, lens)
+    check_att(got, ref)
+
+
+def test_attention_rope_base_and_empty_batch():
+    rng = np.random.default_rng(92)
+    q, kc, vc = att_inputs(rng, 1, 4, 1, 64, 40)
+    got = run_att(q, kc, vc, [37], base=1e6)
+    ref = oracle.attention_decode(q, kc, vc, [37], base=1e6)
+    check_att(got, ref)
+    out = torch.empty(0, 4, 64, device="cuda")
+    z = torch.zeros(1, device="cuda")
+    zc = torch.zeros(0, 1, 40, 64, dtype=torch.int16, device="cuda")
+    fm.fmoe_attention_decode(torch.empty(0, 4, 64, device="cuda"), zc, zc,
+                             torch.zeros(1, dtype=torch.int32, device="cuda"), out, z)
     torch.cuda.synchronize()
