@@ -32,6 +32,11 @@ Other workloads (not the default line):
            sequences, 32 query heads over 2 KV heads of dimension 256, a bf16
            cache of up to 8192 positions with lengths drawn in [2048, 8192],
            rotating over 4 layers' caches.
+  stream   batch-1 layers whose experts live in pinned host memory (two full
+           4-bit layers, 7.3 GB, alternating): a step routes the token on the
+           GPU, fetches its 4 routed experts and the shared one into the HBM
+           slab array (fmoe_fetch_experts, no host round trip) and runs the
+           layer on it.
 
 Prints one JSON line.  `value` is the achieved HBM throughput (algorithmic
 bytes / time); per-layer microseconds and tokens/s are reported beside it.
@@ -48,13 +53,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+HOST_LINK_GBPS = 64.0     # the GPU's host link, PCIe 5.0 x16, one direction
 METRIC = ("µs per MoE layer & achieved HBM GB/s (% of peak), 4-bit, hidden 4096, "
           "512 experts")
 GRAPH_LEN = 64
 XPOOL = 64
 DEFAULT_STEPS = {"layer4": (640, 64), "layer2": (640, 64), "expert": (640, 64),
                  "stack60": (20, 2), "chain60": (20, 2), "deltanet": (640, 64),
-                 "attention": (640, 64)}
+                 "attention": (640, 64), "stream": (64, 8)}
 SPIN_US = 2000          # GPU busy-wait queued ahead of a timed region
 
 
@@ -67,7 +73,7 @@ def parse(argv=None):
     p.add_argument("--warmup", type=int, default=None, help="untimed steps before (>= 0)")
     p.add_argument("--workload", default="layer4",
                    choices=["layer4", "layer2", "expert", "stack60", "chain60", "deltanet",
-                            "attention"],
+                            "attention", "stream"],
                    help="layer4/layer2: one batch-1 layer per step; expert: one expert's "
                         "gate/up/down per step; stack60: 60 chained layers x 32 tokens per step; "
                         "chain60: 60 chained layers x 1 token per step")
@@ -369,6 +375,8 @@ def main():
         out = bench_deltanet(args, torch)
     elif args.workload == "attention":
         out = bench_attention(args, torch)
+    elif args.workload == "stream":
+        out = bench_stream(args, torch)
     else:
         out = bench_layer(args, torch)
     if out is not None:
@@ -1253,6 +1261,144 @@ def bench_attention(args, torch):
                                "threads": f"1 thread of {os.cpu_count()} host logical cores",
                                "cpu_model": host_cpu_model()}
     return res
+
+
+def bench_stream(args, torch):
+    """Host-tier expert streaming at the full layer shape: two layers' 513 slabs
+    each in pinned host memory, one HBM slab array shared by both (tags = the
+    layer), step i runs layer i mod 2 on input vector i mod 64: route (device),
+    fetch the 5 active experts' slabs host -> HBM, layer forward.  Every step
+    misses (the other layer left its experts in the slots).  Reported: us per
+    layer with streaming, and the host-link bytes of the fetches per second of
+    fetch time."""
+    import ctypes as C
+    import numpy as np
+    import bit_dequant_expert_amd as fm
+    import synth
+
+    cfg = synth.CONFIGS["layer4"]
+    sp = cfg.spec
+    off, stride = sp.layout()
+    NL = 2
+    dev = torch.device("cuda:0")
+    nbytes_tier = stride * (cfg.E + 1)
+    print(f"[bench] pinning {NL * nbytes_tier / 1e9:.1f} GB of host slabs", file=sys.stderr, flush=True)
+    hosts = []
+    hbm = torch.empty(nbytes_tier, dtype=torch.uint8, device=dev)
+    for l in range(NL):
+        synth.fill_device_slabs(hbm.data_ptr(), sp, cfg.seed, l, 0, cfg.E + 1, stride)
+        h = torch.empty(nbytes_tier, dtype=torch.uint8, pin_memory=True)
+        h.copy_(hbm)
+        hosts.append(h)
+    torch.cuda.synchronize()
+    fmt = fm.qformat(sp.bits, sp.group, sp.sbytes == 2)
+    layers, routers = [], []
+    for l in range(NL):
+        Wr = torch.from_numpy(synth.router(cfg, l)).to(dev)
+        wsg = torch.from_numpy(synth.shared_gate(cfg, l)).to(dev)
+        gam = torch.from_numpy(synth.gamma(cfg, l)).to(dev)
+        routers.append(Wr)
+        layers.append(fm.fmoe_layer_desc(cfg.H, cfg.I, cfg.E, cfg.k, fmt, Wr, hbm, stride, wsg,
+                                         gam, cfg.eps))
+    tags = torch.full((cfg.E + 1,), -1, dtype=torch.int32, device=dev)
+    ncp = torch.zeros(1, dtype=torch.int32, device=dev)
+    xhost = synth.activations(cfg, XPOOL, pool=0)
+    xpool = torch.from_numpy(xhost).to(dev)
+    hbuf = torch.empty(XPOOL, cfg.H, device=dev)
+    ybuf = torch.empty(XPOOL, cfg.H, device=dev)
+    idx = torch.empty(XPOOL, cfg.k, dtype=torch.int32, device=dev)
+    wts = torch.empty(XPOOL, cfg.k, device=dev)
+    rws_b = fm.fmoe_route_workspace_size(1, cfg.E)
+    rws = torch.zeros(rws_b, dtype=torch.uint8, device=dev)
+    lws_b = fm.fmoe_workspace_size(layers[0], 1)
+    lws = torch.zeros(lws_b, dtype=torch.uint8, device=dev)
+    lib = fm.lib()
+    Lp = [C.addressof(L) for L in layers]
+    row = cfg.H * 4
+
+    def step(i, stream, fetch=True, layer_fwd=True):
+        l, j = i % NL, i % XPOOL
+        xi = xpool.data_ptr() + j * row
+        ii = idx[j].data_ptr()
+        rc = lib.fmoe_route_topk(routers[l].data_ptr(), xi, 1, cfg.H, cfg.E, cfg.k, ii,
+                                 wts[j].data_ptr(), None, rws.data_ptr(), rws_b, stream)
+        if rc == 0 and fetch:
+            rc = lib.fmoe_fetch_experts(ii, cfg.k, cfg.E, hosts[l].data_ptr(), stride, stride,
+                                        hbm.data_ptr(), tags.data_ptr(), cfg.E + 1, l,
+                                        ncp.data_ptr(), stream)
+        if rc == 0 and layer_fwd:
+            rc = fm.fmoe_moe_layer_forward_raw(Lp[l], 1, xi, xi, hbuf.data_ptr() + j * row,
+                                               ybuf.data_ptr() + j * row, None, None, None,
+                                               lws.data_ptr(), lws_b, stream)
+        if rc != 0:
+            raise fm.FmoeError(rc, fm.fmoe_last_error())
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in range(4):
+            step(i, s.cuda_stream)
+    torch.cuda.synchronize()
+    # parity: a few steps eagerly, outputs against the oracle
+    sample = [(i % NL, i % XPOOL) for i in range(4, 8)]
+    got = []
+    for i in range(4, 8):
+        with torch.cuda.stream(s):
+            step(i, s.cuda_stream)
+        torch.cuda.synchronize()
+        j = i % XPOOL
+        got.append((idx[j].cpu().numpy(), wts[j].cpu().numpy(), np.zeros(cfg.H),
+                    hbuf[j].cpu().numpy(), ybuf[j].cpu().numpy()))
+    cus, _, parity = cpu_baseline(cfg, sample, xhost, got)
+    parity["max_rel_l2"].pop("moe", None)
+    parity["pass"] = (parity["index_mismatch"] == 0 and parity["max_w_abs_err"] <= 1e-5
+                      and max(parity["max_rel_l2"].values()) <= 2e-3)
+    n0 = int(ncp.item())
+    runner = GraphRunner(torch, s, step, NL * XPOOL)
+    timed = step_chunks(args.steps, 8)
+    warm = step_chunks(args.warmup, 8 + args.steps)
+    runner.prepare(warm + timed)
+    runner.run(warm)
+    torch.cuda.synchronize()
+    n1 = int(ncp.item())
+    total_ms, wall_ms = runner.timed(timed)
+    n2 = int(ncp.item())
+    ms = total_ms / args.steps
+    # the same steps without the fetch (experts already in HBM for that layer
+    # would be the all-hit case): route + layer only
+    nofetch = GraphRunner(torch, s, lambda i, cs: step(i, cs, fetch=False), NL * XPOOL)
+    nofetch.prepare(timed)
+    nf_ms, _ = nofetch.timed(timed)
+    copied = (n2 - n1) / args.steps
+    link_gbps = copied * stride / max(1e-9, (ms - nf_ms / args.steps) * 1e-3) / 1e9
+    nbytes, _ = layer_bytes(cfg)
+    return {
+        "metric": "µs per MoE layer with host-tier expert streaming (4-bit, hidden 4096, 512 experts)",
+        "value": round(ms * 1000.0, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes x f16 activations, f32 accumulation (router f64)",
+        "data": "synthetic",
+        "config": {"workload": f"moe_stream_h{cfg.H}_e{cfg.E}_i{cfg.I}_top{cfg.k}+1_batch1",
+                   "layers_alternating": NL, "host_tier_gb": round(NL * nbytes_tier / 1e9, 1),
+                   "hbm_tier_gb": round(nbytes_tier / 1e9, 1)},
+        "slabs_copied_per_layer": round(copied, 3),
+        "us_per_layer_without_fetch": round(nf_ms / args.steps * 1000.0, 3),
+        "host_link_gbps_during_fetch": round(link_gbps, 1),
+        "fetch_note": "fetch time = step time minus the same steps without the fetch",
+        "roofline": {"bound": "host link", "kernel": "k_fetch",
+                     "achieved": round(link_gbps, 1), "peak": HOST_LINK_GBPS, "unit": "GB/s",
+                     "frac": round(link_gbps / HOST_LINK_GBPS, 4), "traffic": None,
+                     "peak_note": "PCIe 5.0 x16, one direction"},
+        "parity_vs_oracle": parity,
+        "timed_region": {"event_ms": round(total_ms, 4), "host_wall_ms": round(wall_ms, 4)},
+        "warmup_copies": n1 - n0,
+    }
 
 
 if __name__ == "__main__":

@@ -41,7 +41,7 @@ ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
                "fmoe_workspace_size", "fmoe_wait_timeout_offset", "fmoe_get_paths",
                "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc", "fmoe_deltanet_step",
-               "fmoe_attention_decode", "fmoe_attention_workspace_size")
+               "fmoe_attention_decode", "fmoe_attention_workspace_size", "fmoe_fetch_experts")
 
 
 class FmoeError(RuntimeError):
@@ -121,6 +121,8 @@ def lib() -> C.CDLL:
         L.fmoe_attention_decode.restype = C.c_int
         L.fmoe_attention_workspace_size.argtypes = [i32, i32, i32, i32]
         L.fmoe_attention_workspace_size.restype = sz
+        L.fmoe_fetch_experts.argtypes = [P, i32, i32, P, i64, i64, P, P, i32, i32, P, P]
+        L.fmoe_fetch_experts.restype = C.c_int
         L.fmoe_workspace_size.argtypes = [C.POINTER(fmoe_layer), i32]
         L.fmoe_workspace_size.restype = sz
         _lib = L
@@ -268,6 +270,13 @@ def fmoe_moe_layer_forward_noalloc(L: fmoe_layer, T: int, x, residual, h_out, y_
 
 
 STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def fmoe_fetch_experts(idx, n_idx, shared, host_slabs, slab_bytes, slab_stride, dev_slabs, tags,
+                       n_slots, tag, n_copied=None, stream=None):
+    _check(lib().fmoe_fetch_experts(_ptr(idx), n_idx, shared, _ptr(host_slabs), slab_bytes,
+                                    slab_stride, _ptr(dev_slabs), _ptr(tags), n_slots, tag,
+                                    _ptr(n_copied), _stream(stream)))
 
 
 def fmoe_attention_workspace_size(batch, n_kv_heads, head_dim, cap) -> int:

@@ -62,7 +62,7 @@ def jobs(trace=False):
     obj = os.path.join(bdir, "fmoe_common.o")
     out.append((obj, [hc, *flags, *DEVICE, "-x", "hip", "-c",
                       os.path.join(CSRC, "fmoe_common.hip"), "-o", obj]))
-    for name in ("fmoe_deltanet", "fmoe_attention"):
+    for name in ("fmoe_deltanet", "fmoe_attention", "fmoe_stream"):
         obj = os.path.join(bdir, f"{name}.o")
         out.append((obj, [hc, *flags, *DEVICE, "-x", "hip", "-c",
                           os.path.join(CSRC, f"{name}.hip"), "-o", obj]))

@@ -706,6 +706,51 @@ fmoe_status fmoe_attention_decode(const float* q, const uint16_t* k_cache, const
                 stream, "attention (debug sync)");
 }
 
+static fmoe_status fmoe_fetch_experts_impl(const int32_t* idx, int32_t n_idx, int32_t shared,
+                                           const void* host_slabs, int64_t slab_bytes,
+                                           int64_t slab_stride, void* dev_slabs, int32_t* tags,
+                                           int32_t n_slots, int32_t tag, int32_t* n_copied,
+                                           void* stream) {
+  if (n_idx < 0 || n_idx > kMaxSel) return fail(FMOE_ERR_SHAPE, "n_idx=%d must be in [0, %d]", n_idx, kMaxSel);
+  if (n_slots <= 0) return fail(FMOE_ERR_SHAPE, "n_slots=%d must be positive", n_slots);
+  if (shared < -1 || shared >= n_slots) return fail(FMOE_ERR_SHAPE, "shared=%d must be -1 or a slot", shared);
+  if (slab_bytes <= 0 || slab_bytes % 16 != 0)
+    return fail(FMOE_ERR_SHAPE, "slab_bytes=%lld must be a positive multiple of 16", (long long)slab_bytes);
+  if (slab_stride < slab_bytes || slab_stride % 16 != 0)
+    return fail(FMOE_ERR_SHAPE, "slab_stride=%lld must be a multiple of 16 and >= slab_bytes", (long long)slab_stride);
+  if (n_idx == 0 && shared < 0) return FMOE_OK;
+  if (n_idx > 0 && !idx) return fail(FMOE_ERR_NULL, "idx is NULL");
+  if (!host_slabs) return fail(FMOE_ERR_NULL, "host_slabs is NULL");
+  if (!dev_slabs) return fail(FMOE_ERR_NULL, "dev_slabs is NULL");
+  if (!tags) return fail(FMOE_ERR_NULL, "tags is NULL");
+  if (!aligned(host_slabs, 16) || !aligned(dev_slabs, 16))
+    return fail(FMOE_ERR_ALIGN, "host_slabs and dev_slabs must be 16-byte aligned");
+  const size_t span = (size_t)(n_slots - 1) * (size_t)slab_stride + (size_t)slab_bytes;
+  if (overlap(host_slabs, span, dev_slabs, span)) return fail(FMOE_ERR_SHAPE, "host_slabs overlaps dev_slabs");
+  // The host tier must be pinned host memory the GPU can read: anything else is
+  // rejected here instead of faulting in the kernel.
+  hipPointerAttribute_t attr;
+  hipError_t he = hipPointerGetAttributes(&attr, host_slabs);
+  if (he != hipSuccess || attr.type != hipMemoryTypeHost || !attr.devicePointer) {
+    (void)hipGetLastError();
+    return fail(FMOE_ERR_UNSUPPORTED, "host_slabs is not pinned host memory mapped for the GPU");
+  }
+  fmoe::FetchArgs a{idx, n_idx, shared, (const uint8_t*)attr.devicePointer, (uint8_t*)dev_slabs,
+                    slab_bytes, slab_stride, tags, n_slots, tag, n_copied};
+  he = fmoe::launch_fetch(a, (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "fetch kernels");
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_fetch_experts(const int32_t* idx, int32_t n_idx, int32_t shared,
+                               const void* host_slabs, int64_t slab_bytes, int64_t slab_stride,
+                               void* dev_slabs, int32_t* tags, int32_t n_slots, int32_t tag,
+                               int32_t* n_copied, void* stream) {
+  return finish(fmoe_fetch_experts_impl(idx, n_idx, shared, host_slabs, slab_bytes, slab_stride,
+                                        dev_slabs, tags, n_slots, tag, n_copied, stream),
+                stream, "fetch (debug sync)");
+}
+
 fmoe_status fmoe_moe_layer_forward_noalloc(const fmoe_layer* L, int32_t T, const float* x,
                                            const float* residual, float* h_out, float* y_out,
                                            int32_t* idx_out, float* w_out, float* moe_out,

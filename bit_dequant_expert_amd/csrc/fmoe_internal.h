@@ -253,6 +253,20 @@ struct AttnArgs {
 bool attention_supported(int NQ, int NKV, int D);
 size_t attention_ws_bytes(int B, int NKV, int D, int cap);
 hipError_t launch_attention(const AttnArgs& p, hipStream_t st);
+// Host-tier expert streaming (fmoe_stream.hip).
+struct FetchArgs {
+  const int32_t* idx;      // [n_idx] experts to fetch (device)
+  int n_idx;
+  int shared;              // one more expert fetched with them, or -1
+  const uint8_t* host;     // device address of the pinned host slabs
+  uint8_t* dev;            // HBM slabs
+  int64_t slab_bytes, stride;
+  int32_t* tags;           // [n_slots] tag of what each HBM slot holds
+  int n_slots;
+  int tag;
+  int* n_copied;           // optional: incremented once per slab copied
+};
+hipError_t launch_fetch(const FetchArgs& a, hipStream_t st);
 // Byte offset of the counter block's wait-timeout word.
 size_t wait_timeout_offset();
 bool fused1_supported(int H, int I, int E, int bits);

@@ -276,6 +276,31 @@ fmoe_status fmoe_attention_decode(const float *q, const uint16_t *k_cache, const
 size_t fmoe_attention_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
                                      int32_t cap);
 
+/* Host-tier expert streaming, for expert sets larger than HBM ([WAS] "1.
+ * SSD-Experten-Streaming mit macOS Page Cache", [HADA] "SSD Expert Streaming":
+ * only the experts a layer selects are read from the slower tier, and a cache
+ * keeps recent ones).  The slower tier is pinned host memory; the faster one a
+ * layer's slab array in HBM whose slot e holds expert e of whichever layer
+ * last fetched it, recorded by the caller's tag in tags[e].  For every expert e
+ * in idx[0 .. n_idx-1] and `shared` (a slot, or -1 for none), whose slot does
+ * not already carry `tag`: copy host_slabs + e*slab_stride (slab_bytes bytes)
+ * to dev_slabs + e*slab_stride; then tags[e] = tag for all of them.  The
+ * indices stay on the device (the routing output of fmoe_route_topk feeds it
+ * directly), and repeated experts are copied once.
+ *   idx [n_idx] int32 DEVICE (entries outside [0, n_slots) copy nothing),
+ *   n_idx <= 8192; host_slabs: pinned host memory mapped for the GPU (for
+ *   example hipHostMalloc or a pinned torch tensor), n_slots slabs of
+ *   slab_stride bytes (FMOE_ERR_UNSUPPORTED if the pointer is not pinned host
+ *   memory); dev_slabs: device memory, the same layout; tags [n_slots] int32
+ *   DEVICE; n_copied: optional int32 DEVICE counter incremented once per slab
+ *   copied.  slab_bytes a positive multiple of 16 <= slab_stride, a multiple of
+ *   16; both base pointers 16-byte aligned.  Two calls whose fetch lists share
+ *   an expert must not run concurrently. */
+fmoe_status fmoe_fetch_experts(const int32_t *idx, int32_t n_idx, int32_t shared,
+                               const void *host_slabs, int64_t slab_bytes, int64_t slab_stride,
+                               void *dev_slabs, int32_t *tags, int32_t n_slots, int32_t tag,
+                               int32_t *n_copied, void *stream);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): fmoe_moe_layer_forward with
  * the same arguments and results, minus the workspace.  Its workspace is a

@@ -230,3 +230,24 @@ def test_attention_validation():
     assert _att(B=0) == fm.FMOE_OK
     # query operands (2 x 2 heads x 8 k-steps x 2 halves x 1 KiB), then 4 chunks of 128 per head
     assert fm.fmoe_attention_workspace_size(2, 2, 256, 512) == 65536 + 2 * 2 * 4 * (32 + 16 * 256) * 4
+
+
+def _fetch(idx=A, n_idx=4, shared=16, host=A + (1 << 30), slab_bytes=4096, stride=4096,
+           dev=A + (2 << 30), tags=A + (3 << 30), n_slots=17, tag=1):
+    return fm.lib().fmoe_fetch_experts(idx, n_idx, shared, host, slab_bytes, stride, dev, tags,
+                                       n_slots, tag, None, None)
+
+
+def test_fetch_validation():
+    # argument errors found before any GPU call
+    assert _fetch(n_idx=-1) == fm.FMOE_ERR_SHAPE
+    assert _fetch(n_idx=8193) == fm.FMOE_ERR_SHAPE
+    assert _fetch(n_slots=0) == fm.FMOE_ERR_SHAPE
+    assert _fetch(shared=17) == fm.FMOE_ERR_SHAPE
+    assert _fetch(slab_bytes=100) == fm.FMOE_ERR_SHAPE
+    assert _fetch(stride=2048) == fm.FMOE_ERR_SHAPE
+    assert _fetch(idx=0) == fm.FMOE_ERR_NULL
+    assert _fetch(tags=0) == fm.FMOE_ERR_NULL
+    assert _fetch(host=A + (1 << 30) + 8) == fm.FMOE_ERR_ALIGN
+    assert _fetch(dev=A + (1 << 30) + 4096) == fm.FMOE_ERR_SHAPE     # overlapping tiers
+    assert _fetch(n_idx=0, shared=-1) == fm.FMOE_OK

@@ -202,3 +202,120 @@ def test_attention_rope_base_and_empty_batch():
     fm.fmoe_attention_decode(torch.empty(0, 4, 64, device="cuda"), zc, zc,
                              torch.zeros(1, dtype=torch.int32, device="cuda"), out, z)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------- expert streaming
+def _pinned(nbytes):
+    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+
+def _fetch_setup(cfg, layer=0):
+    """Host tier (pinned) holding the layer's slabs, an HBM tier filled with a
+    marker byte, tags zero."""
+    import synth
+    sp = cfg.spec
+    _, stride = sp.layout()
+    host = _pinned(stride * (cfg.E + 1))
+    dev_tmp = torch.empty(stride * (cfg.E + 1), dtype=torch.uint8, device="cuda")
+    synth.fill_device_slabs(dev_tmp.data_ptr(), sp, cfg.seed, layer, 0, cfg.E + 1, stride)
+    host.copy_(dev_tmp.cpu())
+    del dev_tmp
+    hbm = torch.full((stride * (cfg.E + 1),), 0xAB, dtype=torch.uint8, device="cuda")
+    tags = torch.zeros(cfg.E + 1, dtype=torch.int32, device="cuda")
+    ncp = torch.zeros(1, dtype=torch.int32, device="cuda")
+    return host, hbm, tags, ncp, stride
+
+
+def test_fetch_experts_routing_driven_cache():
+    # Route 3 tokens on the device, fetch their experts and the shared one into
+    # HBM, run the layer on the HBM tier and check it against the oracle; a
+    # second fetch with the same tag copies nothing (cache hit), a new tag
+    # copies again.
+    import synth
+    from test_gpu_parity import GpuLayer, check_layer
+    cfg = synth.CONFIGS["tiny"]
+    note("fetch tiny")
+    host, hbm, tags, ncp, stride = _fetch_setup(cfg)
+    gl = GpuLayer(cfg)                  # router, gates, norm (and its own slabs, unused here)
+    T = 3
+    x = synth.activations(cfg, T, pool=50)
+    idx = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, cfg.k, device="cuda")
+    ws = torch.zeros(fm.fmoe_route_workspace_size(T, cfg.E), dtype=torch.uint8, device="cuda")
+    fm.fmoe_route_topk(gl.Wr_d, dev(x), cfg.k, idx, w, None, ws)
+    fm.fmoe_fetch_experts(idx, T * cfg.k, cfg.E, host, stride, stride, hbm, tags, cfg.E + 1, 7,
+                          ncp)
+    torch.cuda.synchronize()
+    sel = sorted(set(idx.cpu().numpy().ravel().tolist()) | {cfg.E})
+    assert int(ncp.item()) == len(sel)
+    hb = host.numpy().reshape(cfg.E + 1, stride).copy()
+    db = hbm.cpu().numpy().reshape(cfg.E + 1, stride)
+    tg = tags.cpu().numpy()
+    for e in range(cfg.E + 1):
+        if e in sel:
+            assert np.array_equal(db[e], hb[e]) and tg[e] == 7, e
+        else:
+            assert (db[e] == 0xAB).all() and tg[e] == 0, e
+    # the layer on the HBM tier
+    L = fm.fmoe_layer_desc(cfg.H, cfg.I, cfg.E, cfg.k, gl.fmt, gl.Wr_d, hbm, stride, gl.wsg_d,
+                           gl.g_d, cfg.eps)
+    out = dict(h=torch.empty(T, cfg.H, device="cuda"), y=torch.empty(T, cfg.H, device="cuda"),
+               moe=torch.empty(T, cfg.H, device="cuda"),
+               idx=torch.empty(T, cfg.k, dtype=torch.int32, device="cuda"),
+               w=torch.empty(T, cfg.k, device="cuda"))
+    lws = torch.zeros(fm.fmoe_workspace_size(L, T), dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    fm.fmoe_moe_layer_forward(L, T, xd, xd, out["h"], out["y"], out["idx"], out["w"], out["moe"],
+                              lws)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    assert np.array_equal(got["idx"], idx.cpu().numpy())
+    check_layer(gl, x, x, got, list(range(T)))
+    # same tag: a hit, even though the host tier changed meanwhile
+    host[:] = 0x11
+    fm.fmoe_fetch_experts(idx, T * cfg.k, cfg.E, host, stride, stride, hbm, tags, cfg.E + 1, 7,
+                          ncp)
+    torch.cuda.synchronize()
+    assert int(ncp.item()) == len(sel)
+    assert np.array_equal(hbm.cpu().numpy().reshape(cfg.E + 1, stride)[sel], hb[sel])
+    # new tag: copied again
+    fm.fmoe_fetch_experts(idx, T * cfg.k, -1, host, stride, stride, hbm, tags, cfg.E + 1, 8, ncp)
+    torch.cuda.synchronize()
+    routed = sorted(set(idx.cpu().numpy().ravel().tolist()))
+    assert int(ncp.item()) == len(sel) + len(routed)
+    db = hbm.cpu().numpy().reshape(cfg.E + 1, stride)
+    for e in routed:
+        assert (db[e] == 0x11).all() and tags[e].item() == 8
+    assert np.array_equal(db[cfg.E], hb[cfg.E]) and tags[cfg.E].item() == 7
+
+
+def test_fetch_experts_full_size_slabs():
+    # Full-size 4-bit slabs (6.75 MiB, 108 pieces each), a list with repeats and
+    # an out-of-range entry.
+    import synth
+    base = synth.CONFIGS["layer4"]
+    cfg = synth.Config("fetch64", base.H, base.I, 64, 4, base.spec, base.seed)
+    note("fetch full-size slabs")
+    host, hbm, tags, ncp, stride = _fetch_setup(cfg, layer=2)
+    lst = torch.tensor([5, 17, 5, 63, -3, 64, 17, 40], dtype=torch.int32, device="cuda")
+    fm.fmoe_fetch_experts(lst, 8, 64, host, stride, stride, hbm, tags, cfg.E + 1, 3, ncp)
+    torch.cuda.synchronize()
+    want = [5, 17, 63, 64, 40]
+    assert int(ncp.item()) == len(want)
+    hb = host.numpy().reshape(cfg.E + 1, stride)
+    db = hbm.cpu().numpy().reshape(cfg.E + 1, stride)
+    for e in range(cfg.E + 1):
+        if e in want:
+            assert np.array_equal(db[e], hb[e]), e
+        else:
+            assert (db[e] == 0xAB).all(), e
+
+
+def test_fetch_experts_rejects_unpinned_host_memory():
+    host = np.zeros(1 << 16, np.uint8)             # pageable
+    hbm = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    tags = torch.zeros(4, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(fm.FmoeError) as ei:
+        fm.fmoe_fetch_experts(idx, 1, -1, host.ctypes.data, 1 << 14, 1 << 14, hbm, tags, 4, 1)
+    assert ei.value.status == fm.FMOE_ERR_UNSUPPORTED
