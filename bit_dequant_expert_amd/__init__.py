@@ -19,6 +19,12 @@ LIB_PATH = os.path.join(PKG, "libfmoe.so")
 # The phase-trace build (same kernels, plus wall-clock stamps of the one-token
 # kernel's phases); selected by use_trace_library() before the first call.
 TRACE_LIB_PATH = os.path.join(PKG, "libfmoe_trace.so")
+# The host-sanitizer build (host code with AddressSanitizer and UBSan, the same
+# device code), for CPU runs with the sanitizer runtimes preloaded; selected
+# by use_sanitizer_library() or FMOE_SANITIZER_BUILD=1 before the first call.
+SAN_LIB_PATH = os.path.join(PKG, "libfmoe_san.so")
+if os.environ.get("FMOE_SANITIZER_BUILD") == "1":
+    LIB_PATH = SAN_LIB_PATH
 
 
 def use_trace_library():
@@ -27,6 +33,14 @@ def use_trace_library():
     if _lib is not None:
         raise RuntimeError("the library is already loaded")
     LIB_PATH = TRACE_LIB_PATH
+
+def use_sanitizer_library():
+    """Load the host-sanitizer build instead of the plain one (before lib())."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = SAN_LIB_PATH
+
 
 FMOE_OK, FMOE_ERR_NULL, FMOE_ERR_SHAPE, FMOE_ERR_ALIGN = 0, 1, 2, 3
 FMOE_ERR_UNSUPPORTED, FMOE_ERR_WORKSPACE, FMOE_ERR_HIP = 4, 5, 6

@@ -73,6 +73,29 @@ def jobs(trace=False):
     return out
 
 
+# Host-sanitizer variant: the C ABI layer (host-only C++) built by g++ with
+# AddressSanitizer and UBSan and linked with the plain build's device objects
+# into libfmoe_san.so; CPU use only (validation paths), with the sanitizer
+# runtimes preloaded into the interpreter.
+SAN_LIB = os.path.join(PKG, "libfmoe_san.so")
+SANITIZE = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized() -> str:
+    if not all(os.path.exists(o) for o, _ in jobs()):   # the plain build's objects
+        build()
+    obj = os.path.join(BUILD, "fmoe_api_san.o")
+    _run(["g++", "-O1", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", *SANITIZE,
+          "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC,
+          "-c", os.path.join(CSRC, "fmoe_api.cpp"), "-o", obj])
+    objs = [o for o, _ in jobs() if not o.endswith("fmoe_api.o")]
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", "-shared", *SANITIZE, "-o", tmp, obj, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+          "-Wl,-rpath,/opt/rocm/lib"])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def build(force: bool = True, verbose: bool = False, trace: bool = False) -> str:
     lib_path = TRACE_LIB if trace else LIB
     if not force and os.path.exists(lib_path):
@@ -92,4 +115,7 @@ def build(force: bool = True, verbose: bool = False, trace: bool = False) -> str
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, trace="--trace" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose=True, trace="--trace" in sys.argv))

@@ -20,9 +20,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.LIB
+        san = os.environ.get("FMOE_SANITIZER_BUILD") == "1"
+        path = _build.SAN_LIB if san else _build.LIB
         if not os.path.exists(path):
-            _build.build()
+            _build.build(sanitize=san)
         L = C.CDLL(path)
         P = C.c_void_p
         i32, i64, dbl = C.c_int, C.c_int64, C.c_double

@@ -15,15 +15,22 @@ CFLAGS = ["-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-Wall", "-Wextra"]
 
 
-def build(force: bool = True) -> str:
-    if not force and os.path.exists(LIB):
-        return LIB
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, "-o", tmp, *SRC, "-lm"]
+# AddressSanitizer + UBSan variant (CPU runs with the sanitizer runtimes preloaded).
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+SANITIZE = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    lib = SAN_LIB if sanitize else LIB
+    if not force and os.path.exists(lib):
+        return lib
+    tmp = lib + ".tmp"
+    cmd = ["gcc", *CFLAGS, *(SANITIZE if sanitize else []), "-o", tmp, *SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build())
+    import sys
+    print(build(sanitize="--sanitize" in sys.argv))
