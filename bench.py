@@ -11,8 +11,9 @@ are seeded synthetic data resident in HBM.  layer2 is the same layer with
 Cold-cache protocol: the steps rotate over R distinct layer replicas (default
 32, ~116 GB of expert slabs) and a pool of 64 activation vectors, so that the
 per-layer router (8 MB) and shared expert (7 MB) do not stay in the 256 MB
-Infinity Cache.  Steps are captured in HIP graphs of 64 layers and replayed;
-HIP events on the capture/replay stream time exactly --steps steps.
+Infinity Cache.  The timed steps are launched one per layer forward behind a
+GPU busy-wait that outlasts their queueing; HIP events on the launch stream
+time exactly --steps steps.  Replays of a 64-layer HIP graph give the spread.
 
 Other workloads (not the default line):
   expert   one expert's fused gate/up -> SwiGLU -> down (fmoe_expert_ffn) at
@@ -62,6 +63,7 @@ DEFAULT_STEPS = {"layer4": (640, 64), "layer2": (640, 64), "expert": (640, 64),
                  "stack60": (20, 2), "chain60": (20, 2), "deltanet": (640, 64),
                  "attention": (640, 64), "stream": (64, 8)}
 SPIN_US = 2000          # GPU busy-wait queued ahead of a timed region
+EAGER_SPIN_PER_STEP_US = 25   # and at least this per eagerly launched step (host queueing)
 
 
 def parse(argv=None):
@@ -160,6 +162,31 @@ class GraphRunner:
             ev1.record(self.stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
+        return ev0.elapsed_time(ev1), wall
+
+    def timed_eager(self, first, n):
+        """Steps first .. first+n-1 launched one by one (no graph) between two HIP
+        events.  The busy-wait queued ahead lasts long enough (SPIN_US, and at
+        least EAGER_SPIN_PER_STEP_US per step) for the host to queue every launch
+        before the GPU reaches the start event, so the region holds the GPU's work
+        and its launch gaps only, none of the host's launch latency nor a graph's
+        first-replay cost.  Returns (event ms, host wall ms)."""
+        torch = self.torch
+        import probes
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(self.stream):
+            probes.spin(max(SPIN_US, EAGER_SPIN_PER_STEP_US * n), self.stream.cuda_stream)
+            ev0.record(self.stream)
+            cs = self.stream.cuda_stream
+            for i in range(first, first + n):
+                self.step(i, cs)
+            ev1.record(self.stream)
+        queued = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        self.last_queue_ms = queued
         return ev0.elapsed_time(ev1), wall
 
     def spread(self, first, count, reps=20):
@@ -519,12 +546,13 @@ def bench_layer(args, torch):
     torch.cuda.synchronize()
     period = R * XPOOL // math.gcd(R, XPOOL)
     runner = GraphRunner(torch, s, step, period)
-    timed = step_chunks(args.steps, 0)
-    warm = step_chunks(args.warmup, args.steps)
-    runner.prepare(warm + timed + [(0, GRAPH_LEN)])
-    runner.run(warm)
+    with torch.cuda.stream(s):
+        for i in range(args.steps, args.steps + args.warmup):   # warm-up steps
+            step(i, s.cuda_stream)
     torch.cuda.synchronize()
-    total_ms, wall_ms = runner.timed(timed)
+    total_ms, wall_ms = runner.timed_eager(0, args.steps)
+    queue_ms = runner.last_queue_ms
+    runner.prepare([(0, GRAPH_LEN)])
     rep_us = [v * 1000.0 / GRAPH_LEN for v in runner.spread(0, GRAPH_LEN)]
     timeout_word = int(ws[fm.fmoe_wait_timeout_offset():][:4].view(torch.int32).item())
 
@@ -557,14 +585,17 @@ def bench_layer(args, torch):
                    "batch": 1, "replicas": R, "graph_len": GRAPH_LEN},
         "us_per_layer": round(us, 3),
         "timed_region": {"event_ms": round(total_ms, 4), "host_wall_ms": round(wall_ms, 4),
-                         "graphs": [c for _, c in timed],
+                         "host_queue_ms": round(queue_ms, 4),
+                         "launches": "one per layer forward, queued behind a GPU busy-wait",
                          "note": f"exactly {args.steps} layer forwards between two HIP events on "
-                                 f"the launch stream, after a {SPIN_US} us GPU busy-wait that "
-                                 "keeps host launch latency out of the region; host wall time "
-                                 "includes that wait and both synchronisations"},
+                                 f"the launch stream; the busy-wait queued first "
+                                 f"({max(SPIN_US, EAGER_SPIN_PER_STEP_US * args.steps)} us) "
+                                 "outlasts the host's queueing of every launch (host_queue_ms), "
+                                 "so the region holds no host latency; host wall time includes "
+                                 "that wait and both synchronisations"},
         "us_per_layer_min_median_p90": spread(rep_us),
-        "spread_note": f"20 further replays of one {GRAPH_LEN}-layer graph, outside the timed "
-                       "region",
+        "spread_note": f"20 further replays of one {GRAPH_LEN}-layer HIP graph, outside the "
+                       "timed region",
         "moe_layer_tokens_per_s": round(1e6 / us, 1),
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "pct_of_measured_stream_ceiling": None if not stream else round(100.0 * gbps / stream, 2),

@@ -30,10 +30,10 @@
 //   phase A  all waves load x, a quarter of router row b and one row of the
 //            shared expert's gate or up (rows n = 2b, 2b + 1); waves 2-3 also
 //            load the shared expert's down rows of down part b.  x is staged in
-//            LDS (fp32 for the router, fp16 pairs for the gate/up rows); the
-//            fp64 logit of row b, with a partial dot product of the shared-gate
-//            row over x[b*H/E, (b+1)*H/E), and the two shared SwiGLU values go
-//            out as records
+//            LDS in fp32; the fp64 logit of row b, with a partial dot product
+//            of the shared-gate row over x[b*H/E, (b+1)*H/E), goes out as a
+//            record; then x is prepared as fp16 pairs for the gate/up rows and
+//            the two shared SwiGLU values go out as a record
 //   phase B  wave 0 polls the E logit records and takes the top-k (one wave,
 //            lower index on ties) and the shared gate; all waves load and
 //            compute routed gate/up part b (expert slot b / (I/gu_rows)),
@@ -550,15 +550,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
   };
   TileI td[kFusedMaxSlots][kUD];
 
-  // x to LDS: fp32 for the router, prepared fp16 for the gate/up rows.
+  // x to LDS in fp32 for the router first; its fp16 preparation for the
+  // gate/up rows follows the logit (it is not on the routing's path).
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     reinterpret_cast<float4*>(lds_x)[q * kThreads + tid] = xq[q];
     if (q == 0) TOK1_MARK(15);   // x (first quarter) in registers
-    prep_x4<BITS, false, true>(xq[q], lds_xp, H, q * (kThreads / 8) + tid / 8);
   }
   lds_barrier();
-  TOK1_MARK(1);   // x staged
+  TOK1_MARK(1);   // x staged (fp32)
 
   uint32_t ep = (uint32_t)__builtin_amdgcn_readfirstlane(ep_raw) + 1u;
   ep &= 0x7FFFFFFFu;
@@ -605,6 +605,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
     lds_barrier();   // sh.rp is reused
   }
   TOK1_MARK(2);   // logit records stored
+
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) prep_x4<BITS, false, true>(xq[q], lds_xp, H, q * (kThreads / 8) + tid / 8);
+  lds_barrier();   // x prepared
 
   // The shared expert's SwiGLU of rows 2 sp, 2 sp + 1: one record each pair.
   XRegs<BITS, NSH> xr;
