@@ -23,8 +23,9 @@ Other workloads (not the default line):
            (x_{l+1} = y_l, r_{l+1} = h_l) for a batch of 32 independent tokens;
            a step is the whole 60-layer pass, captured in one HIP graph.
   chain60  the same 60 layers for one token (batch-1 decode through the whole
-           MoE stack): a step is the 60-layer pass, one HIP graph of 60
-           one-token layer launches.
+           MoE stack): a step is the 60-layer pass, one fmoe_moe_stack_forward
+           call (the chained one-token kernel, one launch for all 60 layers);
+           one HIP graph of 60 one-token layer launches is timed beside it.
   deltanet one Gated DeltaNet decode step (fmoe_deltanet_step) of one
            linear-attention layer for 32 sequences x 64 heads of 128 x 128 fp32
            state (268 MB), rotating over 8 layers' states so that no step finds
@@ -90,8 +91,9 @@ def parse(argv=None):
     p.add_argument("--no-stream-probe", action="store_true",
                    help="skip measuring the streaming-read ceiling")
     p.add_argument("--phase-trace", type=int, default=0,
-                   help="run this many one-token layer calls on the phase-trace build and print "
-                        "the timeline of the kernel's phases (layer workloads only)")
+                   help="run this many calls on the phase-trace build and print the timeline of "
+                        "the one-token kernel's phases (layer workloads; chain60: its second "
+                        "layer)")
     return p.parse_args(argv)
 
 
@@ -255,11 +257,11 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_hash, workload):
-    """HBM bytes per launch of the layer kernel, from the rocprofv3 counter
-    summary profiles/k_layer1t_<workload>_traffic.txt when it was taken on this
-    exact kernel source (its `source_hash:` line), else None."""
-    path = os.path.join(ROOT, "profiles", f"k_layer1t_{workload}_traffic.txt")
+def traffic_from_profiles(kernel_hash, workload, kernel="k_layer1t"):
+    """HBM bytes per launch of a kernel, from the rocprofv3 counter summary
+    profiles/<kernel>_<workload>_traffic.txt when it was taken on this exact
+    kernel source (its `source_hash:` line), else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -443,11 +445,18 @@ TRACE_EVENTS = ["entry", "x staged", "logits stored", "shared SwiGLU published",
                 "x in registers"]
 
 
-def phase_trace(args, torch, fm, step, R):
-    """Wall-clock stamps of the one-token kernel's phase boundaries (trace
+CHAIN_TRACE_EVENTS = ["layer start", "logits stored", "shared SwiGLU published", "top-k known",
+                      "routed SwiGLU published", "first images in LDS", "part published",
+                      "every part polled", "next x complete", "down rows requested",
+                      "down rows computed"]
+
+
+def phase_trace(args, torch, fm, step, R, names=TRACE_EVENTS):
+    """Wall-clock stamps of a one-token kernel's phase boundaries (trace
     build): per call, each workgroup's time of each event after the first
-    workgroup's entry; reported as the min / median / max over workgroups,
-    each the median over calls."""
+    workgroup's first event (entry; the traced layer's start in a chain);
+    reported as the min / median / max over workgroups, each the median over
+    calls."""
     import ctypes as C
     import numpy as np
     nwg, nev = 1024, 16
@@ -468,7 +477,7 @@ def phase_trace(args, torch, fm, step, R):
         live = t[:, 0] > 0
         t0 = t[live, 0].min()
         rows = []
-        for e in range(len(TRACE_EVENTS)):
+        for e in range(len(names)):
             v = t[live, e]
             v = (v[v > 0] - t0) / 100.0          # 100 MHz ticks -> us
             rows.append((v.min(), np.median(v), v.max()) if v.size else (np.nan,) * 3)
@@ -477,7 +486,7 @@ def phase_trace(args, torch, fm, step, R):
     return {"calls": args.phase_trace, "unit": "us after the first workgroup's entry",
             "events": {name: {"min": round(float(a[0]), 3), "median": round(float(a[1]), 3),
                               "max": round(float(a[2]), 3)}
-                       for name, a in zip(TRACE_EVENTS, arr) if not np.isnan(a[1])}}
+                       for name, a in zip(names, arr) if not np.isnan(a[1])}}
 
 
 def bench_layer(args, torch):
@@ -930,15 +939,19 @@ def bench_stack(args, torch):
 def bench_chain(args, torch):
     """Batch-1 decode through 60 distinct 4-bit layers chained on the device
     (each layer's y and h are the next layer's x and residual); a step is the
-    whole 60-layer pass for one token, one HIP graph of 60 one-token layer
-    launches.  Each layer writes its own h and y, so that sampled layers can be
-    checked against the oracle fed the GPU's own layer inputs."""
+    whole 60-layer pass for one token: one fmoe_moe_stack_forward call, which
+    runs the 60 layers in one launch of the chained one-token kernel.  Each
+    layer writes its own h and y, so that sampled layers can be checked against
+    the oracle fed the GPU's own layer inputs.  The same pass as 60 one-token
+    layer launches in one HIP graph is timed beside it (context)."""
     import ctypes as C
     import numpy as np
     import bit_dequant_expert_amd as fm
     import oracle
     import synth
 
+    if args.phase_trace:
+        fm.use_trace_library()
     cfg = synth.CONFIGS["layer4"]
     sp = cfg.spec
     NL = 60
@@ -958,8 +971,17 @@ def bench_chain(args, torch):
     torch.cuda.synchronize()
     print("[bench] layers ready", file=sys.stderr, flush=True)
     Lp = [C.addressof(L) for L in layers]
+    arr = (fm.fmoe_layer * NL)(*layers)
+    lib = fm.lib()
 
     def step(i, stream):
+        rc = lib.fmoe_moe_stack_forward(arr, NL, 1, x0.data_ptr(), x0.data_ptr(), hs.data_ptr(),
+                                        ys.data_ptr(), idx.data_ptr(), wts.data_ptr(),
+                                        ws.data_ptr(), ws_bytes, stream)
+        if rc != 0:
+            raise fm.FmoeError(rc, fm.fmoe_last_error())
+
+    def step_layers(i, stream):
         x = r = x0.data_ptr()
         for l in range(NL):
             h, y = hs[l].data_ptr(), ys[l].data_ptr()
@@ -978,6 +1000,12 @@ def bench_chain(args, torch):
         torch.cuda.synchronize()
         print(json.dumps({"kernel_steps": args.kernel_steps, "workload": args.workload}))
         return None
+    if args.phase_trace:
+        print(json.dumps({"phase_trace": phase_trace(args, torch, fm, step, 1,
+                                                     names=CHAIN_TRACE_EVENTS),
+                          "traced_layer": 1, "workload": args.workload,
+                          "kernel_source_hash": source_hash()}))
+        return None
 
     with torch.cuda.stream(s):
         step(0, s.cuda_stream)                  # eager warm-up before capture
@@ -990,6 +1018,20 @@ def bench_chain(args, torch):
     total_ms, wall_ms = runner.timed(timed)
     rep_ms = runner.spread(0, 1, reps=min(args.steps, 10))
     timeout_word = int(ws[fm.fmoe_wait_timeout_offset():][:4].view(torch.int32).item())
+    # the outputs of the timed pass, for the parity check below
+    hs_h, ys_h = hs.cpu().numpy(), ys.cpu().numpy()
+    idx_h, w_h = idx.cpu().numpy(), wts.cpu().numpy()
+    # context: the same pass as 60 one-token launches in one graph
+    with torch.cuda.stream(s):
+        step_layers(0, s.cuda_stream)
+    torch.cuda.synchronize()
+    same_bits = bool(np.array_equal(hs.cpu().numpy(), hs_h) and np.array_equal(ys.cpu().numpy(), ys_h))
+    lrunner = GraphRunner(torch, s, lambda i, cs: step_layers(i, cs), 1)
+    lrunner.prepare([(0, 1)])
+    lrunner.run(warm)
+    l_ms, _ = lrunner.timed(timed)
+    l_ms /= args.steps
+    timeout_word |= int(ws[fm.fmoe_wait_timeout_offset():][:4].view(torch.int32).item())
     ms = total_ms / args.steps
     us_layer = ms * 1000.0 / NL
     nbytes, ebytes = layer_bytes(cfg)
@@ -1021,18 +1063,22 @@ def bench_chain(args, torch):
                                  "two HIP events on the launch stream"},
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "algorithmic_bytes_per_layer": nbytes,
-        "roofline": {"bound": "hbm", "kernel": "k_layer1t (one launch per layer)",
+        "roofline": {"bound": "hbm", "kernel": "k_chain1t (60 layers in one launch)",
                      "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic_from_profiles(khash, "layer4")},
+                     "traffic": traffic_from_profiles(khash, "chain60", kernel="k_chain1t"),
+                     "traffic_note": "HBM bytes of one launch (60 layers)"},
+        "per_layer_launches": {"us_per_layer": round(l_ms * 1000.0 / NL, 3),
+                               "ms_per_step": round(l_ms, 6),
+                               "same_bits_as_one_launch": same_bits,
+                               "note": "the same pass as 60 one-token layer launches in one "
+                                       "HIP graph"},
         "wait_timeout_word": timeout_word,
         "kernel_source_hash": khash,
     }
     # Parity of the timed pass: sampled layers against the oracle on the GPU's
     # own inputs of that layer (teacher forcing); their oracle time is the CPU
     # baseline.
-    hs_h, ys_h = hs.cpu().numpy(), ys.cpu().numpy()
-    idx_h, w_h = idx.cpu().numpy(), wts.cpu().numpy()
     sample = [0, 1, 29, 58, 59] if args.cpu_sample >= 5 else [0, NL - 1]
     parity = {"layers": sample, "index_mismatch": 0, "excluded_near_ties": 0,
               "max_rel_l2": {"h": 0.0, "y": 0.0}}

@@ -55,7 +55,8 @@ ABI_SYMBOLS = ("fmoe_abi_version", "fmoe_last_error", "fmoe_slab_layout", "fmoe_
                "fmoe_expert_ffn_workspace_size", "fmoe_moe_layer_forward",
                "fmoe_workspace_size", "fmoe_wait_timeout_offset", "fmoe_get_paths",
                "fmoe_set_paths", "fmoe_moe_layer_forward_noalloc", "fmoe_deltanet_step",
-               "fmoe_attention_decode", "fmoe_attention_workspace_size", "fmoe_fetch_experts")
+               "fmoe_attention_decode", "fmoe_attention_workspace_size", "fmoe_fetch_experts",
+               "fmoe_moe_stack_forward")
 
 
 class FmoeError(RuntimeError):
@@ -137,6 +138,9 @@ def lib() -> C.CDLL:
         L.fmoe_attention_workspace_size.restype = sz
         L.fmoe_fetch_experts.argtypes = [P, i32, i32, P, i64, i64, P, P, i32, i32, P, P]
         L.fmoe_fetch_experts.restype = C.c_int
+        L.fmoe_moe_stack_forward.argtypes = [C.POINTER(fmoe_layer), i32, i32, P, P, P, P, P, P,
+                                             P, sz, P]
+        L.fmoe_moe_stack_forward.restype = C.c_int
         L.fmoe_workspace_size.argtypes = [C.POINTER(fmoe_layer), i32]
         L.fmoe_workspace_size.restype = sz
         _lib = L
@@ -274,6 +278,15 @@ def fmoe_moe_layer_forward(L: fmoe_layer, T: int, x, residual, h_out, y_out, idx
         C.byref(L), T, _ptr(x), _ptr(residual), _ptr(h_out), _ptr(y_out), _ptr(idx_out),
         _ptr(w_out), _ptr(moe_out), _ptr(ws), 0 if ws is None else _nbytes(ws),
         _stream(stream)))
+
+
+def fmoe_moe_stack_forward(layers, T: int, x, residual, h_out, y_out, idx_out=None,
+                           w_out=None, ws=None, stream=None):
+    """layers: a sequence of fmoe_layer (or a ctypes array of them)."""
+    arr = layers if isinstance(layers, C.Array) else (fmoe_layer * max(1, len(layers)))(*layers)
+    _check(lib().fmoe_moe_stack_forward(
+        arr, len(layers), T, _ptr(x), _ptr(residual), _ptr(h_out), _ptr(y_out), _ptr(idx_out),
+        _ptr(w_out), _ptr(ws), 0 if ws is None else _nbytes(ws), _stream(stream)))
 
 
 def fmoe_moe_layer_forward_noalloc(L: fmoe_layer, T: int, x, residual, h_out, y_out,

@@ -431,6 +431,24 @@ static fmoe_status layer_args_check(const fmoe_layer* L, int32_t T, const float*
   return FMOE_OK;
 }
 
+// The arguments of the one-token kernels that come from the layer and the
+// workspace (the vectors are the caller's to set).
+static fmoe::Tok1Args tok1_args(const fmoe_layer* L, const int64_t off[9], uint8_t* wsb) {
+  fmoe::Tok1Args ta{};
+  ta.slabs = (const uint8_t*)L->slabs;
+  ta.stride = L->slab_stride;
+  for (int i = 0; i < 9; ++i) ta.off[i] = off[i];
+  ta.Wr = L->router_w; ta.wsg = L->shared_gate_w; ta.gamma = L->norm_w;
+  ta.eps = L->norm_eps;
+  ta.H = L->hidden; ta.I = L->inter; ta.E = L->n_experts; ta.k = L->top_k;
+  ta.area = wsb + fmoe::kFusedCtrBytes;
+  ta.timeout = (int*)(wsb + fmoe::wait_timeout_offset());
+  const uint64_t lim_us = g_paths.wait_limit_us > 0 ? (uint64_t)g_paths.wait_limit_us : 200000u;
+  ta.spin_ticks = lim_us * 100u;   // the wall clock runs at 100 MHz
+  ta.stall_part = g_paths.test_stall_part > 0 ? g_paths.test_stall_part - 1 : -1;
+  return ta;
+}
+
 static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, const float* x,
                                    const float* residual, float* h_out, float* y_out,
                                    int32_t* idx_out, float* w_out, float* moe_out, void* ws,
@@ -459,19 +477,10 @@ static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, c
   memcpy(src.off, off, sizeof off);
 
   if (T == 1 && !fused_disabled() && !g_paths.t1_counters) {
-    fmoe::Tok1Args ta{};
-    ta.slabs = src.base;
-    ta.stride = src.stride;
-    memcpy(ta.off, src.off, sizeof ta.off);
-    ta.Wr = L->router_w; ta.wsg = L->shared_gate_w; ta.x = x; ta.resid = residual;
-    ta.gamma = L->norm_w; ta.h_out = h_out; ta.y_out = y_out; ta.moe_out = moe_out;
-    ta.w_out = w_out; ta.idx_out = idx_out; ta.eps = L->norm_eps;
-    ta.H = H; ta.I = I; ta.E = E; ta.k = k;
-    ta.area = wsb + fmoe::kFusedCtrBytes;
-    ta.timeout = (int*)(wsb + fmoe::wait_timeout_offset());
-    const uint64_t lim_us = g_paths.wait_limit_us > 0 ? (uint64_t)g_paths.wait_limit_us : 200000u;
-    ta.spin_ticks = lim_us * 100u;   // the wall clock runs at 100 MHz
-    ta.stall_part = g_paths.test_stall_part > 0 ? g_paths.test_stall_part - 1 : -1;
+    fmoe::Tok1Args ta = tok1_args(L, off, wsb);
+    ta.x = x; ta.resid = residual;
+    ta.h_out = h_out; ta.y_out = y_out; ta.moe_out = moe_out;
+    ta.w_out = w_out; ta.idx_out = idx_out;
 #ifdef FMOE_TRACE
     ta.trace = (uint64_t*)g_trace;
 #endif
@@ -613,6 +622,101 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer* L, int32_t T, const float* 
   return finish(fmoe_moe_layer_forward_impl(L, T, x, residual, h_out, y_out, idx_out, w_out,
                                             moe_out, ws, ws_bytes, stream),
                 stream, "layer (debug sync)");
+}
+
+// Layers of one stack call must agree in everything but their weights.
+static bool same_shape(const fmoe_layer& a, const fmoe_layer& b) {
+  return a.hidden == b.hidden && a.inter == b.inter && a.n_experts == b.n_experts &&
+         a.top_k == b.top_k && a.fmt.bits == b.fmt.bits && a.fmt.group == b.fmt.group &&
+         a.fmt.sdtype == b.fmt.sdtype && a.slab_stride == b.slab_stride &&
+         a.norm_eps == b.norm_eps;
+}
+
+static fmoe_status fmoe_moe_stack_forward_impl(const fmoe_layer* layers, int32_t n_layers,
+                                               int32_t T, const float* x, const float* residual,
+                                               float* h_out, float* y_out, int32_t* idx_out,
+                                               float* w_out, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  if (!layers) return fail(FMOE_ERR_NULL, "layers is NULL");
+  if (n_layers < 0) return fail(FMOE_ERR_SHAPE, "n_layers=%d must be >= 0", n_layers);
+  if (n_layers == 0) return FMOE_OK;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!same_shape(layers[l], layers[0]))
+      return fail(FMOE_ERR_SHAPE, "layer %d differs from layer 0 in shape, format, stride or eps", l);
+    fmoe_status st = layer_args_check(&layers[l], T, x, residual, h_out, y_out, nullptr);
+    if (st != FMOE_OK) return st;
+  }
+  if (T == 0) return FMOE_OK;
+  const fmoe_layer* L = &layers[0];
+  const int H = L->hidden, k = L->top_k;
+  const size_t vb = (size_t)T * H * 4, ob = vb * (size_t)n_layers;
+  if (residual != x && overlap(residual, vb, x, vb))
+    return fail(FMOE_ERR_SHAPE, "residual partially overlaps x");
+  if (overlap(h_out, ob, x, vb) || overlap(h_out, ob, residual, vb) ||
+      overlap(y_out, ob, x, vb) || overlap(y_out, ob, residual, vb) || overlap(y_out, ob, h_out, ob))
+    return fail(FMOE_ERR_SHAPE, "h_out and y_out must not overlap x, residual or each other");
+  const size_t ib = (size_t)T * k * 4 * (size_t)n_layers;
+  if (idx_out && w_out && overlap(idx_out, ib, w_out, ib))
+    return fail(FMOE_ERR_SHAPE, "idx_out overlaps w_out");
+  QFmt f;
+  check_fmt(&L->fmt, &f);
+  const LayerWs W = layer_ws(T, H, L->inter, L->n_experts, k, f.bits);
+  if (!ws) return fail(FMOE_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(FMOE_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < W.total) return fail(FMOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, W.total);
+  uint8_t* wsb = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (T == 1 && !fused_disabled() && !g_paths.t1_counters) {
+    // one launch per fmoe::kTok1MaxChain layers
+    int64_t off[9];
+    slab_layout(H, L->inter, f, off);
+    int done = 0;
+    while (done < n_layers) {
+      const int n = n_layers - done < fmoe::kTok1MaxChain ? n_layers - done : fmoe::kTok1MaxChain;
+      fmoe::Tok1Args ta = tok1_args(L, off, wsb);
+      ta.x = done == 0 ? x : y_out + (size_t)(done - 1) * H;
+      ta.resid = done == 0 ? residual : h_out + (size_t)(done - 1) * H;
+      ta.h_out = h_out + (size_t)done * H;
+      ta.y_out = y_out + (size_t)done * H;
+      ta.idx_out = idx_out ? idx_out + (size_t)done * k : nullptr;
+      ta.w_out = w_out ? w_out + (size_t)done * k : nullptr;
+#ifdef FMOE_TRACE
+      ta.trace = (uint64_t*)g_trace;
+#endif
+      fmoe::Tok1Chain ch{};
+      ch.n = n;
+      for (int l = 0; l < n; ++l) {
+        const fmoe_layer& Ll = layers[done + l];
+        ch.layer[l] = fmoe::Tok1ChainLayer{Ll.router_w, Ll.shared_gate_w, Ll.norm_w,
+                                           (const uint8_t*)Ll.slabs};
+      }
+      hipError_t te = fmoe::launch_chain1(f, ta, ch, s);
+      if (te == hipErrorNotSupported && done == 0) break;   // the shape: per-layer calls
+      if (te != hipSuccess) return hip_fail(te, "chained one-token kernel");
+      done += n;
+    }
+    if (done == n_layers) return FMOE_OK;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const size_t o = (size_t)l * T * H, oi = (size_t)l * T * k;
+    fmoe_status st = fmoe_moe_layer_forward_impl(
+        &layers[l], T, l == 0 ? x : y_out + o - (size_t)T * H,
+        l == 0 ? residual : h_out + o - (size_t)T * H, h_out + o, y_out + o,
+        idx_out ? idx_out + oi : nullptr, w_out ? w_out + oi : nullptr, nullptr, ws, ws_bytes,
+        stream);
+    if (st != FMOE_OK) return st;
+  }
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_moe_stack_forward(const fmoe_layer* layers, int32_t n_layers, int32_t T,
+                                   const float* x, const float* residual, float* h_out,
+                                   float* y_out, int32_t* idx_out, float* w_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return finish(fmoe_moe_stack_forward_impl(layers, n_layers, T, x, residual, h_out, y_out,
+                                            idx_out, w_out, ws, ws_bytes, stream),
+                stream, "stack (debug sync)");
 }
 
 static fmoe_status fmoe_deltanet_step_impl(const float* q, const float* k, const float* v,

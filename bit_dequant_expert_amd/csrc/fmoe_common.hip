@@ -211,16 +211,11 @@ hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st) {
   return run_variant(c);
 }
 
-// The one-token layer with self-checking records (fmoe_tok1.h).  Shapes:
-// hidden rows of 64 or 128 segments, intermediate rows of 16, 32 or 64
-// segments with I <= H, E <= 2048, k + 1 <= 17 slots, at most 1024 down parts.
-// Grid: max(routed gate/up parts, down parts, shared row pairs), capped at the
-// resident workgroups (routed parts and shared pairs past the grid loop).
-// Every workgroup must hold a router row or a shared row pair (b < E or
-// b < I/2): both are published after the workgroup's last read of x and
-// polled by every workgroup before its first write of h_out, which may alias x.
-hipError_t launch_tok1(QFmt f, const Tok1Args& a_in, hipStream_t st) {
-  Tok1Args a = a_in;
+namespace {
+
+// The shape checks and part geometry of the one-token kernels (a.gu_rows,
+// a.d_rows, a.nGUs, a.nD); hipErrorNotSupported outside what they handle.
+hipError_t tok1_geometry(QFmt f, Tok1Args& a) {
   const int H = a.H, I = a.I, E = a.E, k = a.k, bits = f.bits;
   const int sh = H * bits / 128, si = I * bits / 128, W = 32 / bits;
   if (!((sh == 64 || sh == 128) && (si == 16 || si == 32 || si == 64))) return hipErrorNotSupported;
@@ -236,6 +231,35 @@ hipError_t launch_tok1(QFmt f, const Tok1Args& a_in, hipStream_t st) {
   a.nGUs = I / gr;
   a.nD = H / dr;
   if (a.nD > kTok1MaxParts) return hipErrorNotSupported;
+  return hipSuccess;
+}
+
+int tok1_n_cu() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 0;
+  }
+  return n_cu;
+}
+
+}  // namespace
+
+// The one-token layer with self-checking records (fmoe_tok1.h).  Shapes:
+// hidden rows of 64 or 128 segments, intermediate rows of 16, 32 or 64
+// segments with I <= H, E <= 2048, k + 1 <= 17 slots, at most 1024 down parts.
+// Grid: max(routed gate/up parts, down parts, shared row pairs), capped at the
+// resident workgroups (routed parts and shared pairs past the grid loop).
+// Every workgroup must hold a router row or a shared row pair (b < E or
+// b < I/2): both are published after the workgroup's last read of x and
+// polled by every workgroup before its first write of h_out, which may alias x.
+hipError_t launch_tok1(QFmt f, const Tok1Args& a_in, hipStream_t st) {
+  Tok1Args a = a_in;
+  hipError_t ge = tok1_geometry(f, a);
+  if (ge != hipSuccess) return ge;
+  const int H = a.H, I = a.I, E = a.E, k = a.k, bits = f.bits;
   const int n_gu = k * a.nGUs, n_sp = I / 2;
   int want = n_gu > a.nD ? n_gu : a.nD;
   if (n_sp > want) want = n_sp;
@@ -246,19 +270,49 @@ hipError_t launch_tok1(QFmt f, const Tok1Args& a_in, hipStream_t st) {
   if (bits == 4 && f.group == 64) occ = tok1_occupancy_4_64(f.sb, ns, E, lds);
   if (bits == 2 && f.group == 32) occ = tok1_occupancy_2_32(f.sb, ns, E, lds);
   if (bits == 2 && f.group == 64) occ = tok1_occupancy_2_64(f.sb, ns, E, lds);
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n_cu = 0;
-  }
-  const int cap = occ * n_cu;
+  const int cap = occ * tok1_n_cu();
   const int grid = want < cap ? want : cap;
   if (grid < 1 || a.nD > grid) return hipErrorNotSupported;
   if (grid > (E > n_sp ? E : n_sp)) return hipErrorNotSupported;
   VCall c = make_call(VCall::TOK1, f, ns, grid, st);
   c.t1 = &a;
+  c.lds = lds;
+  return run_variant(c);
+}
+
+// The chained one-token kernel (fmoe_chain.h): the shapes of the one-token
+// kernel with E <= 512 and k + 1 <= kFusedMaxSlots, one workgroup per down
+// part (grid = nD, all resident), every workgroup holding a router row or a
+// shared row pair (nD <= max(E, I/2)), at most kTok1MaxPartRecs part records
+// and kTok1MaxChain layers.
+hipError_t launch_chain1(QFmt f, const Tok1Args& a_in, const Tok1Chain& ch, hipStream_t st) {
+  Tok1Args a = a_in;
+  hipError_t ge = tok1_geometry(f, a);
+  if (ge != hipSuccess) return ge;
+  if (ch.n < 1 || ch.n > kTok1MaxChain) return hipErrorInvalidValue;
+  const int H = a.H, I = a.I, E = a.E, bits = f.bits;
+  if (E > 512) return hipErrorNotSupported;   // one wave's top-k of 8 keys per lane
+  if (a.k + 1 > kFusedMaxSlots) return hipErrorNotSupported;   // phase C in one batch
+  const int R = (a.d_rows + 3) / 3;
+  if (a.d_rows > 16 || (int64_t)R * a.nD > kTok1MaxPartRecs) return hipErrorNotSupported;
+  if (H / 4 % 128 != 0) return hipErrorNotSupported;   // the next x: float4 per holder thread
+  const int n_sp = I / 2;
+  if (a.nD > (E > n_sp ? E : n_sp)) return hipErrorNotSupported;
+  // Dynamic LDS of at least a third of the CU's: two workgroups a CU at most,
+  // so that the grid spreads evenly over the CUs (the kernel's registers
+  // would admit three on some CUs and leave others with one).
+  size_t lds = fused_lds_bytes(H, I, bits);
+  if (lds < (size_t)kLdsPerCu / 3 + 1024) lds = (size_t)kLdsPerCu / 3 + 1024;
+  const int ns = segs_per_lane(H, bits);
+  int occ = 0;
+  if (bits == 4 && f.group == 32) occ = chain1_occupancy_4_32(f.sb, ns, E, lds);
+  if (bits == 4 && f.group == 64) occ = chain1_occupancy_4_64(f.sb, ns, E, lds);
+  if (bits == 2 && f.group == 32) occ = chain1_occupancy_2_32(f.sb, ns, E, lds);
+  if (bits == 2 && f.group == 64) occ = chain1_occupancy_2_64(f.sb, ns, E, lds);
+  if (a.nD > occ * tok1_n_cu()) return hipErrorNotSupported;
+  VCall c = make_call(VCall::CHAIN1, f, ns, a.nD, st);
+  c.t1 = &a;
+  c.ch = &ch;
   c.lds = lds;
   return run_variant(c);
 }

@@ -32,17 +32,23 @@ constexpr int kTok1ImgBytesPerElem = 4;
 constexpr int kTok1MaxI4 = 2048, kTok1MaxI2 = 4096;
 constexpr size_t kTok1LogitOff = 256;
 constexpr size_t kTok1SharedOff = kTok1LogitOff + 16 * (size_t)kTok1MaxE;
+// Part records: one per down part (its sum of h^2), or, in the chained kernel,
+// (d_rows + 3) / 3 per part (its d_rows values of h and their sum of squares),
+// at most kTok1MaxPartRecs in all.
+constexpr int kTok1MaxPartRecs = 3 * kTok1MaxParts;
 constexpr size_t kTok1PartOff = kTok1SharedOff + 16 * (size_t)(kTok1MaxI2 / 2);
-constexpr size_t kTok1ImgOff = kTok1PartOff + 16 * (size_t)kTok1MaxParts;
+constexpr size_t kTok1ImgOff = kTok1PartOff + 16 * (size_t)kTok1MaxPartRecs;
 constexpr size_t kTok1AreaBytes =
-    kTok1ImgOff + (size_t)kTok1MaxSlots * kTok1ImgBytesPerElem * kTok1MaxI2;
+    (kTok1ImgOff + (size_t)kTok1MaxSlots * kTok1ImgBytesPerElem * kTok1MaxI2 + 255) / 256 * 256;
 
 // Every workspace layout keeps its data past this head, which holds only
 // counters that each call returns to zero and the one-token kernel's record
 // area (self-checking records, never read as data by another call kind): a
 // call of any kind never leaves data where another kind of call keeps its
 // counters or records.
-constexpr size_t kWsReserved = kFusedCtrBytes + kTok1AreaBytes;
+// Two record areas: the one-token kernel uses the first, the chained kernel
+// alternates between both by layer.
+constexpr size_t kWsReserved = kFusedCtrBytes + 2 * kTok1AreaBytes;
 __host__ __device__ constexpr int fused_ug(int nsh) { return nsh == 1 ? 4 : 2; }
 inline int fused_gu_rows(int H, int bits) { return kFusedWaves * fused_ug(segs_per_lane(H, bits)); }
 inline int fused_d_rows(int I, int bits) { return kFusedWaves * kFusedUD * rows_per_iter(I, bits); }
@@ -108,6 +114,20 @@ struct Tok1Args {
   uint64_t* trace;    // phase trace (builds with FMOE_TRACE only): kTok1TraceEvents per workgroup
 };
 constexpr int kTok1TraceEvents = 16;
+
+// Layers of one launch of the chained one-token kernel (fmoe_chain.h): the
+// per-layer pointers travel as kernel arguments.
+constexpr int kTok1MaxChain = 64;
+struct Tok1ChainLayer {
+  const float* Wr;
+  const float* wsg;
+  const float* gamma;
+  const uint8_t* slabs;
+};
+struct Tok1Chain {
+  Tok1ChainLayer layer[kTok1MaxChain];
+  int n;
+};
 
 // Arguments of the one-launch single-expert FFN.
 struct Expert1Args {

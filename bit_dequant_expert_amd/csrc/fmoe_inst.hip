@@ -2,7 +2,7 @@
 // (bits, group) pair, given by FMOE_BITS and FMOE_GROUP at compile time.  The
 // build compiles this file once per pair, in parallel.
 #include "fmoe_mfma.h"
-#include "fmoe_tok1.h"
+#include "fmoe_chain.h"
 
 #if !defined(FMOE_BITS) || !defined(FMOE_GROUP)
 #error "FMOE_BITS and FMOE_GROUP must be defined"
@@ -130,6 +130,17 @@ hipError_t run_one(const VCall& c) {
       }
       break;
     }
+    case VCall::CHAIN1: {
+      if constexpr (NS > 2) {
+        return hipErrorNotSupported;
+      } else {
+        const dim3 blk(kThreads), grid(c.grid);
+        const Tok1Args& t = *c.t1;   // E <= 512 (launch_chain1 checks it)
+        hipLaunchKernelGGL((k_chain1t<B, G, SB, NS, 8>), grid, blk, c.lds, c.st, t.x, t.area, t,
+                           *c.ch);
+      }
+      break;
+    }
     case VCall::EXPERT1: {
       if constexpr (NS > 2) {
         return hipErrorNotSupported;
@@ -174,6 +185,21 @@ int tok1_occupancy(size_t lds) {
   return cached;
 }
 
+// Resident workgroups of the chained one-token kernel per CU.
+template <int SB, int NS, int V>
+int chain1_occupancy(size_t lds) {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&k_chain1t<FMOE_BITS, FMOE_GROUP, SB, NS, V>),
+            kThreads, lds) != hipSuccess || n < 1)
+      n = 0;
+    cached = n;
+  }
+  return cached;
+}
+
 // Resident workgroups of the one-launch expert kernel per CU.
 template <int SB, int NS>
 int expert1_occupancy(size_t lds) {
@@ -204,6 +230,15 @@ int FMOE_CAT(tok1_occupancy_, FMOE_BITS, FMOE_GROUP)(int sb, int ns, int E, size
   if (sb == 4 && ns == 2) return E <= 512 ? tok1_occupancy<4, 2, 8>(lds) : tok1_occupancy<4, 2, 32>(lds);
   if (sb == 2 && ns == 1) return E <= 512 ? tok1_occupancy<2, 1, 8>(lds) : tok1_occupancy<2, 1, 32>(lds);
   if (sb == 2 && ns == 2) return E <= 512 ? tok1_occupancy<2, 2, 8>(lds) : tok1_occupancy<2, 2, 32>(lds);
+  return 0;
+}
+
+int FMOE_CAT(chain1_occupancy_, FMOE_BITS, FMOE_GROUP)(int sb, int ns, int E, size_t lds) {
+  if (E > 512) return 0;
+  if (sb == 4 && ns == 1) return chain1_occupancy<4, 1, 8>(lds);
+  if (sb == 4 && ns == 2) return chain1_occupancy<4, 2, 8>(lds);
+  if (sb == 2 && ns == 1) return chain1_occupancy<2, 1, 8>(lds);
+  if (sb == 2 && ns == 2) return chain1_occupancy<2, 2, 8>(lds);
   return 0;
 }
 

@@ -165,7 +165,7 @@ inline int segs_per_lane(int K, int bits) {  // NS: 16-byte segments one lane re
 // translation unit per pair, compiled in parallel) instantiates the kernels.
 struct VCall {
   enum Kind { GEMV, GEMV_SWIGLU, GATEUP, DOWN_COMBINE, DOWN_SLOTS, EXPERT_MFMA, FUSED1, EXPERT1,
-              TOK1 } kind;
+              TOK1, CHAIN1 } kind;
   QFmt f;
   int ns;
   int grid;
@@ -182,6 +182,7 @@ struct VCall {
   const struct FusedArgs* fu;
   const struct Expert1Args* ex;
   const struct Tok1Args* t1;
+  const struct Tok1Chain* ch;   // CHAIN1: the layers (t1: the shared arguments)
   size_t lds;
 };
 hipError_t run_variant_4_32(const VCall& c);
@@ -196,6 +197,10 @@ int tok1_occupancy_4_32(int sb, int ns, int E, size_t lds);
 int tok1_occupancy_4_64(int sb, int ns, int E, size_t lds);
 int tok1_occupancy_2_32(int sb, int ns, int E, size_t lds);
 int tok1_occupancy_2_64(int sb, int ns, int E, size_t lds);
+int chain1_occupancy_4_32(int sb, int ns, int E, size_t lds);
+int chain1_occupancy_4_64(int sb, int ns, int E, size_t lds);
+int chain1_occupancy_2_32(int sb, int ns, int E, size_t lds);
+int chain1_occupancy_2_64(int sb, int ns, int E, size_t lds);
 int expert1_occupancy_4_32(int sb, int ns, size_t lds);
 int expert1_occupancy_4_64(int sb, int ns, size_t lds);
 int expert1_occupancy_2_32(int sb, int ns, size_t lds);
@@ -220,6 +225,12 @@ hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st);
 // the row geometry is outside what the fused kernel is instantiated for.
 hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st);
 hipError_t launch_tok1(QFmt f, const struct Tok1Args& a, hipStream_t st);
+// One token through ch.n layers of one shape in one persistent launch
+// (fmoe_chain.h); a.h_out, a.y_out hold ch.n rows of H, a.idx_out, a.w_out
+// ch.n rows of k.  hipErrorNotSupported where the shape or the resident
+// workgroups do not admit it.
+hipError_t launch_chain1(QFmt f, const struct Tok1Args& a, const struct Tok1Chain& ch,
+                         hipStream_t st);
 // The single-expert FFN in one launch; hipErrorNotSupported when the shape
 // or the resident workgroups do not admit it (the caller then uses two).
 hipError_t launch_expert1(QFmt f, Expert1Args a, hipStream_t st);

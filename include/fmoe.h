@@ -229,6 +229,27 @@ fmoe_status fmoe_moe_layer_forward(const fmoe_layer *L, int32_t T, const float *
                                    void *ws, size_t ws_bytes, void *stream);
 size_t fmoe_workspace_size(const fmoe_layer *L, int32_t T);
 
+/* T tokens through n_layers MoE layers in order ([HADA] "Deferred GPU Expert
+ * Compute": each layer's combine, norm and residual feed the next layer on the
+ * device).  Layer 0 takes x and residual; layer l > 0 takes y_out[l-1] as x and
+ * h_out[l-1] as residual; each layer computes what fmoe_moe_layer_forward
+ * computes, into row l of the outputs:
+ *   x, residual [T,H] fp32 (residual may alias x); h_out, y_out [n_layers,T,H]
+ *   fp32, overlapping neither x, residual nor each other; idx_out and w_out
+ *   [n_layers,T,k] may each be NULL.  Every layer has the shape, format,
+ *   slab_stride and norm_eps of layers[0] (FMOE_ERR_SHAPE otherwise); only the
+ *   weight pointers differ.  ws: fmoe_workspace_size(&layers[0], T) bytes.
+ *   n_layers == 0 or T == 0 is a no-op.
+ * At T == 1 up to 64 layers run in one launch: the workgroups stay resident
+ * from layer to layer and each builds the next layer's input in its own LDS
+ * from the records of the last hand-off, so neither the launch gap nor a
+ * round trip of x through memory separates two layers.  Other shapes run one
+ * layer call after another; the results are the same. */
+fmoe_status fmoe_moe_stack_forward(const fmoe_layer *layers, int32_t n_layers, int32_t T,
+                                   const float *x, const float *residual, float *h_out,
+                                   float *y_out, int32_t *idx_out, float *w_out, void *ws,
+                                   size_t ws_bytes, void *stream);
+
 /* One decode step of the Gated DeltaNet state update for `batch` sequences x
  * `heads` heads ([WAS] "4. Accelerate BLAS fuer Gated DeltaNet-Schichten": the
  * 64-head state matrix of a linear-attention layer updated by a scale, a

@@ -171,6 +171,39 @@ def test_path_selection_rejects_bad_threshold():
     assert fm.fmoe_get_paths().mfma_min_tokens >= 1
 
 
+def _stack(layers, n=None, T=1, x=A, r=A, h=A + (1 << 24), y=A + (2 << 24), ws=A + (4 << 24),
+           ws_bytes=1 << 34):
+    arr = (fm.fmoe_layer * max(1, len(layers)))(*layers)
+    return fm.lib().fmoe_moe_stack_forward(arr, len(layers) if n is None else n, T, x, r, h, y,
+                                           None, None, ws, ws_bytes, None)
+
+
+def test_stack_validation():
+    L = _layer()
+    row = 4096 * 4
+    assert fm.lib().fmoe_moe_stack_forward(None, 2, 1, A, A, A + (1 << 24), A + (2 << 24), None,
+                                           None, A + (4 << 24), 1 << 34, None) == fm.FMOE_ERR_NULL
+    assert _stack([L, L], n=-1) == fm.FMOE_ERR_SHAPE
+    assert _stack([L, _layer(top_k=2)]) == fm.FMOE_ERR_SHAPE
+    assert _stack([L, _layer(eps=1e-5)]) == fm.FMOE_ERR_SHAPE
+    assert _stack([L, _layer(bits=2, stride=7077888)]) == fm.FMOE_ERR_SHAPE
+    assert _stack([L, _layer(stride=7077888 + 256)]) == fm.FMOE_ERR_SHAPE
+    assert _stack([L, _layer(slabs=0)]) == fm.FMOE_ERR_NULL
+    assert _stack([L, L], x=0) == fm.FMOE_ERR_NULL
+    assert _stack([L, L], h=A + row // 2) == fm.FMOE_ERR_SHAPE            # h overlaps x
+    assert _stack([L, L], y=A + (1 << 24) + row) == fm.FMOE_ERR_SHAPE     # y overlaps h's row 1
+    assert _stack([L, L], ws_bytes=1000) == fm.FMOE_ERR_WORKSPACE
+    assert _stack([L, L], ws=0) == fm.FMOE_ERR_WORKSPACE
+    assert _stack([L, L], ws=A + 16) == fm.FMOE_ERR_ALIGN
+    assert fm.fmoe_last_error()
+
+
+def test_stack_empty_is_noop():
+    L = _layer()
+    assert _stack([L, L], n=0) == fm.FMOE_OK
+    assert _stack([L, L], T=0) == fm.FMOE_OK
+
+
 def _fwd_noalloc(L, T=1, x=A, r=A + (1 << 20), h=A + (2 << 20), y=A + (3 << 20), moe=None):
     return fm.lib().fmoe_moe_layer_forward_noalloc(C.byref(L), T, x, r, h, y, None, None, moe,
                                                    None)
