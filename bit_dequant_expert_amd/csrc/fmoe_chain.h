@@ -100,14 +100,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
   lds_barrier();
 
   // The first loads of a layer's phase A (router row b, the shared-gate value
-  // of this thread, the shared row pair b) do not depend on x: they are issued
+  // of this thread, and in wave 3 the shared row pair b) do not depend on x:
+  // they are issued
   // for layer 0 here and for layer l + 1 at the start of layer l's phase D,
   // so that they are in flight while the last hand-off of layer l completes.
   // (The last layer issues its own loads again: a load issued on every path
   // keeps the registers of the earlier one dead through phases B-C.)
   const int n_sp = I / 2;
   float4 wv[kQ];
-  TileH ts;
+  TileH ts[2][2];   // wave 3: the shared expert's [row 2 sp + r][gate, up]
   float wsg_v;
   auto first_loads = [&](const Tok1ChainLayer& Ln) {
     const int tid = tid_x(), lane = tid & 63;
@@ -118,10 +119,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
 #pragma unroll
     for (int q = 0; q < kQ; ++q) wv[q] = ld_nt(row + q0 + q * 64);
     wsg_v = Ln.wsg[min((int)((int64_t)e * H / E) + tid, H - 1)];
-    const uint8_t* base = Ln.slabs + (int64_t)E * a.stride;
-    const int m = wave & 1;
-    ts.load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
-            2 * min(b, n_sp - 1) + (wave >> 1), geoH);
+    if (writer_wave) {
+      const uint8_t* base = Ln.slabs + (int64_t)E * a.stride;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          ts[r][m].load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
+                        2 * min(b, n_sp - 1) + r, geoH);
+    }
   };
   first_loads(ch.layer[0]);
 
@@ -153,9 +159,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
     CHAIN_MARK(0, 0);   // layer start
     auto shared_load = [&](int sp) {
       const uint8_t* base = L.slabs + (int64_t)E * a.stride;
-      const int m = wave & 1;
-      ts.load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
-              2 * sp + (wave >> 1), geoH);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          ts[r][m].load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
+                        2 * sp + r, geoH);
     };
     auto down_tile = [&](TileI& t, int64_t e, int u) {
       const uint8_t* base = L.slabs + e * a.stride;
@@ -212,27 +221,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
                                  H, q * (kThreads / 8) + tid / 8);
     lds_barrier();
 
-    XRegs<BITS, NSH> xr;
-    for (int sp = b; sp < n_sp; sp += nwg) {
-      if (sp != b) shared_load(sp);
-      xr.load(lds_xp, H, geoH);
-      const float d = sum_lanes(tile_dot(ts, xr), kWave);
-      if (lane == kWave - 1) sh.act[wave] = d;
-      lds_barrier();
-      if (writer_wave && lane == 0) {
-        const uint32_t v0 = __float_as_uint(silu(sh.act[0]) * sh.act[1]);
-        const uint32_t v1 = __float_as_uint(silu(sh.act[2]) * sh.act[3]);
-        rec_st(rsh, (uint32_t)(16 * sp),
-               u32x4_t{v0, v1, 0u, rec_check(ep, v0, v1, 0u, pos_salt(kSaltShared, sp))});
-      }
-      lds_barrier();
-    }
-    CHAIN_MARK(2, 0);   // shared SwiGLU published
-
     // ------------------------------------------------------------ phase B
+    // wave 0: the top-k; wave 3 meanwhile: the shared expert's SwiGLU values
+    XRegs<BITS, NSH> xr;
     if (wave == 0) {
       const bool ok = topk_wave<VW>(rlog, E, k, ep, a.spin_ticks, sh);
       if (!ok && lane == 0) sh.fail = 1;
+    } else if (writer_wave) {
+      for (int sp = b; sp < n_sp; sp += nwg) {
+        if (sp != b) shared_load(sp);
+        xr.load(lds_xp, H, geoH);
+        uint32_t v[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float g = wave_sum(tile_dot(ts[r][0], xr));
+          const float u = wave_sum(tile_dot(ts[r][1], xr));
+          v[r] = __float_as_uint(silu(g) * u);
+        }
+        if (lane == 0)
+          rec_st(rsh, (uint32_t)(16 * sp),
+                 u32x4_t{v[0], v[1], 0u, rec_check(ep, v[0], v[1], 0u, pos_salt(kSaltShared, sp))});
+      }
+      CHAIN_MARK(2, 3);   // shared SwiGLU published
     }
     lds_barrier();
     CHAIN_MARK(3, 0);   // top-k known

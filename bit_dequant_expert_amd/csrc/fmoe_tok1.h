@@ -27,15 +27,15 @@
 // (their loads never sit in front of a poll).
 //
 // Workgroup b (all workgroups resident; the launcher checks occupancy):
-//   phase A  all waves load x, a quarter of router row b and one row of the
-//            shared expert's gate or up (rows n = 2b, 2b + 1); waves 2-3 also
-//            load the shared expert's down rows of down part b.  x is staged in
-//            LDS in fp32; the fp64 logit of row b, with a partial dot product
-//            of the shared-gate row over x[b*H/E, (b+1)*H/E), goes out as a
-//            record; then x is prepared as fp16 pairs for the gate/up rows and
-//            the two shared SwiGLU values go out as a record
+//   phase A  all waves load x and a quarter of router row b; wave 3 also
+//            loads the shared expert's gate and up rows n = 2b, 2b + 1.  x is
+//            staged in LDS in fp32; the fp64 logit of row b, with a partial
+//            dot product of the shared-gate row over x[b*H/E, (b+1)*H/E), goes
+//            out as a record; then x is prepared as fp16 pairs for the gate/up
+//            rows
 //   phase B  wave 0 polls the E logit records and takes the top-k (one wave,
-//            lower index on ties) and the shared gate; all waves load and
+//            lower index on ties) and the shared gate, while wave 3 computes
+//            the two shared SwiGLU values and publishes them; all waves load and
 //            compute routed gate/up part b (expert slot b / (I/gu_rows)),
 //            published as prepared fp16 blocks; waves 2-3 load the selected
 //            experts' down rows right behind their gate/up rows
@@ -524,17 +524,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
   int glo, ghi;
   gate_slice(min(b, E - 1), glo, ghi);
   const float wsg_v = a.wsg[min(glo + tid, H - 1)];   // used where glo + tid < ghi
-  // One shared gate/up row per wave: wave w takes matrix w & 1 (gate, up) of
-  // row 2 sp + (w >> 1), for shared pairs sp = b, b + nwg, ...
+  // The shared expert's rows 2 sp and 2 sp + 1 (gate and up of each), for
+  // shared pairs sp = b, b + nwg, ..., are wave 3's alone: it computes both
+  // SwiGLU values and publishes them with no workgroup barrier, while wave 0
+  // polls the logits.
   const int n_sp = I / 2;
-  TileH ts;
+  TileH ts[2][2];   // wave 3: [row 2 sp + r][gate, up]
   auto shared_load = [&](int sp) {
     const uint8_t* base = a.slabs + (int64_t)E * a.stride;
-    const int m = wave & 1;
-    ts.load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
-            2 * sp + (wave >> 1), geoH);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        ts[r][m].load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
+                      2 * sp + r, geoH);
   };
-  shared_load(min(b, n_sp - 1));
+  if (writer_wave) shared_load(min(b, n_sp - 1));
   TOK1_MARK(14);   // phase A loads issued
   // Down rows of part b held by waves 2-3: rows b*d_rows + (w-2)*kUD*RPI +
   // u*RPI + lane_row (u < kUD).
@@ -610,28 +615,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
   for (int q = 0; q < kQ; ++q) prep_x4<BITS, false, true>(xq[q], lds_xp, H, q * (kThreads / 8) + tid / 8);
   lds_barrier();   // x prepared
 
-  // The shared expert's SwiGLU of rows 2 sp, 2 sp + 1: one record each pair.
-  XRegs<BITS, NSH> xr;
-  for (int sp = b; sp < n_sp; sp += nwg) {
-    if (sp != b) shared_load(sp);
-    xr.load(lds_xp, H, geoH);
-    const float d = sum_lanes(tile_dot(ts, xr), kWave);
-    if (lane == kWave - 1) sh.act[wave] = d;
-    lds_barrier();
-    if (writer_wave && lane == 0) {
-      const uint32_t v0 = __float_as_uint(silu(sh.act[0]) * sh.act[1]);
-      const uint32_t v1 = __float_as_uint(silu(sh.act[2]) * sh.act[3]);
-      rec_st(rsh, (uint32_t)(16 * sp),
-             u32x4_t{v0, v1, 0u, rec_check(ep, v0, v1, 0u, pos_salt(kSaltShared, sp))});
-    }
-    lds_barrier();   // sh.act is reused
-  }
-  TOK1_MARK(3);   // shared SwiGLU published
-
   // ---------------------------------------------------------------- phase B
+  // Wave 0 polls the logits and takes the top-k; wave 3 meanwhile computes
+  // the shared expert's SwiGLU of rows 2 sp, 2 sp + 1 (one record each pair).
+  XRegs<BITS, NSH> xr;
   if (wave == 0) {
     const bool ok = topk_wave<VW>(rlog, E, k, ep, a.spin_ticks, sh);
     if (!ok && lane == 0) sh.fail = 1;
+  } else if (writer_wave) {
+    for (int sp = b; sp < n_sp; sp += nwg) {
+      if (sp != b) shared_load(sp);
+      xr.load(lds_xp, H, geoH);
+      uint32_t v[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float g = wave_sum(tile_dot(ts[r][0], xr));
+        const float u = wave_sum(tile_dot(ts[r][1], xr));
+        v[r] = __float_as_uint(silu(g) * u);
+      }
+      if (lane == 0)
+        rec_st(rsh, (uint32_t)(16 * sp),
+               u32x4_t{v[0], v[1], 0u, rec_check(ep, v[0], v[1], 0u, pos_salt(kSaltShared, sp))});
+    }
+    TOK1_MARK_W(3, 3);   // shared SwiGLU published
   }
   lds_barrier();
   TOK1_MARK(4);   // top-k known
