@@ -423,6 +423,18 @@ def stream_probe(args, torch):
         return None
 
 
+def handoff(args, torch):
+    if args.no_stream_probe:
+        return None
+    try:
+        import probes
+        v = probes.handoff_us(torch)
+        return None if v is None else round(v, 3)
+    except Exception as exc:  # context only
+        print(f"[bench] hand-off probe skipped: {exc}", file=sys.stderr)
+        return None
+
+
 def empty_gap(args, torch):
     if args.no_stream_probe:
         return None
@@ -573,6 +585,7 @@ def bench_layer(args, torch):
     traffic = traffic_from_profiles(khash, args.workload)
     stream = stream_probe(args, torch)
     gap = empty_gap(args, torch)
+    hand = handoff(args, torch)
     out = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -619,7 +632,12 @@ def bench_layer(args, torch):
         "context": {"hbm_stream_read_gbps_measured": stream,
                     "stream_note": "best of 10 passes of a plain 4 GiB streaming read on this GPU",
                     "empty_kernel_gap_us": gap,
-                    "gap_note": "per launch, 2000 empty one-wave kernels replayed from one graph"},
+                    "gap_note": "per launch, 2000 empty one-wave kernels replayed from one graph",
+                    "all_to_all_handoff_us": hand,
+                    "handoff_note": "512 workgroups each store one 16-byte record, one wave of "
+                                    "each polls all 512 (device-coherent loads and stores): "
+                                    "median time until a workgroup has seen them all; the "
+                                    "layer has three such hand-offs on its critical path"},
         "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:

@@ -1,5 +1,6 @@
 """Measurement probes used by bench.py: HBM streaming-read ceiling, empty-kernel
-launch gap, and a bounded spin that keeps the GPU busy while the host queues a
+launch gap, the latency of an all-to-all hand-off through device-coherent
+records, and a bounded spin that keeps the GPU busy while the host queues a
 timed region.  Not part of the MoE layer."""
 import ctypes as C
 import os
@@ -28,6 +29,7 @@ def lib():
         L.probe_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
         L.probe_empty.argtypes = [C.c_int, C.c_void_p]
         L.probe_spin.argtypes = [C.c_int, C.c_void_p]
+        L.probe_handoff.argtypes = [C.c_void_p, C.c_int, C.c_uint32, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib
 
@@ -69,6 +71,30 @@ def empty_gap_us(torch, n=2000):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1000.0 / n
+
+
+def handoff_us(torch, grid=512, reps=24):
+    """All-to-all hand-off on `grid` workgroups (as many as the one-token layer
+    runs): every workgroup stores one 16-byte record, one wave of each polls
+    all of them.  Per launch, the median over workgroups of the time from the
+    first workgroup's start until the workgroup has seen every record; the
+    median of that over launches (the first 4 dropped).  None if a wait gave up."""
+    rec = torch.zeros(grid * 16, dtype=torch.uint8, device="cuda")
+    st = torch.zeros(grid * 2, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    meds = []
+    for r in range(reps):
+        rc = lib().probe_handoff(rec.data_ptr(), grid, r + 1, st.data_ptr(), s)
+        if rc != 0:
+            raise RuntimeError(f"probe_handoff launch failed: {rc}")
+        torch.cuda.synchronize()
+        h = st.view(grid, 2).cpu()
+        if bool((h[:, 1] == 0).any()):
+            return None
+        if r >= 4:
+            meds.append(float(((h[:, 1] - h[:, 0].min()).double() / 100.0).median()))
+    meds.sort()
+    return meds[len(meds) // 2]
 
 
 def spin(us, stream):
