@@ -161,6 +161,22 @@ def test_stack_layer_by_layer_shapes(T):
         oracle_check(gl, o, range(T))
 
 
+def test_stack_batch32_layer_by_layer(layers4):
+    # A batch through the stack entry point: the batched path, one layer call
+    # after another, equal to the caller's own chain of layer calls.
+    cfg = layers4[0].cfg
+    note("layer4 stack of 2, T=32")
+    T = 32
+    ws = torch.zeros(fm.fmoe_workspace_size(layers4[0].L, T), dtype=torch.uint8, device="cuda")
+    x = dev(synth.activations(cfg, T, pool=27))
+    st = run_stack(layers4[:2], x, x, ws)
+    outs = run_layers(layers4[:2], x, x, ws)
+    assert _wait_timeouts(ws) == 0
+    assert_same(st, outs)
+    excluded = oracle_check(layers4[1], outs[1], (0, 31))
+    assert excluded <= 1
+
+
 def test_stack_wait_gives_up_loud(layers4):
     # Forced from the host: down part 0 never publishes (fmoe_paths.test_stall_part)
     # and waits are bounded at 2 ms.  Every layer's outputs are NaN, the timeout
