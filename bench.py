@@ -831,10 +831,14 @@ def bench_stack(args, torch):
     import bit_dequant_expert_amd as fm
     import synth
 
+    import contextlib
     cfg = synth.CONFIGS["layer4"]
     sp = cfg.spec
     NL, T = 60, 32
-    MODES = ("independent", "chained")
+    # the default (every expert of the batch on the matrix cores), and the
+    # configuration's split (experts with >= 16 tokens on the matrix cores, the
+    # rest on the multi-token GEMV kernels) beside it
+    MODES = ("independent", "chained", "independent_split16", "chained_split16")
     dev = torch.device("cuda:0")
     off, stride = sp.layout()
     print(f"[bench] generating {NL} layers ({NL * stride * (cfg.E + 1) / 1e9:.1f} GB)",
@@ -855,7 +859,7 @@ def bench_stack(args, torch):
     def step(mode, stream):
         x = r = xs[0].data_ptr()
         for l in range(NL):
-            if mode == "independent":
+            if mode.startswith("independent"):
                 x = r = xs[l].data_ptr()
             h, y = hbuf[l % 2].data_ptr(), ybuf[l % 2].data_ptr()
             rc = fm.fmoe_moe_layer_forward_raw(Lp[l], T, x, r, h, y, idx[mode][l].data_ptr(),
@@ -876,14 +880,16 @@ def bench_stack(args, torch):
 
     res = {}
     for mode in MODES:
-        with torch.cuda.stream(s):
-            step(mode, s.cuda_stream)                 # eager warm-up before capture
-        torch.cuda.synchronize()
-        # one graph holds one whole 60-layer step; a chunk of 1 step per graph
-        runner = GraphRunner(torch, s, lambda i, cs, mode=mode: step(mode, cs), 1)
+        split = fm.paths(mfma_min_tokens=16) if mode.endswith("split16") else contextlib.nullcontext()
+        with split:
+            with torch.cuda.stream(s):
+                step(mode, s.cuda_stream)                 # eager warm-up before capture
+            torch.cuda.synchronize()
+            # one graph holds one whole 60-layer step; a chunk of 1 step per graph
+            runner = GraphRunner(torch, s, lambda i, cs, mode=mode: step(mode, cs), 1)
+            runner.prepare([(0, 1)])                      # the kernels are chosen here
         timed = step_chunks(args.steps, 0, size=1)
         warm = step_chunks(args.warmup, 0, size=1)
-        runner.prepare([(0, 1)])
         runner.run(warm)
         total_ms, wall_ms = runner.timed(timed)
         rep_ms = runner.spread(0, 1, reps=min(args.steps, 10))
@@ -929,7 +935,8 @@ def bench_stack(args, torch):
         "us_per_layer": main_res["us_per_layer"],
         "routing": "independent: every layer takes a fresh N(0,1) batch (x = r), so routing "
                    "is independent across tokens and layers; chained: y and h of each layer "
-                   "are the next layer's x and residual",
+                   "are the next layer's x and residual; _split16: experts with fewer than 16 "
+                   "tokens on the multi-token GEMV kernels instead of the matrix cores",
         "modes": res,
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "roofline": {"bound": "hbm", "kernel": "all launches of the 60 layers (one graph)",
