@@ -107,6 +107,22 @@ def test_stack_over_64_layers(layers4):
     assert np.isfinite(st["y"].cpu().numpy()).all()
 
 
+@pytest.mark.parametrize("n", [1, 65])
+def test_stack_one_and_65_layers(layers4, n):
+    # A chain of one layer (one launch that is also the last layer), and 65
+    # layers (a launch of 64 and a launch of 1).
+    cfg = layers4[0].cfg
+    note(f"layer4 stack of {n}")
+    ws = torch.zeros(fm.fmoe_workspace_size(layers4[0].L, 1), dtype=torch.uint8, device="cuda")
+    seq = [layers4[(3 * l) % 4] for l in range(n)]
+    x = dev(synth.activations(cfg, 1, pool=28))
+    r = dev(synth.normal(cfg.seed, 0, 63, (1, cfg.H)))
+    st = run_stack(seq, x, r, ws)
+    outs = run_layers(seq, x, r, ws)
+    assert _wait_timeouts(ws) == 0
+    assert_same(st, outs)
+
+
 def test_stack_calls_interleaved_on_one_workspace(layers4):
     # Stack calls and single-layer calls in turn on one workspace, 40 times:
     # every call a new epoch of the shared records; each reproduces its first
