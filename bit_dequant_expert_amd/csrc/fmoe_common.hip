@@ -146,14 +146,14 @@ hipError_t launch_down_slots(QFmt f, const DArgs& a, int grid, hipStream_t st) {
 }
 
 bool mfma_supported(int H, int I, int bits, int group) {
-  return bits == 4 && H % 128 == 0 && I % 128 == 0 && I <= kMfmaMaxI && H <= kMfmaMaxH &&
+  return bits == 4 && H % 128 == 0 && H % kMoeDnRows == 0 && I % 128 == 0 && I <= kMfmaMaxI && H <= kMfmaMaxH &&
          H / group <= kMfmaMaxGroups && I / group <= kMfmaMaxGroups && H / group >= 4 &&
          I / group >= 4;
 }
 
 hipError_t launch_moe_mfma(QFmt f, const MfmaArgs& a, int mode, hipStream_t st) {
   const int N = mode == 0 ? a.I : a.H;
-  const int grid = a.maxA * (N / (mode == 0 ? kMoeGuRows : 64));
+  const int grid = a.maxA * (N / (mode == 0 ? kMoeGuRows : kMoeDnRows));
   if (grid <= 0) return hipSuccess;
   VCall c = make_call(VCall::EXPERT_MFMA, f, 1, grid, st);
   c.mf = &a;

@@ -134,6 +134,17 @@ constexpr int kMfmaMaxH = 8192;       // gate/up input images built in one pass 
 constexpr int kMoeGuSplit = FMOE_MOE_GU_SPLIT;
 constexpr int kMoeGuRows = 64 / kMoeGuSplit;
 constexpr int kMoeLdsTokens = 2;      // gate/up passes with at most this many tokens read A from LDS
+#ifndef FMOE_MOE_DN_TILES
+#define FMOE_MOE_DN_TILES 2
+#endif
+#ifndef FMOE_MOE_DN_WGS
+#define FMOE_MOE_DN_WGS 3
+#endif
+// Down matrix-core workgroups: each wave takes kMoeDnTiles 16-row tiles, 64
+// rows apart, so a workgroup covers kMoeDnRows rows; kMoeDnWgs workgroups a CU.
+constexpr int kMoeDnTiles = FMOE_MOE_DN_TILES;
+constexpr int kMoeDnRows = 64 * kMoeDnTiles;
+constexpr int kMoeDnWgs = FMOE_MOE_DN_WGS;
 struct MfmaArgs {
   ExpertSrc src;
   const int32_t* act;

@@ -15,7 +15,8 @@
 //
 // Work split: one wave owns 16 weight rows of one expert over the whole K
 // (no reduction across waves); the 4 waves of a workgroup take 4 adjacent row
-// tiles of the same expert.  Tokens go in passes of 16 (one MFMA tile).
+// tiles of the same expert (down: kMoeDnTiles such groups of 64 rows, each
+// wave one tile of each, sharing its activation words).  Tokens go in passes of 16 (one MFMA tile).
 // K runs in blocks of 128: lane group l / 16 takes 32 consecutive codes (16
 // bytes) of its row, one 16-byte load, and feeds them to 4 MFMA steps; the
 // activation words follow the same k order.  Codes (and the gate/up
@@ -138,7 +139,7 @@ __device__ __forceinline__ f16x8 weights_f16x8(uint32_t w, f16x2 s2, f16x2 b2) {
 __host__ __device__ inline int moe_scl_row(int K, int G, int SB) { return (K / G) * SB + 4; }
 __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, int SB) {
   const int nm = mode == 0 ? 2 : 1, K = mode == 0 ? H : I;
-  const int rw = mode == 0 ? kMoeGuRows : 64;
+  const int rw = mode == 0 ? kMoeGuRows : kMoeDnRows;
   const size_t scl = ((size_t)nm * 2 * rw * moe_scl_row(K, G, SB) + 15) / 16 * 16;
   const size_t img = (size_t)(mode == 0 ? kMoeLdsTokens : 16) * (K / 8 + 1) * 16;
   const size_t red =
@@ -166,13 +167,16 @@ __host__ __device__ inline size_t moe_mfma_lds(int mode, int H, int I, int G, in
 // and up (K = H) with SwiGLU into abuf; the activation words come from the
 // token images in LDS when the pass has at most kMoeLdsTokens tokens, else
 // from global memory through the register ring.  MODE 1 rows: 64 rb .. 64 rb
-// + 63 (N % 64 == 0), wave w the tile of 16 rows 64 rb + 16 w, all of K.  MODE 1: down (K = I) into yslot, the images of the pass's SwiGLU
+// + 63 (N % 64 == 0), wave w the tile of 16 rows 64 rb + 16 w, all of K
+// (with kMoeDnTiles > 1: rows kMoeDnRows rb .., wave w the tiles 16 w + 64 j).  MODE 1: down (K = I) into yslot, the images of the pass's SwiGLU
 // rows built in LDS first.  Lane l: B column (weight row) l % 16, A row
 // (token) l % 16, k sub-block l / 16; D element i is token 4 (l / 16) + i,
 // weight row l % 16.  Needs K % 128 == 0.
 template <int G, int SB, int MODE>
-__global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
+__global__ __launch_bounds__(kThreads, MODE == 1 ? kMoeDnWgs : 4) void k_moe_mfma(MfmaArgs a) {
   constexpr int NM = MODE == 0 ? 2 : 1;   // matrices: gate and up, or down
+  // Code streams (accumulators) of a wave: the two matrices, or the down tiles.
+  constexpr int NA = MODE == 0 ? 2 : kMoeDnTiles;
   extern __shared__ __align__(16) uint4 lds4[];
   __shared__ float s_sc[16];
   __shared__ int s_ent[16];
@@ -182,11 +186,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
   // two that puts that largest value in [2^10, 2^11) (so every dequantised fp16
   // weight stays below 2^15), and the fp32 result is multiplied back: fp16's
   // range does not limit the format's.
-  __shared__ uint32_t s_rmax[64];
+  __shared__ uint32_t s_rmax[MODE == 0 ? 64 : kMoeDnRows];
   // Gate/up: kMoeGuRows rows per workgroup, S waves per 16-row tile, each
   // over a part of K; down: 64 rows, a wave's 16 rows over the whole K.
   constexpr int S = MODE == 0 ? kMoeGuSplit : 1;
-  constexpr int RW = 64 / S;   // rows per workgroup
+  constexpr int RW = MODE == 0 ? 64 / S : kMoeDnRows;   // rows per workgroup
   const int N = MODE == 0 ? a.I : a.H, K = MODE == 0 ? a.H : a.I;
   const int nrb = N / RW;
   const int ai = blockIdx.x / nrb, rb = blockIdx.x - ai * nrb;
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
   const int SROW = moe_scl_row(K, G, SB);
   const int nl = tile * 16 + (lane & 15);   // row within the workgroup's
   const int om = MODE == 0 ? 0 : 6;
-  static_assert(RW <= 64, "row maxima");
+  static_assert(RW <= kThreads, "row maxima");
   if (tid < RW) s_rmax[tid] = 0u;   // ordered before the staging by the pass barriers
   // |v| of the scale words of one 4-byte word (fp32: one value; bf16: two,
   // as the fp32 bit patterns of their magnitudes), for an unsigned max.
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
   // into padded LDS rows.  When they fit in kSR 16-byte words per thread they
   // are loaded into registers first and stored later (scales_load,
   // scales_store), else copied in one loop (stage_scales).
-  constexpr int kSR = 1;
+  constexpr int kSR = MODE == 1 ? kMoeDnTiles : 1;
   const int rowb = NG * SB;
   const int sper = RW * rowb / 16, stot = 2 * NM * sper;
   // (Down only: gate/up has no registers to spare for it.)
@@ -286,10 +290,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
   // Addresses: the wave's first row as a wave-uniform base (SGPRs) and one
   // 32-bit offset per lane, so that a ring slot costs no address registers.
   const int64_t row0 = (int64_t)rb * RW + tile * 16;
-  const uint8_t* qm[NM];
+  const uint8_t* qm[NA];
 #pragma unroll
-  for (int mi = 0; mi < NM; ++mi)
-    qm[mi] = uniform_gptr(base + a.src.off[om + 3 * mi] + row0 * (K / 2) + kb0 * 64);
+  for (int mi = 0; mi < NA; ++mi)
+    qm[mi] = MODE == 0 ? uniform_gptr(base + a.src.off[3 * mi] + row0 * (K / 2) + kb0 * 64)
+                       : uniform_gptr(base + a.src.off[om] + (row0 + 64 * mi) * (K / 2) + kb0 * 64);
   const uint32_t lq = (uint32_t)(lane & 15) * (uint32_t)(K / 2) + (uint32_t)jg * 16u;
 
   for (int c0 = 0; c0 < cnt; c0 += 16) {
@@ -306,17 +311,19 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
     // own A row only, and idle rows are never stored, so they need no zeros.
     const int ar = min(am, pc - 1);
 
-    f32x4 acc[NM];
+    f32x4 acc[NA];
 #pragma unroll
-    for (int mi = 0; mi < NM; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The power of two of the lane's weight row (see s_rmax): 2^-e into fp16.
-    auto row_shift = [&]() {
-      const float mx = __uint_as_float(s_rmax[nl]);
+    for (int mi = 0; mi < NA; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Row of the workgroup that code stream mi of this lane takes.
+    auto srow = [&](int mi) { return MODE == 0 ? nl : nl + 64 * mi; };
+    // The power of two of a weight row (see s_rmax): 2^-e into fp16.
+    auto row_shift = [&](int r) {
+      const float mx = __uint_as_float(s_rmax[r]);
       int ex = 0;
       frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
       return mx > 0.f ? min(max(ex - 11, -100), 100) : 0;
     };
-    float rin = 1.f;
+    float rin[NA];
 
     auto run = [&](auto al_c) {
       constexpr bool AL = decltype(al_c)::value;          // activation words from LDS
@@ -324,10 +331,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
       constexpr int NXW = AL ? 1 : 4;
       const uint4* xrow = a.ximg + (int64_t)(MODE == 0 ? s_ent[ar] / a.kp1 : 0) * NW + kb0 * 16 + jg * 4;
       const uint4* lrow = s_img + ar * (NW + 1) + kb0 * 16 + jg * 4;
-      uint4 rq[PB][NM], rx[PB][NXW];
+      uint4 rq[PB][NA], rx[PB][NXW];
       auto issue = [&](int u, int b) {
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
+        for (int mi = 0; mi < NA; ++mi)
           rq[u][mi] = *reinterpret_cast<const uint4*>(uniform_gptr(qm[mi] + b * 64) + lq);
         if (!AL) {
 #pragma unroll
@@ -340,14 +347,15 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
         for (int s = 0; s < 4; ++s) xw[s] = AL ? lrow[b * 16 + s] : rx[u][s % NXW];
         const int gi = ((kb0 + b) * 128 + jg * 32) / G;
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          const uint8_t* sr = s_scl + ((size_t)(2 * mi) * RW + nl) * SROW + gi * SB;
-          const uint8_t* br = s_scl + ((size_t)(2 * mi + 1) * RW + nl) * SROW + gi * SB;
+        for (int mi = 0; mi < NA; ++mi) {
+          const int ms = MODE == 0 ? mi : 0;   // matrix of the stream
+          const uint8_t* sr = s_scl + ((size_t)(2 * ms) * RW + srow(mi)) * SROW + gi * SB;
+          const uint8_t* br = s_scl + ((size_t)(2 * ms + 1) * RW + srow(mi)) * SROW + gi * SB;
           const float sv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(sr))
                                    : *reinterpret_cast<const float*>(sr);
           const float bv = SB == 2 ? sb_value<2>(*reinterpret_cast<const uint16_t*>(br))
                                    : *reinterpret_cast<const float*>(br);
-          const _Float16 sh = (_Float16)(sv * rin), bh = (_Float16)(bv * rin);
+          const _Float16 sh = (_Float16)(sv * rin[mi]), bh = (_Float16)(bv * rin[mi]);
           const f16x2 s2 = {sh, sh}, b2 = {bh, bh};
           const uint32_t cw[4] = {rq[u][mi].x, rq[u][mi].y, rq[u][mi].z, rq[u][mi].w};
 #pragma unroll
@@ -403,7 +411,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
         }
       }
       __syncthreads();
-      rin = ldexpf(1.f, -row_shift());
+#pragma unroll
+      for (int mi = 0; mi < NA; ++mi) rin[mi] = ldexpf(1.f, -row_shift(srow(mi)));
       // Whole rings without branches while a whole next ring follows (the
       // load waits stay exact); then the ring in flight is computed while the
       // r blocks after it, if any, are requested, and those last.  No block
@@ -437,31 +446,36 @@ __global__ __launch_bounds__(kThreads, 4) void k_moe_mfma(MfmaArgs a) {
       __syncthreads();
       if (part > 0) {
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
-          s_red[((tile * (S - 1) + part - 1) * NM + mi) * kWave + lane] = acc[mi];
+        for (int mi = 0; mi < NA; ++mi)
+          s_red[((tile * (S - 1) + part - 1) * NA + mi) * kWave + lane] = acc[mi];
       }
       __syncthreads();
       if (part > 0) continue;
 #pragma unroll
       for (int j = 1; j < S; ++j)
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-          const f32x4 v = s_red[((tile * (S - 1) + j - 1) * NM + mi) * kWave + lane];
+        for (int mi = 0; mi < NA; ++mi) {
+          const f32x4 v = s_red[((tile * (S - 1) + j - 1) * NA + mi) * kWave + lane];
           acc[mi] = f32x4{acc[mi][0] + v[0], acc[mi][1] + v[1], acc[mi][2] + v[2], acc[mi][3] + v[3]};
         }
     }
 
-    const float rout = ldexpf(1.f, row_shift());
+    float rout[NA];
+#pragma unroll
+    for (int mi = 0; mi < NA; ++mi) rout[mi] = ldexpf(1.f, row_shift(srow(mi)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * jg + i;
       if (m < pc) {
         const int p = s_ent[m];
-        const float sc = s_sc[m] * rout;
-        if (MODE == 0)
-          a.abuf[(int64_t)p * a.I + n] = silu(acc[0][i] * sc) * (acc[NM - 1][i] * sc);
-        else
-          a.yslot[(int64_t)p * a.H + n] = acc[0][i] * sc;
+        if constexpr (MODE == 0) {
+          const float sc = s_sc[m] * rout[0];
+          a.abuf[(int64_t)p * a.I + n] = silu(acc[0][i] * sc) * (acc[1][i] * sc);
+        } else {
+#pragma unroll
+          for (int mi = 0; mi < NA; ++mi)
+            a.yslot[(int64_t)p * a.H + n + 64 * mi] = acc[mi][i] * (s_sc[m] * rout[mi]);
+        }
       }
     }
   }
