@@ -121,7 +121,7 @@ int64_t slab_layout(int H, int I, const QFmt& f, int64_t off[9]) {
 
 // ------------------------------------------------------------- workspace
 struct LayerWs {
-  size_t ctr, lg64, sel, w, g, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist;
+  size_t ctr, lg64, sel, w, g, gl, act, xprep, abuf, ccnt, aprep, yslot, gh, part, dlist;
   size_t ximg, xsc, xsum, total;
   int maxA, nrb_gu, nrb_d;
 };
@@ -139,11 +139,13 @@ LayerWs layer_ws(int T, int H, int I, int E, int k, int bits) {
   size_t pos = 0;
   w.ctr = pos; pos += fmoe::kWsReserved;   // counters (the one-launch path's block)
   // Router logits: [T, E+1] for the one-launch path, partial sums per slice
-  // [ksplit, T, E+1] for the multi-launch path (ksplit >= 1).
-  w.lg64 = pos; pos = align256(pos + (size_t)fmoe::route_ksplit(T, E + 1) * T * (E + 1) * 8);
+  // [ksplit, T, E] for the multi-launch path (ksplit >= 1).
+  const size_t lg_n = (size_t)fmoe::route_ksplit(T, E) * T * E;
+  w.lg64 = pos; pos = align256(pos + (lg_n > (size_t)T * (E + 1) ? lg_n : (size_t)T * (E + 1)) * 8);
   w.sel = pos; pos = align256(pos + (size_t)T * k * 4);
   w.w = pos; pos = align256(pos + (size_t)T * k * 4);
   w.g = pos; pos = align256(pos + (size_t)T * 4);
+  w.gl = pos; pos = align256(pos + (size_t)T * 8);
   w.act = pos; pos = align256(pos + act_ints(w.maxA, T, kp1) * 4);
   w.xprep = pos; pos = align256(pos + (size_t)T * fmoe::xprep_bytes(H));
   w.abuf = pos; pos = align256(pos + ent * I * 4);
@@ -519,12 +521,14 @@ static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, c
 
   fmoe::RouteArgs ra{};
   ra.Wr = L->router_w; ra.wsg = L->shared_gate_w; ra.x = x;
-  ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.rows = E + 1;
-  ra.ksplit = fmoe::route_ksplit(T, E + 1);
+  // The router rows only (512 rows are 32 whole tiles of the logit product);
+  // the shared gate's dot product is taken by a wave of its own.
+  ra.T = T; ra.H = H; ra.E = E; ra.k = k; ra.rows = E;
+  ra.ksplit = fmoe::route_ksplit(T, E);
   ra.part = (double*)(wsb + W.lg64);
   ra.sel_ws = (int32_t*)(wsb + W.sel);
   ra.idx_out = idx_out; ra.w_out = w_out;
-  ra.w_ws = (float*)(wsb + W.w); ra.g_ws = (float*)(wsb + W.g);
+  ra.w_ws = (float*)(wsb + W.w); ra.g_ws = (float*)(wsb + W.g); ra.gl = (double*)(wsb + W.gl);
   ra.counter = ctr + 0;
   ra.act = act; ra.maxA = W.maxA; ra.kp1 = kp1; ra.mfma_thr = mfma_thr;
   ra.xprep = use_gemv ? wsb + W.xprep : nullptr; ra.bits = f.bits;
@@ -537,6 +541,9 @@ static fmoe_status fmoe_moe_layer_forward_impl(const fmoe_layer* L, int32_t T, c
     ra.ximg = (uint4*)(wsb + W.ximg);
     ra.xsc = (float*)(wsb + W.xsc);
   }
+#ifdef FMOE_TRACE
+  ra.trace = (uint64_t*)g_trace;
+#endif
   hipError_t he = fmoe::launch_route(ra, s);
   if (he != hipSuccess) return hip_fail(he, "route kernel");
 

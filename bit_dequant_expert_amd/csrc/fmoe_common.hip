@@ -349,12 +349,14 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nlog = ((a.rows + 15) / 16) * ((a.T + 31) / 32) * a.ksplit;
-  const int nimg = a.ximg ? (a.T + kThreads / kWave - 1) / (kThreads / kWave) : 0;
-  hipLaunchKernelGGL(k_route_logits, dim3(nlog + a.n_prep_wgs + nimg), dim3(kThreads), 0, st, a);
+  const int nx = (a.ximg || a.gl) ? a.T : 0;   // per token: its image and gate logit
+  hipLaunchKernelGGL(k_route_logits, dim3(nlog + a.n_prep_wgs + nx), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lg = (size_t)a.rows * 8;
-  const size_t gr = a.act ? ((size_t)a.T * a.k + 3 * (size_t)a.E) * 4 : 0;
+  // grouping: token masks (T <= 64), selections, three per-expert arrays
+  const size_t gr =
+      a.act ? (a.T <= 64 ? (size_t)a.E * 8 : 0) + ((size_t)a.T * a.k + 3 * (size_t)a.E) * 4 : 0;
   const size_t lds = lg > gr ? lg : gr;
   const int v_need = (a.E + 63) / 64;
 #define FMOE_RS(V)                                                                   \

@@ -40,9 +40,10 @@ struct ActView {
 
 struct RouteArgs {
   const float* Wr;
-  const float* wsg;        // shared-gate row (router row E) or null
+  const float* wsg;        // shared-gate vector or null
+  double* gl;              // [T] its logits wsg . x (written by k_route_logits) or null
   const float* x;          // [T, H]
-  int T, H, E, k, rows;    // rows = E (+1 with wsg)
+  int T, H, E, k, rows;    // rows of the logit product (= E)
   int ksplit;              // slices of the hidden dim (route_ksplit)
   double* part;            // [ksplit, T, rows] partial logits
   int32_t* sel_ws;         // [T, k] selections handed to the grouping, or null
@@ -61,7 +62,10 @@ struct RouteArgs {
   float* xsc;              // their scales [T]
   int* ccnt;               // gate/up completion counters, cleared by the prep workgroups
   int n_ccnt;
+  uint64_t* trace;         // phase stamps (FMOE_TRACE builds only): kRouteTraceSel per
+                           // select workgroup, then kRouteTraceLog per logit workgroup
 };
+constexpr int kRouteTraceSel = 8, kRouteTraceLog = 4;
 
 // Slices of the hidden dim for the router's matrix product: enough
 // workgroups (16 rows x 32 tokens x slice) to cover the chip, at most 8.

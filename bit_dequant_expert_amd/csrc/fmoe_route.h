@@ -12,7 +12,8 @@
 //                   add in a fixed order through LDS); partial sums per slice
 //                   go to the workspace.  Extra workgroups prepare the
 //                   activations of the gate/up products (GEMV form, or the
-//                   matrix-core images: one wave per token).
+//                   matrix-core images: one wave per token) and take the
+//                   shared expert's gate logit wsg . x (one wave per token).
 //   k_route_select  one workgroup per token: adds the slices in a fixed
 //                   order, picks the top k (larger logit first, lower index on
 //                   ties), the softmax weights over the selection and the
@@ -25,6 +26,17 @@
 
 namespace fmoe {
 
+// Phase stamps of the FMOE_TRACE build: one thread per workgroup writes the
+// 100 MHz wall clock at its marks (the select kernel's workgroups first).
+#ifdef FMOE_TRACE
+#define ROUTE_MARK(base, ev, cond)                                                  \
+  do {                                                                              \
+    if ((cond) && a.trace) a.trace[(base) + (ev)] = wall_clock64();                 \
+  } while (0)
+#else
+#define ROUTE_MARK(base, ev, cond) do {} while (0)
+#endif
+
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
@@ -34,12 +46,48 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   const int nlog = nrt * ntp * a.ksplit;
 
   if ((int)blockIdx.x >= nlog + a.n_prep_wgs) {
-    // ---- matrix-core images of the tokens (one wave per token)
-    const int t = ((int)blockIdx.x - nlog - a.n_prep_wgs) * (kThreads / kWave) + wave;
-    if (!a.ximg || t >= a.T) return;
-    const float sc = image_row<64, kMfmaMaxH / 512>(a.x + (int64_t)t * a.H, a.H,
-                                                    a.ximg + (int64_t)t * (a.H / 8), nullptr);
-    if (lane == 0) a.xsc[t] = sc;
+    // ---- one workgroup per token: wave 0 writes the matrix-core image of x
+    // (fp16 pairs in unpack order, one power-of-two scale); waves 1 and 2 take
+    // the shared expert's gate logit wsg . x in fp64 (every product of two
+    // fp32 values is exact): each lane sums its float4 chunks in order, then
+    // the lanes, then the two halves in wave order.
+    __shared__ double s_gh;
+    const int t = (int)blockIdx.x - nlog - a.n_prep_wgs;
+    const int XB = a.T * kRouteTraceSel + nlog * kRouteTraceLog + t * 2;
+    ROUTE_MARK(XB, 0, tid == 0);
+    const bool gate = a.wsg && a.gl;
+    double acc = 0.0;
+    if (wave == 0) {
+      if (a.ximg) {
+        const float sc = image_row<64, kMfmaMaxH / 512>(a.x + (int64_t)t * a.H, a.H,
+                                                        a.ximg + (int64_t)t * (a.H / 8), nullptr);
+        if (lane == 0) a.xsc[t] = sc;
+      }
+    } else if (wave <= 2 && gate) {
+      const float4* w4 = reinterpret_cast<const float4*>(a.wsg);
+      const float4* x4 = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
+      const int nq = a.H / 4, half = (nq + 1) / 2;
+      const int q_lo = wave == 1 ? 0 : half, q_hi = wave == 1 ? half : nq;
+      constexpr int kGQ = 8;   // float4 chunks a lane has in flight
+      for (int q0 = q_lo + lane; q0 < q_hi; q0 += kGQ * kWave) {
+        float4 wv[kGQ], xv[kGQ];
+#pragma unroll
+        for (int j = 0; j < kGQ; ++j) {
+          const int q = q0 + j * kWave;
+          wv[j] = q < q_hi ? w4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+          xv[j] = q < q_hi ? x4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < kGQ; ++j)
+          acc += (double)wv[j].x * xv[j].x + (double)wv[j].y * xv[j].y +
+                 (double)wv[j].z * xv[j].z + (double)wv[j].w * xv[j].w;
+      }
+      acc = sum_lanes64(acc);
+      if (wave == 2 && lane == 0) s_gh = acc;
+    }
+    __syncthreads();
+    if (gate && wave == 1 && lane == 0) a.gl[t] = acc + s_gh;
+    ROUTE_MARK(XB, 1, tid == 0);
     return;
   }
   if ((int)blockIdx.x >= nlog) {
@@ -61,6 +109,8 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
     return;
   }
 
+  const int LB = a.T * kRouteTraceSel + (int)blockIdx.x * kRouteTraceLog;
+  ROUTE_MARK(LB, 0, tid == 0);
   const int ks = blockIdx.x % a.ksplit;
   const int rest = blockIdx.x / a.ksplit;
   const int rt = rest % nrt, tp = rest / nrt;
@@ -68,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   // and column m of the B tile (tokens) at the k index of group g.
   const int m = lane & 15, g = lane >> 4;
   const int row = rt * 16 + m;
-  const float* wrow = row < a.E ? a.Wr + (int64_t)row * a.H : (row < a.rows ? a.wsg : a.Wr);
+  const float* wrow = a.Wr + (int64_t)(row < a.rows ? row : 0) * a.H;
   const bool wok = row < a.rows;
   const int t0 = tp * 32 + m, t1 = t0 + 16;
   const bool ok0 = t0 < a.T, ok1 = t1 < a.T;
@@ -115,8 +165,10 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
     load_block(b, wv0, xa0, xb0);
     load_block(min(b + 1, b1 - 1), wv1, xa1, xb1);
     mul_block(wv0, xa0, xb0);
+    ROUTE_MARK(LB, 1, tid == 0 && b == b0);
     if (b + 1 < b1) mul_block(wv1, xa1, xb1);
   }
+  ROUTE_MARK(LB, 2, tid == 0);
 
   // Waves 1..3 hand their tiles to wave 0, which adds them in wave order.
   if (wave > 0) {
@@ -143,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  ROUTE_MARK(LB, 3, tid == 0);
   double* part = a.part + (int64_t)ks * a.T * a.rows;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -156,9 +209,13 @@ template <int VMAX>
 __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
   extern __shared__ __align__(16) double lds_d[];
   __shared__ int s_last;
-  __shared__ int s_scan[8];
+  __shared__ uint64_t s_wsum[kThreads / kWave];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
+  const int SB = t * kRouteTraceSel;
+  ROUTE_MARK(SB, 0, tid == 0);
+  // The shared gate's logit, requested with the partial sums.
+  const double glt = a.g_ws && a.gl && tid == 0 ? a.gl[t] : 0.0;
 
   // Logits of this token: the slices added in slice order.
   double* s_lg = lds_d;   // [rows]
@@ -190,6 +247,7 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
     }
   }
   __syncthreads();
+  ROUTE_MARK(SB, 1, tid == 0);
 
   if (wave == 0) {
     uint64_t key[VMAX];
@@ -222,28 +280,34 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
         if (lane == L && v == bv) key[v] = 0ull;
       if (lane == r) sel_e = win;
     }
+    // Weights: softmax over the selected logits, in fp32 from the fp64 logits
+    // (the one-token kernel's arithmetic).
     const double l = lane < a.k ? s_lg[sel_e] : 0.0;
-    const double l0 = __shfl(l, 0);
-    const double ex = lane < a.k ? exp(l - l0) : 0.0;
-    const double z = sum_lanes64(ex);
+    const double l0 = readlane_f64(l, 0);
+    const float ex = lane < a.k ? expf((float)(l - l0)) : 0.f;
+    const float z = wave_sum(ex);
     if (lane < a.k) {
-      const float w = (float)(ex / z);
+      const float w = ex / z;
       const int64_t o = (int64_t)t * a.k + lane;
       if (a.idx_out) a.idx_out[o] = sel_e;
       if (a.w_out) a.w_out[o] = w;
       if (a.w_ws) a.w_ws[o] = w;
       if (a.sel_ws) st_agent(a.sel_ws + o, sel_e);
     }
-    if (lane == 0 && a.g_ws && a.rows > a.E)
-      a.g_ws[t] = (float)(1.0 / (1.0 + exp(-s_lg[a.E])));
+    if (lane == 0 && a.g_ws && a.gl) a.g_ws[t] = 1.f / (1.f + expf(-(float)glt));
+    // The grouping reads this wave's selections: drain its stores, then count
+    // the token in.
+    ROUTE_MARK(SB, 2, lane == 0);
+    if (a.act) {
+      vm_drain();
+      if (lane == 0) s_last = (add_agent(a.counter, 1) == a.T - 1);
+      ROUTE_MARK(SB, 3, lane == 0);
+    }
   }
   if (!a.act) return;
-
-  vm_drain();
-  __syncthreads();
-  if (tid == 0) s_last = (add_agent(a.counter, 1) == a.T - 1);
   __syncthreads();
   if (!s_last) return;
+  ROUTE_MARK(SB, 5, tid == 0);
 
   // ---- last workgroup: group token slots by expert.
   int32_t* act = a.act;
@@ -253,25 +317,55 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
   int32_t* act_mf = act_cnt + a.maxA;
   int32_t* entries = act_mf + a.maxA;
   const int nsel = a.T * a.k;
-  int* s_sel = reinterpret_cast<int*>(lds_d);   // [T*k], then [E] x 3
+  // LDS: per-expert token masks [E] (T <= 64), then the selections [T*k] and
+  // per-expert counts, active positions and first entries [E] x 3.
+  const bool masks = a.T <= 64;
+  uint64_t* s_msk = reinterpret_cast<uint64_t*>(lds_d);
+  int* s_sel = reinterpret_cast<int*>(s_msk + (masks ? a.E : 0));
   for (int j = tid; j < nsel; j += kThreads) s_sel[j] = ld_agent(a.sel_ws + j);
   int* s_cnt = s_sel + nsel;   // [E]
   int* s_pos = s_cnt + a.E;    // [E] rank among active experts
   int* s_off = s_pos + a.E;    // [E] first entry
-  for (int e = tid; e < a.E; e += kThreads) s_cnt[e] = 0;
+  for (int e = tid; e < a.E; e += kThreads) {
+    s_cnt[e] = 0;
+    if (masks) s_msk[e] = 0ull;
+  }
   __syncthreads();
-  for (int j = tid; j < nsel; j += kThreads) atomicAdd(&s_cnt[s_sel[j]], 1);
+  for (int j = tid; j < nsel; j += kThreads) {
+    atomicAdd(&s_cnt[s_sel[j]], 1);
+    if (masks) atomicOr(reinterpret_cast<unsigned long long*>(&s_msk[s_sel[j]]), 1ull << (j / a.k));
+  }
   __syncthreads();
+  ROUTE_MARK(SB, 6, tid == 0);
+  // Per thread a run of experts: active ones, slots, and matrix-core ones,
+  // scanned over the workgroup as one packed 64-bit value (16 | 16 | 32 bits).
   const int per = (a.E + kThreads - 1) / kThreads;
   const int e0 = tid * per, e1 = min(a.E, e0 + per);
-  int nf = 0, nc = 0;
-  for (int e = e0; e < e1; ++e) { nf += s_cnt[e] > 0; nc += s_cnt[e]; }
-  int tf, tc;
-  int bf = block_exscan(nf, s_scan, tf);
-  int bc = block_exscan(nc, s_scan, tc);
+  uint64_t pk = 0;
+  for (int e = e0; e < e1; ++e)
+    pk += (uint64_t)(s_cnt[e] > 0) | ((uint64_t)(s_cnt[e] >= a.mfma_thr) << 16) |
+          ((uint64_t)s_cnt[e] << 32);
+  uint64_t inc = pk;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint64_t o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = inc;
+  __syncthreads();
+  uint64_t before = 0, total = 0;
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    if (w < wave) before += s_wsum[w];
+    total += s_wsum[w];
+  }
+  const uint64_t ex = before + inc - pk;
+  int bf = (int)(ex & 0xFFFF), bc = (int)(ex >> 32);
+  const int sh = a.T >= a.mfma_thr ? 1 : 0;
+  int bm = (int)((ex >> 16) & 0xFFFF) + sh;
+  const int tf = (int)(total & 0xFFFF), tm = (int)((total >> 16) & 0xFFFF);
   // The shared expert (all T tokens: the most work) takes active index 0 so
   // that the expert kernels start its workgroups first; routed experts follow
-  // in expert order at 1 .. tf.
+  // in expert order at 1 .. tf.  Matrix-core list: the shared expert, then the
+  // routed experts at or above the threshold in expert order.
   for (int e = e0; e < e1; ++e) {
     s_pos[e] = bf + 1;
     s_off[e] = bc;
@@ -279,35 +373,34 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
       act_e[bf + 1] = e;
       act_off[bf + 1] = bc;
       act_cnt[bf + 1] = s_cnt[e];
+      if (s_cnt[e] >= a.mfma_thr) act_mf[bm++] = bf + 1;
       ++bf;
     }
     bc += s_cnt[e];
   }
   __syncthreads();
   // Stable scatter: a slot's rank among the slots of its expert is the number
-  // of earlier slots (token order, then selection order) with that expert.
+  // of earlier slots (token order, then selection order) with that expert.  A
+  // token selects an expert at most once, so with the token masks that is the
+  // number of earlier tokens in the expert's mask.
   const int4* s_sel4 = reinterpret_cast<const int4*>(s_sel);
   for (int j = tid; j < nsel; j += kThreads) {
-    const int e = s_sel[j];
-    int rank = 0, jj = 0;
+    const int e = s_sel[j], tj = j / a.k;
+    int rank = 0;
+    if (masks) {
+      rank = __popcll(s_msk[e] & ((1ull << tj) - 1ull));
+    } else {
+      int jj = 0;
 #pragma unroll 4
-    for (; jj + 4 <= j; jj += 4) {   // four slots per LDS read
-      const int4 v = s_sel4[jj >> 2];
-      rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+      for (; jj + 4 <= j; jj += 4) {   // four slots per LDS read
+        const int4 v = s_sel4[jj >> 2];
+        rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+      }
+      for (; jj < j; ++jj) rank += (s_sel[jj] == e);
     }
-    for (; jj < j; ++jj) rank += (s_sel[jj] == e);
-    entries[s_off[e] + rank] = (j / a.k) * a.kp1 + (j % a.k);
+    entries[s_off[e] + rank] = tj * a.kp1 + (j % a.k);
   }
   for (int tt = tid; tt < a.T; tt += kThreads) entries[nsel + tt] = tt * a.kp1 + a.k;
-  // Matrix-core list: the shared expert, then the routed experts at or above
-  // the threshold in expert order.
-  int nm = 0;
-  for (int e = e0; e < e1; ++e) nm += s_cnt[e] >= a.mfma_thr;
-  int tm;
-  const int sh = a.T >= a.mfma_thr ? 1 : 0;
-  int bm = block_exscan(nm, s_scan, tm) + sh;
-  for (int e = e0; e < e1; ++e)
-    if (s_cnt[e] >= a.mfma_thr) act_mf[bm++] = s_pos[e];
   if (tid == 0) {
     act_e[0] = a.E;
     act_off[0] = nsel;
@@ -317,6 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_route_select(RouteArgs a) {
     act[1] = tm + sh;
     st_agent(a.counter, 0);
   }
+  ROUTE_MARK(SB, 7, tid == 0);
 }
 
 }  // namespace fmoe
