@@ -349,7 +349,7 @@ hipError_t launch_fused1(QFmt f, const FusedArgs& a, hipStream_t st) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nlog = ((a.rows + 15) / 16) * ((a.T + 31) / 32) * a.ksplit;
-  const int nx = (a.ximg || a.gl) ? a.T : 0;   // per token: its image and gate logit
+  const int nx = (a.ximg || a.gl) ? a.T : 0;   // per token (first): its image and gate logit
   hipLaunchKernelGGL(k_route_logits, dim3(nlog + a.n_prep_wgs + nx), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -45,14 +45,18 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   const int nrt = (a.rows + 15) / 16, ntp = (a.T + 31) / 32;
   const int nlog = nrt * ntp * a.ksplit;
 
-  if ((int)blockIdx.x >= nlog + a.n_prep_wgs) {
+  // Workgroups: T token workgroups first (their loads go out ahead of the
+  // bulk), then the logit tiles, then the GEMV-form preparation.
+  const int nx = (a.ximg || a.gl) ? a.T : 0;
+  const int bi = (int)blockIdx.x - nx;
+  if (bi < 0) {
     // ---- one workgroup per token: wave 0 writes the matrix-core image of x
     // (fp16 pairs in unpack order, one power-of-two scale); waves 1 and 2 take
     // the shared expert's gate logit wsg . x in fp64 (every product of two
     // fp32 values is exact): each lane sums its float4 chunks in order, then
     // the lanes, then the two halves in wave order.
     __shared__ double s_gh;
-    const int t = (int)blockIdx.x - nlog - a.n_prep_wgs;
+    const int t = (int)blockIdx.x;
     const int XB = a.T * kRouteTraceSel + nlog * kRouteTraceLog + t * 2;
     ROUTE_MARK(XB, 0, tid == 0);
     const bool gate = a.wsg && a.gl;
@@ -90,10 +94,10 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
     ROUTE_MARK(XB, 1, tid == 0);
     return;
   }
-  if ((int)blockIdx.x >= nlog) {
+  if (bi >= nlog) {
     // ---- activation prep for the gate/up products (independent of routing)
     if (!a.xprep) return;
-    const int pb = blockIdx.x - nlog;
+    const int pb = bi - nlog;
     // The gate/up kernel's completion counters live in the workspace's data
     // region, where a call of another shape may have left data: clear them
     // here, one launch ahead of their first use.
@@ -109,10 +113,10 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
     return;
   }
 
-  const int LB = a.T * kRouteTraceSel + (int)blockIdx.x * kRouteTraceLog;
+  const int LB = a.T * kRouteTraceSel + bi * kRouteTraceLog;
   ROUTE_MARK(LB, 0, tid == 0);
-  const int ks = blockIdx.x % a.ksplit;
-  const int rest = blockIdx.x / a.ksplit;
+  const int ks = bi % a.ksplit;
+  const int rest = bi / a.ksplit;
   const int rt = rest % nrt, tp = rest / nrt;
   // Operand lanes: lane = m + 16 g supplies row m of the A tile (router rows)
   // and column m of the B tile (tokens) at the k index of group g.
@@ -130,11 +134,12 @@ __global__ __launch_bounds__(kThreads) void k_route_logits(RouteArgs a) {
   const int b0 = (int)((int64_t)s * nblk / NS), b1 = (int)((int64_t)(s + 1) * nblk / NS);
 
   f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-  // Lane group g covers elements kb .. kb+15 of its row and of its tokens.
+  // Lane group g takes elements 16 j + 4 g .. + 3 of the block (j < 4) of its
+  // row and of its tokens: each load covers 64 contiguous bytes of 16 rows.
   auto load_block = [&](int b, float4 (&wv)[4], float4 (&xa)[4], float4 (&xb)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int kk = b * 64 + 16 * g + 4 * j;
+      const int kk = b * 64 + 16 * j + 4 * g;
       const bool in = kk < a.H;   // H % 4 == 0: a float4 is wholly in or out
       const int kc = in ? kk : 0;
       wv[j] = ld_nt(reinterpret_cast<const float4*>(wrow + kc));
