@@ -12,10 +12,13 @@ namespace fmoe {
 // Sigmoid-Gating", and the two-phase RMSNorm: h = r + sum_i w_i y_i + g y_s
 // (routed slots in selection order, then the shared one), y = gamma h / rms(h).
 // Each thread keeps its float4s of h in registers between the two phases; the
-// slot loads are issued four slots at a time ahead of their use.
-__global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
-  constexpr int MAXJ = 8;   // H <= 8 * 4 * kThreads
-  __shared__ float s_part[kThreads / kWave];
+// slot loads are issued four slots at a time ahead of their use.  1024 threads
+// a token: a CU has every float4 of a 4096-wide row in flight at once.
+constexpr int kCombThreads = 1024;
+__global__ __launch_bounds__(kCombThreads) void k_combine_norm(CombineArgs a) {
+  constexpr int NT = kCombThreads;
+  constexpr int MAXJ = 2;   // H <= 2 * 4 * NT
+  __shared__ float s_part[NT / kWave];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nf = a.H / 4;
   const int64_t row = (int64_t)t * a.H;
@@ -23,7 +26,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
   float4 acc[MAXJ], rv[MAXJ], gm[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
-    const int f = j * kThreads + tid;
+    const int f = j * NT + tid;
     const int fc = f < nf ? f : 0;
     acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     rv[j] = reinterpret_cast<const float4*>(a.resid + row)[fc];
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
       if (i0 + q >= a.kp1) c[q] = 0.f;
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) {
-        const int f = j * kThreads + tid;
+        const int f = j * NT + tid;
         v[q][j] = ys[(int64_t)i * nf + (f < nf ? f : 0)];
       }
     }
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
-    const int f = j * kThreads + tid;
+    const int f = j * NT + tid;
     if (f < nf) {
       const float4 h = make_float4(rv[j].x + acc[j].x, rv[j].y + acc[j].y, rv[j].z + acc[j].z,
                                    rv[j].w + acc[j].w);
@@ -76,11 +79,11 @@ __global__ __launch_bounds__(kThreads) void k_combine_norm(CombineArgs a) {
   if (lane == kWave - 1) s_part[wave] = ss;
   __syncthreads();
   float tot = 0.f;
-  for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+  for (int w = 0; w < NT / kWave; ++w) tot += s_part[w];
   const float inv = 1.f / sqrtf(tot / (float)a.H + a.eps);
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
-    const int f = j * kThreads + tid;
+    const int f = j * NT + tid;
     if (f < nf)
       reinterpret_cast<float4*>(a.y_out + row)[f] =
           make_float4(gm[j].x * rv[j].x * inv, gm[j].y * rv[j].y * inv, gm[j].z * rv[j].z * inv,
@@ -370,7 +373,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine_norm, dim3(a.T), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(k_combine_norm, dim3(a.T), dim3(kCombThreads), 0, st, a);
   return hipGetLastError();
 }
 
