@@ -539,7 +539,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
         ts[r][m].load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
                       2 * sp + r, geoH);
   };
-  if (writer_wave) shared_load(min(b, n_sp - 1));
   TOK1_MARK(14);   // phase A loads issued
   // Down rows of part b held by waves 2-3: rows b*d_rows + (w-2)*kUD*RPI +
   // u*RPI + lane_row (u < kUD).
@@ -610,6 +609,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
     lds_barrier();   // sh.rp is reused
   }
   TOK1_MARK(2);   // logit records stored
+  // Wave 3 requests its shared rows only now: in phase A the router rows have
+  // the memory to themselves (the shared SwiGLU has slack until phase C).
+  if (writer_wave) shared_load(min(b, n_sp - 1));
 
 #pragma unroll
   for (int q = 0; q < kQ; ++q) prep_x4<BITS, false, true>(xq[q], lds_xp, H, q * (kThreads / 8) + tid / 8);
