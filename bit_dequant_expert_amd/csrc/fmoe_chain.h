@@ -427,8 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
         gu_publish(part);
       }
       const int t = tid;    // 0 .. 127
-      bool ok = poll_shared<128>(lds_x, rsh, I, ep, a.spin_ticks, t);
-      ok &= poll_images<BITS, 128>(lds_ap, 1, rimg, I, 1, k, ep, a.spin_ticks, t);
+      bool ok = poll_shared_images<BITS, 128>(lds_x, rsh, lds_ap, 1, rimg, I, 1, k, ep,
+                                              a.spin_ticks, t);
       if (!ok) sh.fail = 1;
       lds_barrier();   // images polled
       CHAIN_MARK(5, 0);   // first images in LDS
