@@ -345,7 +345,9 @@ def test_layer_tiny_single_tokens():
         check_layer(gl, x[t:t + 1], r[t:t + 1], got, [0])
 
 
-@pytest.mark.parametrize("T", [2, 5, 16, 32])
+# 65 and 100 tokens: several token tiles of the router's product, and the
+# grouping's rank by scanning (its token masks cover at most 64 tokens).
+@pytest.mark.parametrize("T", [2, 5, 16, 32, 65, 100])
 def test_layer_tiny_batched(T):
     cfg = synth.CONFIGS["tiny"]
     note(f"layer tiny T={T}")
