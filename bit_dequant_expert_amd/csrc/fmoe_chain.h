@@ -99,12 +99,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
   }
   lds_barrier();
 
-  // The first loads of a layer's phase A (router row b and the shared-gate
-  // value of this thread) do not depend on x: they are issued for layer 0
-  // here and for layer l + 1 at the start of layer l's phase D, so that they
-  // are in flight while the last hand-off of layer l completes.  Wave 3's
-  // shared row pair follows the layer's logit record (the router rows have
-  // the memory to themselves until then; the shared SwiGLU has slack).
+  // The first loads of a layer's phase A (router row b, the shared-gate value
+  // of this thread, and in wave 3 the shared row pair b) do not depend on x:
+  // they are issued
+  // for layer 0 here and for layer l + 1 at the start of layer l's phase D,
+  // so that they are in flight while the last hand-off of layer l completes.
   // (The last layer issues its own loads again: a load issued on every path
   // keeps the registers of the earlier one dead through phases B-C.)
   const int n_sp = I / 2;
@@ -113,12 +112,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
   float wsg_v;
   auto first_loads = [&](const Tok1ChainLayer& Ln) {
     const int tid = tid_x(), lane = tid & 63;
+    const RowGeo geoH(H, BITS);
     const int e = min(b, E - 1);
     const float4* row = reinterpret_cast<const float4*>(Ln.Wr + (int64_t)e * H);
     const int q0 = wave * (H / 16) + lane;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) wv[q] = ld_nt(row + q0 + q * 64);
     wsg_v = Ln.wsg[min((int)((int64_t)e * H / E) + tid, H - 1)];
+    if (writer_wave) {
+      const uint8_t* base = Ln.slabs + (int64_t)E * a.stride;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          ts[r][m].load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
+                        2 * min(b, n_sp - 1) + r, geoH);
+    }
   };
   first_loads(ch.layer[0]);
 
@@ -204,7 +213,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
       lds_barrier();
     }
     CHAIN_MARK(1, 3);   // logits stored
-    if (writer_wave) shared_load(min(b, n_sp - 1));
 
     // x prepared as fp16 pairs for the gate/up rows
 #pragma unroll
@@ -427,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
         gu_publish(part);
       }
       const int t = tid;    // 0 .. 127
-      bool ok = poll_shared_images<BITS, 128>(lds_x, rsh, lds_ap, 1, rimg, I, 1, k, ep,
-                                              a.spin_ticks, t);
+      bool ok = poll_shared<128>(lds_x, rsh, I, ep, a.spin_ticks, t);
+      ok &= poll_images<BITS, 128>(lds_ap, 1, rimg, I, 1, k, ep, a.spin_ticks, t);
       if (!ok) sh.fail = 1;
       lds_barrier();   // images polled
       CHAIN_MARK(5, 0);   // first images in LDS

@@ -266,92 +266,35 @@ __device__ __forceinline__ bool poll_images(uint8_t* lds_ap, int lds_first, cons
   return ok_all;
 }
 
-// The two polls of phase C's first batch in the same rounds: the shared
-// expert's I/2 SwiGLU records (two fp32 values each) into an fp32 staging
-// area of LDS, and the routed SwiGLU blocks of slots [s0, s0 + ns) into the
-// LDS images (as poll_images).  The shared records were published long before, so they
-// complete in the first round, which thus costs no round trip of its own.
-template <int BITS, int NT>
-__device__ __forceinline__ bool poll_shared_images(float* stage, const rsrc_t& rsh, uint8_t* lds_ap,
-                                                   int lds_first, const rsrc_t& rimg, int I, int s0,
-                                                   int ns, uint32_t ep, uint64_t limit, int t) {
-  using B = ImgBlk<BITS>;
-  constexpr int W = B::W, PPS = QF<BITS>::PPS;
-  constexpr int kPer = 4;                     // records (shared) and blocks (routed) per thread a pass
-  const int S = I * BITS / 128;
-  const int nb = I / W;                       // blocks per image
-  const int total = ns * nb;
-  const int n_sh = I / 2;
-  const int64_t ib = wimg_bytes(I, BITS);
-  const int per_pass = kPer * NT;
-  const int passes = max((n_sh + per_pass - 1) / per_pass, (total + per_pass - 1) / per_pass);
+// Polls the shared expert's I/2 SwiGLU records (two fp32 values each) into an
+// fp32 staging area of LDS.  NT threads, thread index t.
+template <int NT>
+__device__ __forceinline__ bool poll_shared(float* stage, const rsrc_t& rsh, int I, uint32_t ep,
+                                            uint64_t limit, int t) {
+  constexpr int kPer = 4;
+  const int n = I / 2;
   bool ok_all = true;
-  for (int ps = 0; ps < passes; ++ps) {
-    const int base = ps * per_pass;
-    bool dsh[kPer], dim[kPer];
-    u32x4_t rs[kPer];
-    u32x4_t ri[kPer][B::NCH];
+  for (int base = 0; base < n; base += kPer * NT) {
+    bool done[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      dsh[j] = base + j * NT + t >= n_sh;
-      dim[j] = base + j * NT + t >= total;
-    }
+    for (int j = 0; j < kPer; ++j) done[j] = base + j * NT + t >= n;
     const uint64_t t0 = now_ticks();
     for (;;) {
+      u32x4_t r[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = min(base + j * NT + t, n_sh - 1);
-        if (!dsh[j]) rs[j] = rec_ld(rsh, (uint32_t)(16 * i));
-      }
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int g = min(base + j * NT + t, total - 1);
-        const int sl = g / nb, blk = g - sl * nb;
-        const uint32_t off = (uint32_t)(((s0 + sl) * nb + blk) * B::BYTES);
-        if (!dim[j]) {
-#pragma unroll
-          for (int c = 0; c < B::NCH; ++c) ri[j][c] = rec_ld(rimg, off + 16 * c);
-        }
+        const int i = min(base + j * NT + t, n - 1);
+        if (!done[j]) r[j] = rec_ld(rsh, (uint32_t)(16 * i));
       }
       bool pending = false;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        if (dsh[j]) continue;
+        if (done[j]) continue;
         const int i = base + j * NT + t;
-        if (!rec_ok(rs[j], ep, pos_salt(kSaltShared, i))) { pending = true; continue; }
-        dsh[j] = true;
-        reinterpret_cast<float2*>(stage)[i] = make_float2(__uint_as_float(rs[j][0]),
-                                                          __uint_as_float(rs[j][1]));
-      }
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (dim[j]) continue;
-        bool ok = true;
-#pragma unroll
-        for (int c = 0; c < B::NCH; ++c) {
-          const uint32_t chk = rec_check(ep, ri[j][c][0], ri[j][c][1], ri[j][c][2], kSaltImg + c);
-          ok &= c == B::NCH - 1 ? ((chk ^ ri[j][c][3]) & 0xFFFFFF00u) == 0 : chk == ri[j][c][3];
-        }
-        if (!ok) { pending = true; continue; }
-        dim[j] = true;
-        const int g = base + j * NT + t;
-        const int sl = g / nb, blk = g - sl * nb;
-        uint32_t pw[B::NCH * 3];
-#pragma unroll
-        for (int c = 0; c < B::NCH; ++c) {
-          pw[3 * c] = ri[j][c][0]; pw[3 * c + 1] = ri[j][c][1]; pw[3 * c + 2] = ri[j][c][2];
-        }
-        const int sh = (int)(ri[j][B::NCH - 1][3] & 0xFFu) - 128;
-        uint8_t* img = lds_ap + (lds_first + sl) * ib;
-#pragma unroll
-        for (int v = 0; v < W / 8; ++v) {
-          const int lin = blk * (W / 8) + v;
-          reinterpret_cast<uint4*>(img)[lds_chunk<BITS, 4>(lin, S)] =
-              make_uint4(pw[4 * v], pw[4 * v + 1], pw[4 * v + 2], pw[4 * v + 3]);
-        }
-        reinterpret_cast<float4*>(img)[lds_chunk<BITS, 4>(S * (PPS / 4) + blk, S)] =
-            make_float4(ldexpf(1.f, sh), __uint_as_float(pw[W / 2]),
-                        __uint_as_float(pw[W / 2 + 1]), 0.f);
+        if (!rec_ok(r[j], ep, pos_salt(kSaltShared, i))) { pending = true; continue; }
+        done[j] = true;
+        reinterpret_cast<float2*>(stage)[i] = make_float2(__uint_as_float(r[j][0]),
+                                                          __uint_as_float(r[j][1]));
       }
       if (!__any(pending)) break;
       if (now_ticks() - t0 > limit) { ok_all = false; break; }
@@ -596,6 +539,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
         ts[r][m].load(base + a.off[3 * m], base + a.off[3 * m + 1], base + a.off[3 * m + 2], H,
                       2 * sp + r, geoH);
   };
+  if (writer_wave) shared_load(min(b, n_sp - 1));
   TOK1_MARK(14);   // phase A loads issued
   // Down rows of part b held by waves 2-3: rows b*d_rows + (w-2)*kUD*RPI +
   // u*RPI + lane_row (u < kUD).
@@ -666,9 +610,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
     lds_barrier();   // sh.rp is reused
   }
   TOK1_MARK(2);   // logit records stored
-  // Wave 3 requests its shared rows only now: in phase A the router rows have
-  // the memory to themselves (the shared SwiGLU has slack until phase C).
-  if (writer_wave) shared_load(min(b, n_sp - 1));
 
 #pragma unroll
   for (int q = 0; q < kQ; ++q) prep_x4<BITS, false, true>(xq[q], lds_xp, H, q * (kThreads / 8) + tid / 8);
@@ -864,8 +805,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
       bool ok = true;
       if (s0 == 0) {
         // the shared expert's values (image slot 0 is built from them below)
-        ok &= poll_shared_images<BITS, 128>(lds_x, rsh, lds_ap, 1, rimg, I, 1, ns - 1, ep,
-                                            a.spin_ticks, t);
+        ok &= poll_shared<128>(lds_x, rsh, I, ep, a.spin_ticks, t);
+        ok &= poll_images<BITS, 128>(lds_ap, 1, rimg, I, 1, ns - 1, ep, a.spin_ticks, t);
       } else {
         ok &= poll_images<BITS, 128>(lds_ap, 0, rimg, I, s0, ns, ep, a.spin_ticks, t);
       }
