@@ -207,7 +207,9 @@ __device__ __forceinline__ bool poll_images(uint8_t* lds_ap, int lds_first, cons
   const int nb = I / W;                       // blocks per image
   const int total = ns * nb;
   const int64_t ib = wimg_bytes(I, BITS);
-  constexpr int kPer = 4;                     // blocks per thread per pass
+  // One block per thread a pass: polls in small rounds finish sooner than one
+  // round over every block (a poll's cost grows with the records it reads).
+  constexpr int kPer = 1;                     // blocks per thread per pass
   bool ok_all = true;
   for (int base = 0; base < total; base += kPer * NT) {
     bool done[kPer];
@@ -271,7 +273,7 @@ __device__ __forceinline__ bool poll_images(uint8_t* lds_ap, int lds_first, cons
 template <int NT>
 __device__ __forceinline__ bool poll_shared(float* stage, const rsrc_t& rsh, int I, uint32_t ep,
                                             uint64_t limit, int t) {
-  constexpr int kPer = 4;
+  constexpr int kPer = 1;
   const int n = I / 2;
   bool ok_all = true;
   for (int base = 0; base < n; base += kPer * NT) {
