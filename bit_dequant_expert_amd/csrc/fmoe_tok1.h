@@ -833,25 +833,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer1t(const float* __restrict
     }
     const uint64_t t0 = now_ticks();
     bool ok_all = true;
-    for (;;) {   // each wave polls its own parts
-      u32x4_t r[J];
+    // each wave polls its own parts, two a thread per pass (small poll rounds
+    // finish sooner; one a pass adds a round trip more than it saves)
+    constexpr int JP = 2;
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int d = min(j * 128 + t, a.nD - 1);
-        if (!done[j]) r[j] = rec_ld(rpart, (uint32_t)(16 * d));
-      }
-      bool pending = false;
+    for (int j0 = 0; j0 < J; j0 += JP) {
+      for (;;) {
+        u32x4_t r[JP];
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        if (done[j]) continue;
-        const int d = j * 128 + t;
-        if (!rec_ok(r[j], ep, pos_salt(kSaltPart, d))) { pending = true; continue; }
-        done[j] = true;
-        pv[j] = __uint_as_float(r[j][0]);
+        for (int jj = 0; jj < JP; ++jj) {
+          const int j = j0 + jj, d = min(j * 128 + t, a.nD - 1);
+          if (j < J && !done[j]) r[jj] = rec_ld(rpart, (uint32_t)(16 * d));
+        }
+        bool pending = false;
+#pragma unroll
+        for (int jj = 0; jj < JP; ++jj) {
+          const int j = j0 + jj;
+          if (j >= J || done[j]) continue;
+          const int d = j * 128 + t;
+          if (!rec_ok(r[jj], ep, pos_salt(kSaltPart, d))) { pending = true; continue; }
+          done[j] = true;
+          pv[j] = __uint_as_float(r[jj][0]);
+        }
+        if (!__any(pending)) break;
+        if (now_ticks() - t0 > a.spin_ticks) { ok_all = false; break; }
+        __builtin_amdgcn_s_sleep(1);
       }
-      if (!__any(pending)) break;
-      if (now_ticks() - t0 > a.spin_ticks) { ok_all = false; break; }
-      __builtin_amdgcn_s_sleep(1);
+      if (!ok_all) break;
     }
     float p = 0.f;
 #pragma unroll
