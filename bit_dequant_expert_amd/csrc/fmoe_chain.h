@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain1t(const float* __restrict
     // into lds_ss (the prepared-x area, free by now).  False if the wait gave
     // up.
     auto poll_parts = [&]() -> bool {
-      constexpr int kPer = 6;
+      constexpr int kPer = 1;   // small poll rounds finish sooner than one round of six
       const int t = tid_x();
       const int nrec = R * a.nD;
       float* lds_ss = reinterpret_cast<float*>(lds_xp);
